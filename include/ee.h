@@ -1,0 +1,221 @@
+/*
+ * ee.h -- C ABI of libee: the forward pass of a pre-LN GPT decoder layer with
+ * redundant-computation elimination (RCE) on one AMD Instinct MI355X (gfx950).
+ *
+ * The method: the Energon-AI announcement article (Colossal-AI team), "Runtime"
+ * section, adds two ops, transpose_padding_remove and transpose_padding_rebuild,
+ * so that the layers of encoder and decoder models do no work on the padding of
+ * variable-length inputs; the EnergonAI README ("Scaling Ability", "Latency")
+ * runs GPT-3 layers in FP16 with that method, with sequence length half the
+ * padding length.  This library computes, on one GPU:
+ *
+ *   offsets:  per-sequence lengths (or the attention mask) prefix-summed into
+ *             packed token offsets;
+ *   remove:   padded [batch, pad_len, hidden] -> packed [T, hidden], T = sum(len);
+ *   layer:    LayerNorm, the QKV / out-projection / MLP GEMMs and GeLU on the T
+ *             valid rows only; attention causally per sequence over the offsets;
+ *   rebuild:  packed [T, hidden] -> padded [batch, pad_len, hidden], pads +0.0.
+ *
+ * Conventions (all entry points):
+ *   - Every device pointer is caller-owned device memory (hipMalloc or any
+ *     allocator), 16-byte aligned, row-major and dense.  Host pointers are
+ *     marked "host".  The library never frees caller memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on `stream`: no device synchronisation,
+ *     no device-to-host copy, no allocation in the forward path.
+ *   - Arguments are validated on the host BEFORE any device work; a failed
+ *     check returns EE_ERR_INVALID_ARG / EE_ERR_UNSUPPORTED / EE_ERR_WORKSPACE
+ *     and enqueues nothing.  A HIP launch error returns EE_ERR_HIP; an
+ *     asynchronous fault of earlier work may surface as EE_ERR_HIP on a later
+ *     call.  ee_last_error() gives a thread-local message for the last failure.
+ *   - No call works in place: outputs must not overlap inputs.
+ *   - Per-sequence lengths are host int32 values in [0, pad_len] (the batcher
+ *     that built the batch knows them); they reach the device as kernel
+ *     arguments, so the caller's array may be reused as soon as the call
+ *     returns.  batch <= EE_MAX_BATCH.
+ *   - Weights use the nn.Linear [out, in] layout.  The fused QKV weight is
+ *     [3*n_heads*head_dim, hidden]: rows q | k | v, each block head-major.
+ *   - Thread safety: distinct layer handles may be used from distinct threads;
+ *     one handle's calls must not run concurrently.
+ */
+#ifndef EE_H_
+#define EE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define EE_API __attribute__((visibility("default")))
+#else
+#define EE_API
+#endif
+
+#define EE_MAX_BATCH 512
+
+typedef enum {
+  EE_OK = 0,
+  EE_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, overlapping buffers */
+  EE_ERR_UNSUPPORTED = 2, /* valid request the kernels do not cover (head_dim, sizes) */
+  EE_ERR_WORKSPACE = 3,   /* workspace smaller than the ..._workspace_size result */
+  EE_ERR_OOM = 4,         /* host allocation failed (handles only) */
+  EE_ERR_HIP = 5          /* a HIP runtime call failed */
+} ee_status;
+
+/* Storage type of activations and weights.  Arithmetic is fp32 in both cases
+ * (fp16 storage with fp32 accumulation is the pages' `half = True` setting,
+ * announcement article, "Ease of use" config). */
+typedef enum { EE_F32 = 0, EE_F16 = 1 } ee_dtype;
+
+/* GeLU form: tanh approximation (GPT-2/3 default) or the erf definition. */
+typedef enum { EE_GELU_TANH = 0, EE_GELU_ERF = 1 } ee_gelu;
+
+/* Epilogue of ee_linear: C = A W^T (+ bias) (+ residual) or gelu(A W^T + bias). */
+typedef enum {
+  EE_EPI_NONE = 0,
+  EE_EPI_BIAS = 1,
+  EE_EPI_BIAS_RESIDUAL = 2,
+  EE_EPI_BIAS_GELU = 3
+} ee_epilogue;
+
+typedef struct {
+  int32_t hidden;    /* H */
+  int32_t n_heads;   /* nh */
+  int32_t head_dim;  /* hd in {16, 32, 64, 128}; H' = nh*hd */
+  int32_t ffn;       /* F */
+  float ln_eps;      /* LayerNorm epsilon (inside the square root), e.g. 1e-5 */
+  ee_dtype dtype;
+  ee_gelu gelu;
+  int32_t fuse_gelu; /* 1: bias+GeLU in the FC1 GEMM epilogue; 0: separate bias+GeLU kernel */
+} ee_layer_desc;
+
+/* Device pointers, all of the descriptor's dtype, borrowed (not copied) by
+ * ee_layer_create for the handle's lifetime. */
+typedef struct {
+  const void *ln1_g, *ln1_b;   /* [H] */
+  const void *w_qkv, *b_qkv;   /* [3H', H], [3H'] */
+  const void *w_out, *b_out;   /* [H, H'],  [H] */
+  const void *ln2_g, *ln2_b;   /* [H] */
+  const void *w_fc1, *b_fc1;   /* [F, H],   [F] */
+  const void *w_fc2, *b_fc2;   /* [H, F],   [H] */
+} ee_layer_weights;
+
+typedef struct ee_layer ee_layer;
+
+/* ---- status ------------------------------------------------------------ */
+EE_API const char* ee_status_string(ee_status s);
+/* Thread-local detail of the last non-OK status returned on this thread. */
+EE_API const char* ee_last_error(void);
+/* Library version string. */
+EE_API const char* ee_version(void);
+
+/* ---- layer handle (announcement article, "Runtime": the RCE layer forward) -- */
+/* Validates the descriptor and borrows the weight pointers.  No device work. */
+EE_API ee_status ee_layer_create(const ee_layer_desc* desc, const ee_layer_weights* weights, ee_layer** out);
+EE_API ee_status ee_layer_destroy(ee_layer* layer);
+
+/* Device workspace bytes that ee_layer_forward / ee_stack_forward need for
+ * `batch` sequences padded to `pad_len` holding at most `max_tokens` valid
+ * tokens (max_tokens < 0 means batch*pad_len).  Holds the offsets, the packed
+ * activations and every intermediate of one layer, 256-byte aligned. */
+EE_API ee_status ee_layer_workspace_size(const ee_layer* layer, int32_t batch, int32_t pad_len,
+                                  int64_t max_tokens, size_t* bytes);
+
+/* One layer: offsets, remove, the packed layer, rebuild.
+ *   x_padded  [batch, pad_len, H] device, layer dtype (pads may hold anything,
+ *             NaN included: no pad value reaches a valid row)
+ *   seq_lens  [batch] host int32 in [0, pad_len] (right padding)
+ *   y_padded  [batch, pad_len, H] device; valid rows = layer output,
+ *             pads = +0.0 (all zeros when every length is 0) */
+EE_API ee_status ee_layer_forward(ee_layer* layer, const void* x_padded, const int32_t* seq_lens,
+                           int32_t batch, int32_t pad_len, void* y_padded,
+                           void* workspace, size_t ws_bytes, void* stream);
+
+/* n_layers layers with one offsets/remove before and one rebuild after; the
+ * packed output of layer l is the input of layer l+1.  All layers must share
+ * one descriptor. */
+EE_API ee_status ee_stack_forward(ee_layer* const* layers, int32_t n_layers, const void* x_padded,
+                           const int32_t* seq_lens, int32_t batch, int32_t pad_len,
+                           void* y_padded, void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- offsets (the attention mask prefix-summed into token offsets) ------- */
+/* From host lengths.  Writes, on `stream`:
+ *   d_cu        [batch+1]        cu[0]=0, cu[b+1]=cu[b]+len[b]
+ *   d_token_src [batch*pad_len]  token_src[t] = b*pad_len + t - cu[b] for t < T
+ *                                (entries >= T are left untouched)
+ *   d_pad2pack  [batch*pad_len]  cu[b]+p for p < len[b], else -1
+ * and T = sum(len) into *total_tokens (host, computed before any device work). */
+EE_API ee_status ee_compute_offsets(const int32_t* seq_lens, int32_t batch, int32_t pad_len,
+                             int32_t* d_cu, int32_t* d_token_src, int32_t* d_pad2pack,
+                             int32_t* total_tokens, void* stream);
+
+/* From a device mask [batch, pad_len] (nonzero byte = valid token): its
+ * flattened exclusive prefix sum gives each valid position its packed index.
+ * Same outputs as above (any mask, not only right-padded ones); T goes to the
+ * device int32 *d_total.  batch*pad_len <= 2^31 - 1. */
+EE_API ee_status ee_compute_offsets_mask(const uint8_t* d_mask, int32_t batch, int32_t pad_len,
+                                  int32_t* d_cu, int32_t* d_token_src, int32_t* d_pad2pack,
+                                  int32_t* d_total, void* stream);
+
+/* ---- transpose_padding_remove / transpose_padding_rebuild --------------- */
+/* Bytes of workspace the two calls below need (the offsets arrays). */
+EE_API ee_status ee_padding_workspace_size(int32_t batch, int32_t pad_len, size_t* bytes);
+
+/* packed[t, :] = padded[token_src[t], :].  d_padded [batch, pad_len, hidden],
+ * d_packed [T, hidden] (T = sum(len)); hidden*sizeof(dtype) % 16 == 0. */
+EE_API ee_status ee_remove_padding(const void* d_padded, const int32_t* seq_lens, int32_t batch,
+                            int32_t pad_len, int32_t hidden, ee_dtype dtype, void* d_packed,
+                            void* workspace, size_t ws_bytes, void* stream);
+
+/* padded[r, :] = packed[pad2pack[r], :], or +0.0 where pad2pack[r] = -1. */
+EE_API ee_status ee_rebuild_padding(const void* d_packed, const int32_t* seq_lens, int32_t batch,
+                             int32_t pad_len, int32_t hidden, ee_dtype dtype, void* d_padded,
+                             void* workspace, size_t ws_bytes, void* stream);
+
+/* ---- the layer's operations on packed rows (each a step of the forward) ---- */
+/* y[r] = (x[r] - mean) / sqrt(var + eps) * gamma + beta per row, biased
+ * variance, fp32 statistics.  x, y [rows, hidden]; gamma, beta [hidden]. */
+EE_API ee_status ee_layernorm(const void* x, const void* gamma, const void* beta, int64_t rows,
+                       int32_t hidden, float eps, ee_dtype dtype, void* y, void* stream);
+
+/* C[M, N] = epilogue(A[M, K] . W[N, K]^T): bias [N], residual [M, N] (may not
+ * alias C).  fp16: MFMA kernels, fp32 accumulation, one rounding to fp16 at
+ * the end.  fp32: fp32 FMA kernels.  M may be 0 (no work). */
+EE_API ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual,
+                    int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
+                    ee_gelu gelu, void* C, void* stream);
+
+/* g[r, c] = gelu(u[r, c] + bias[c]): the standalone form of the FC1 epilogue
+ * (announcement article, "Ease of use" listing: add bias + activation). */
+EE_API ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t cols, ee_dtype dtype,
+                       ee_gelu gelu, void* g, void* stream);
+
+/* Causal attention per sequence over packed offsets.  qkv [T, 3H'] (q | k | v,
+ * head-major), d_cu [batch+1] device int32 (e.g. from ee_compute_offsets),
+ * o [T, H'].  Query i of sequence b attends to keys cu[b] .. cu[b]+i with
+ * weights softmax(q.k / sqrt(head_dim)); max_len >= every sequence length. */
+EE_API ee_status ee_attention_varlen(const void* qkv, const int32_t* d_cu, int32_t batch, int32_t max_len,
+                              int32_t n_heads, int32_t head_dim, int64_t total_tokens,
+                              ee_dtype dtype, void* o, void* stream);
+
+/* ---- per-kernel timing ----------------------------------------------------- */
+/* While enabled, every kernel that the calls above launch from this process is
+ * bracketed by a pair of hipEvents recorded on its launch stream. */
+typedef struct {
+  char name[32];      /* launch site, e.g. "gemm_fc1", "attention", "remove" */
+  int64_t launches;
+  double total_ms;    /* sum of event-measured durations */
+} ee_kernel_stat;
+
+EE_API ee_status ee_profile_enable(int32_t on);
+/* Waits for the recorded events, writes up to `capacity` per-site totals into
+ * `out` (host), sets *count, and clears the record. */
+EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EE_H_ */

@@ -1,0 +1,151 @@
+"""Whole-layer and stack parity of the HIP path against the CPU oracle's padded
+forward (the definition), through the C ABI, on seeded workloads.
+
+Bars: fp16 storage / fp32 accumulation: normwise max relative error <= 2e-2
+over valid rows; fp32: <= 1e-4; pads exactly +0.0; valid rows bit-identical
+whatever the pads hold (NaN included)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_padding_amd as ee
+import workloads
+from gpu_helpers import DEV, normwise_rel, say, to_host64, valid_mask
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_layer(w, lens, x, params, fuse_gelu=True, gelu=ee.GELU_TANH, layers_params=None):
+    dt = ee.F16 if w.dtype == "f16" else ee.F32
+    plist = layers_params or [params]
+    dev_params = [{k: v.to(DEV) for k, v in p.items()} for p in plist]
+    layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, dp, dtype=dt, gelu=gelu, fuse_gelu=fuse_gelu)
+              for dp in dev_params]
+    B, P, _ = x.shape
+    ws = torch.empty(layers[0].workspace_size(B, P, sum(lens)), dtype=torch.uint8, device=DEV)
+    xd = x.to(DEV)
+    y = torch.full_like(xd, 9.0)
+    if len(layers) == 1:
+        layers[0].forward(xd, lens, y, ws)
+    else:
+        ee.ee_stack_forward(layers, xd, lens, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def _check(w, lens, y, ref, tol, label):
+    got = to_host64(y)
+    m = valid_mask(lens, got.shape[1])
+    err = normwise_rel(got[m], ref[m]) if m.any() else 0.0
+    pads = got[~m]
+    say(f"{label}: T={sum(lens)} rel {err:.3e}")
+    assert np.all(pads == 0) and not np.any(np.signbit(pads)), "pads must be +0.0"
+    assert err <= tol, f"{label}: rel {err}"
+    return err
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2, 3, 4])
+@pytest.mark.parametrize("variant", ["init", "affine"])
+def test_tiny_fp32_layer(seed, variant):
+    w = workloads.get("tiny-fp32")
+    lens = workloads.lengths(w, seed)
+    x = workloads.activations(w, seed, w.batch, w.pad_len, lens)
+    p = workloads.layer_params(w, seed, 0, variant=variant)
+    y = _run_layer(w, lens, x, p)
+    ref = oracle.layer_forward_padded(x.double().numpy(), lens, p, w.n_heads, w.head_dim)
+    _check(w, lens, y, ref, 1e-4, f"tiny-fp32 seed={seed} {variant}")
+
+
+@pytest.mark.parametrize("seed,variant,fuse,gelu", [
+    (1234, "init", True, ee.GELU_TANH), (1234, "affine", True, ee.GELU_TANH),
+    (7, "affine", False, ee.GELU_TANH), (8, "affine", True, ee.GELU_ERF),
+])
+def test_gpt2_small_layer(seed, variant, fuse, gelu):
+    w = workloads.get("gpt2-small")
+    lens = workloads.lengths(w, seed)
+    x = workloads.activations(w, seed, w.batch, w.pad_len, lens)
+    p = workloads.layer_params(w, seed, 0, variant=variant)
+    y = _run_layer(w, lens, x, p, fuse_gelu=fuse, gelu=gelu)
+    ref = oracle.layer_forward_padded(x.double().numpy(), lens, p, w.n_heads, w.head_dim,
+                                      gelu_form="tanh" if gelu == ee.GELU_TANH else "erf")
+    _check(w, lens, y, ref, 2e-2, f"gpt2-small seed={seed} {variant} fuse={fuse} gelu={gelu}")
+
+
+@pytest.mark.parametrize("lens", [[0] * 8, [128] * 8, [1] * 8, [0, 128, 0, 1, 0, 77, 0, 0], [100]])
+def test_gpt2_small_edge_lengths(lens):
+    w = dataclasses.replace(workloads.get("gpt2-small"), batch=len(lens))
+    x = workloads.activations(w, 3, len(lens), w.pad_len, lens)
+    p = workloads.layer_params(w, 3, 0, variant="affine")
+    y = _run_layer(w, lens, x, p)
+    if sum(lens) == 0:
+        assert torch.all(y == 0) and not torch.any(torch.signbit(y))
+        return
+    ref = oracle.layer_forward_padded(x.double().numpy(), lens, p, w.n_heads, w.head_dim)
+    _check(w, lens, y, ref, 2e-2, f"gpt2-small lens={lens[:4]}...")
+
+
+def test_nan_pads_do_not_reach_valid_rows():
+    w = workloads.get("gpt2-small")
+    lens = workloads.lengths(w, 11)
+    p = workloads.layer_params(w, 11, 0, variant="affine")
+    x_r = workloads.activations(w, 11, w.batch, w.pad_len, lens)
+    x_n = workloads.activations(w, 11, w.batch, w.pad_len, lens, pad_fill="nan")
+    y_r = _run_layer(w, lens, x_r, p)
+    y_n = _run_layer(w, lens, x_n, p)
+    assert not torch.isnan(y_n).any()
+    assert torch.equal(y_r, y_n)
+
+
+def test_each_sequence_alone_matches_batch():
+    """Sequences are independent: running one alone, unpadded, gives its rows of
+    the batch (same kernels; compared to the oracle bound, not bitwise, since the
+    GEMM tiling of T rows differs)."""
+    w = workloads.get("gpt2-small")
+    lens = workloads.lengths(w, 21)
+    x = workloads.activations(w, 21, w.batch, w.pad_len, lens)
+    p = workloads.layer_params(w, 21, 0, variant="affine")
+    y = to_host64(_run_layer(w, lens, x, p))
+    for b in (0, 5):
+        n = lens[b]
+        w1 = dataclasses.replace(w, batch=1, pad_len=n)
+        y1 = to_host64(_run_layer(w1, [n], x[b:b + 1, :n].contiguous(), p))
+        assert normwise_rel(y1[0], y[b, :n]) <= 5e-3
+
+
+def test_stack_matches_oracle():
+    w = dataclasses.replace(workloads.get("gpt2-small"), batch=6, layers=3)
+    lens = [128, 1, 77, 0, 100, 64]
+    x = workloads.activations(w, 5, w.batch, w.pad_len, lens)
+    ps = [workloads.layer_params(w, 5, l, variant="affine") for l in range(3)]
+    y = _run_layer(w, lens, x, None, layers_params=ps)
+    ref = oracle.stack_forward_packed(x.double().numpy(), lens, ps, w.n_heads, w.head_dim)
+    _check(w, lens, y, ref, 2e-2, "gpt2-small 3-layer stack")
+
+
+def test_tiny_fp32_stack_matches_padded_definition():
+    w = workloads.get("tiny-fp32")
+    lens = workloads.lengths(w, 9)
+    x = workloads.activations(w, 9, w.batch, w.pad_len, lens)
+    ps = [workloads.layer_params(w, 9, l, variant="affine") for l in range(4)]
+    y = _run_layer(w, lens, x, None, layers_params=ps)
+    ref = oracle.stack_forward_padded(x.double().numpy(), lens, ps, w.n_heads, w.head_dim)
+    _check(w, lens, y, ref, 1e-4, "tiny-fp32 4-layer stack")
+
+
+def test_profile_records_every_launch_site():
+    w = workloads.get("gpt2-small")
+    lens = workloads.lengths(w, 1)
+    x = workloads.activations(w, 1, w.batch, w.pad_len, lens)
+    p = workloads.layer_params(w, 1, 0)
+    ee.ee_profile_enable(True)
+    try:
+        _run_layer(w, lens, x, p)
+        stats = ee.ee_profile_collect()
+    finally:
+        ee.ee_profile_enable(False)
+    for site in ("offsets", "remove", "ln1", "gemm_qkv", "attention", "gemm_out", "ln2", "gemm_fc1", "gemm_fc2",
+                 "rebuild"):
+        assert stats[site]["launches"] == 1 and stats[site]["total_ms"] > 0

@@ -1,0 +1,250 @@
+"""Per-kernel parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bars: bit-exact for offsets, indices and remove/rebuild; bit-exact for the
+integer-valued GEMM test; otherwise a normwise relative error bound derived
+from fp16 output rounding (2^-11 relative, plus fp32 accumulation), written
+in each test."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_padding_amd as ee
+from gpu_helpers import DEV, normwise_rel, say, to_host64, valid_mask
+
+pytestmark = pytest.mark.gpu
+
+GEN = torch.Generator().manual_seed(20240607)
+
+
+def _i32(n):
+    return torch.empty(max(1, n), dtype=torch.int32, device=DEV)
+
+
+# ------------------------------------------------------------------ offsets
+LEN_CASES = [
+    ([2, 0, 3], 4), ([1] * 7, 5), ([9] * 3, 9), ([0, 0, 0], 6), ([5], 5), ([0], 3),
+    ([0, 128, 1, 64, 127, 128, 33, 2], 128),
+]
+
+
+def _rand_lens(B, P, seed, lo=0):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randint(lo, P + 1, (B,), generator=g).tolist()
+
+
+@pytest.mark.parametrize("lens,P", LEN_CASES + [(_rand_lens(512, 256, 1), 256), (_rand_lens(64, 3000, 2), 3000)])
+def test_offsets_bit_exact(lens, P):
+    B = len(lens)
+    cu, src, p2p = _i32(B + 1), _i32(B * P), _i32(B * P)
+    src.fill_(-7)
+    T = ee.ee_compute_offsets(lens, P, cu, src, p2p)
+    torch.cuda.synchronize()
+    rcu, rsrc, rp2p, rT = oracle.offsets_from_lengths(lens, P)
+    assert T == rT
+    assert cu.cpu().tolist() == rcu.tolist()
+    assert p2p.cpu().tolist() == rp2p.tolist()
+    assert src.cpu()[:T].tolist() == rsrc.tolist()
+    assert torch.all(src.cpu()[T:] == -7)   # entries past T untouched
+
+
+@pytest.mark.parametrize("lens,P", LEN_CASES + [(_rand_lens(64, 256, 3), 256), (_rand_lens(40, 1000, 4), 1000)])
+def test_offsets_from_mask_bit_exact(lens, P):
+    B = len(lens)
+    mask = torch.tensor(valid_mask(lens, P).astype(np.uint8), device=DEV)
+    cu, src, p2p, tot = _i32(B + 1), _i32(B * P), _i32(B * P), _i32(1)
+    ee.ee_compute_offsets_mask(mask, cu, src, p2p, tot)
+    torch.cuda.synchronize()
+    rcu, rsrc, rp2p, rT = oracle.offsets_from_mask(mask.cpu().numpy())
+    assert int(tot.item()) == rT == sum(lens)
+    assert cu.cpu().tolist() == rcu.tolist()
+    assert p2p.cpu().tolist() == rp2p.tolist()
+    assert src.cpu()[:rT].tolist() == rsrc.tolist()
+
+
+def test_offsets_from_general_mask():
+    g = torch.Generator().manual_seed(5)
+    m = (torch.rand(33, 77, generator=g) < 0.4).to(torch.uint8)
+    B, P = m.shape
+    cu, src, p2p, tot = _i32(B + 1), _i32(B * P), _i32(B * P), _i32(1)
+    ee.ee_compute_offsets_mask(m.to(DEV), cu, src, p2p, tot)
+    torch.cuda.synchronize()
+    rcu, rsrc, rp2p, rT = oracle.offsets_from_mask(m.numpy())
+    assert int(tot.item()) == rT
+    assert cu.cpu().tolist() == rcu.tolist() and p2p.cpu().tolist() == rp2p.tolist()
+    assert src.cpu()[:rT].tolist() == rsrc.tolist()
+
+
+# ------------------------------------------------------------------ remove / rebuild
+@pytest.mark.parametrize("dtype,H", [(torch.float16, 768), (torch.float16, 12288), (torch.float32, 64),
+                                     (torch.float16, 8), (torch.float32, 1028)])
+@pytest.mark.parametrize("lens,P", [([3, 0, 16, 1, 9], 16), ([128] * 4, 256), ([0, 0], 4), ([7], 7)])
+def test_remove_rebuild_bit_exact(dtype, H, lens, P):
+    B = len(lens)
+    x = torch.randn(B, P, H, generator=GEN).to(dtype)
+    mask = valid_mask(lens, P)
+    x[torch.from_numpy(~mask)] = float("nan")          # pads must never reach the output
+    xd = x.to(DEV)
+    T = sum(lens)
+    packed = torch.full((max(T, 1), H), 3.0, dtype=dtype, device=DEV)
+    ws = torch.empty(ee.ee_padding_workspace_size(B, P), dtype=torch.uint8, device=DEV)
+    ee.ee_remove_padding(xd, lens, packed, ws)
+    y = torch.full((B, P, H), 5.0, dtype=dtype, device=DEV)
+    ee.ee_rebuild_padding(packed, lens, y, ws)
+    torch.cuda.synchronize()
+    xn = x.numpy()
+    ref_packed = oracle.remove_padding(xn, lens)
+    if T:
+        assert np.array_equal(packed.cpu().numpy()[:T].view(np.uint8), ref_packed.view(np.uint8))
+    yr = y.cpu().numpy()
+    ref_y = oracle.rebuild_padding(ref_packed, lens, P)
+    assert np.array_equal(yr.view(np.uint8), ref_y.view(np.uint8))      # +0.0 pads, bit for bit
+    assert not np.isnan(yr).any()
+
+
+# ------------------------------------------------------------------ LayerNorm
+@pytest.mark.parametrize("dtype,H,rows,tol", [
+    (torch.float16, 768, 37, 2e-3), (torch.float16, 12288, 19, 2e-3), (torch.float16, 64, 300, 2e-3),
+    (torch.float32, 64, 33, 1e-5), (torch.float32, 12288, 7, 1e-5), (torch.float16, 4096, 5, 2e-3),
+])
+def test_layernorm_parity(dtype, H, rows, tol):
+    x = (torch.randn(rows, H, generator=GEN) * 3 + 0.7).to(dtype)
+    g = (1 + 0.1 * torch.randn(H, generator=GEN)).to(dtype)
+    b = (0.1 * torch.randn(H, generator=GEN)).to(dtype)
+    y = torch.empty(rows, H, dtype=dtype, device=DEV)
+    ee.ee_layernorm(x.to(DEV), g.to(DEV), b.to(DEV), 1e-5, y)
+    torch.cuda.synchronize()
+    ref = oracle.layer_norm(x.double().numpy(), g.double().numpy(), b.double().numpy(), 1e-5)
+    err = normwise_rel(to_host64(y), ref)
+    say(f"layernorm {dtype} H={H}: rel {err:.2e}")
+    assert err <= tol
+
+
+# ------------------------------------------------------------------ GEMM
+def _small_ints(shape, lo=-2, hi=2):
+    return torch.randint(lo, hi + 1, shape, generator=GEN).to(torch.float16)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 64), (37, 96, 128), (300, 256, 192), (516, 2304, 768),
+                                   (1000, 1000, 640), (4112, 768, 3072), (2048, 4096, 12288),
+                                   (4100, 4200, 320), (4096, 4096, 1024)])
+@pytest.mark.parametrize("epi", [ee.EPI_NONE, ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL])
+def test_gemm_integer_exact(M, N, K, epi):
+    """Small-integer fp16 operands: every product and partial sum is an integer
+    below 2^24, exact in fp32 in any order, so the only rounding is the final
+    fp32 -> fp16 one; the result must equal the fp16 rounding (nearest-even) of
+    the exact sum, bit for bit."""
+    A, W = _small_ints((M, K)), _small_ints((N, K))
+    bias = _small_ints((N,)) if epi != ee.EPI_NONE else None
+    R = _small_ints((M, N), -8, 8) if epi == ee.EPI_BIAS_RESIDUAL else None
+    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    ee.ee_linear(A.to(DEV), W.to(DEV), None if bias is None else bias.to(DEV), None if R is None else R.to(DEV),
+                 epi, C)
+    torch.cuda.synchronize()
+    exact = A.double().numpy() @ W.double().numpy().T
+    if bias is not None:
+        exact = exact + bias.double().numpy()
+    if R is not None:
+        exact = exact + R.double().numpy()
+    assert np.abs(exact).max() < 2 ** 24
+    ref16 = exact.astype(np.float16)
+    got = C.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), ref16.view(np.uint16)), \
+        f"{np.count_nonzero(got != ref16)} of {got.size} differ"
+
+
+@pytest.mark.parametrize("M,N,K,epi,gelu", [
+    (129, 768, 768, ee.EPI_BIAS_GELU, ee.GELU_TANH), (516, 3072, 768, ee.EPI_BIAS_GELU, ee.GELU_ERF),
+    (4100, 1024, 1024, ee.EPI_BIAS_GELU, ee.GELU_TANH), (77, 2304, 768, ee.EPI_BIAS, ee.GELU_TANH),
+])
+def test_gemm_f16_random_parity(M, N, K, epi, gelu):
+    A = torch.randn(M, K, generator=GEN).to(torch.float16)
+    W = (0.02 * torch.randn(N, K, generator=GEN)).to(torch.float16)
+    bias = (0.1 * torch.randn(N, generator=GEN)).to(torch.float16)
+    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    ee.ee_linear(A.to(DEV), W.to(DEV), bias.to(DEV), None, epi, C, gelu=gelu)
+    torch.cuda.synchronize()
+    u = oracle.linear(A.double().numpy(), W.double().numpy(), bias.double().numpy())
+    ref = oracle.gelu(u, "tanh" if gelu == ee.GELU_TANH else "erf") if epi == ee.EPI_BIAS_GELU else u
+    err = normwise_rel(to_host64(C), ref)
+    say(f"gemm f16 {M}x{N}x{K} epi={epi}: rel {err:.2e}")
+    assert err <= 2e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 7, 3), (64, 256, 64), (100, 70, 130)])
+@pytest.mark.parametrize("epi", [ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL, ee.EPI_BIAS_GELU])
+def test_gemm_f32_parity(M, N, K, epi):
+    A = torch.randn(M, K, generator=GEN)
+    W = 0.1 * torch.randn(N, K, generator=GEN)
+    bias = torch.randn(N, generator=GEN)
+    R = torch.randn(M, N, generator=GEN)
+    C = torch.empty(M, N, device=DEV)
+    ee.ee_linear(A.to(DEV), W.to(DEV), bias.to(DEV), R.to(DEV) if epi == ee.EPI_BIAS_RESIDUAL else None, epi, C)
+    torch.cuda.synchronize()
+    ref = oracle.linear(A.double().numpy(), W.double().numpy(), bias.double().numpy())
+    if epi == ee.EPI_BIAS_RESIDUAL:
+        ref = ref + R.double().numpy()
+    if epi == ee.EPI_BIAS_GELU:
+        ref = oracle.gelu(ref)
+    assert normwise_rel(to_host64(C), ref) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype,tol", [(torch.float16, 2e-3), (torch.float32, 1e-6)])
+@pytest.mark.parametrize("gelu", [ee.GELU_TANH, ee.GELU_ERF])
+def test_bias_gelu_parity(dtype, tol, gelu):
+    u = (2 * torch.randn(300, 3072, generator=GEN)).to(dtype)
+    b = torch.randn(3072, generator=GEN).to(dtype)
+    g = torch.empty_like(u, device=DEV)
+    ee.ee_bias_gelu(u.to(DEV), b.to(DEV), g, gelu=gelu)
+    torch.cuda.synchronize()
+    ref = oracle.gelu(u.double().numpy() + b.double().numpy(), "tanh" if gelu == ee.GELU_TANH else "erf")
+    assert normwise_rel(to_host64(g), ref) <= tol
+
+
+# ------------------------------------------------------------------ attention
+ATTN_LENS = [1, 31, 32, 33, 127, 128, 129, 200, 256, 5]
+
+
+@pytest.mark.parametrize("dtype,hd,nh,tol", [
+    (torch.float16, 128, 2, 3e-3), (torch.float16, 64, 3, 3e-3), (torch.float16, 32, 2, 3e-3),
+    (torch.float16, 16, 4, 3e-3), (torch.float32, 16, 4, 1e-5), (torch.float32, 64, 2, 1e-5),
+    (torch.float32, 128, 1, 1e-5),
+])
+def test_attention_varlen_parity(dtype, hd, nh, tol):
+    lens = ATTN_LENS
+    cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu_h[-1])
+    qkv = torch.randn(T, 3 * nh * hd, generator=GEN).to(dtype)
+    o = torch.full((T, nh * hd), 7.0, dtype=dtype, device=DEV)
+    cu = torch.tensor(cu_h, device=DEV)
+    ee.ee_attention_varlen(qkv.to(DEV), cu, len(lens), max(lens), nh, hd, o)
+    torch.cuda.synchronize()
+    ref = oracle.causal_attention_packed(qkv.double().numpy(), cu_h, nh, hd)
+    got = to_host64(o)
+    err = normwise_rel(got, ref)
+    say(f"attention {dtype} hd={hd} nh={nh}: rel {err:.2e}")
+    assert err <= tol
+    # query 0 of every sequence sees only key 0: o = v0 (up to the output rounding)
+    Hp = nh * hd
+    v = qkv.double().numpy()[:, 2 * Hp:]
+    for b in range(len(lens)):
+        assert np.allclose(got[cu_h[b]], v[cu_h[b]], rtol=1e-3 if dtype == torch.float16 else 1e-6, atol=1e-6)
+
+
+def test_attention_sequences_are_independent():
+    """Permuting the sequences of the batch permutes the output rows exactly."""
+    nh, hd = 4, 128
+    lens = [100, 3, 256, 40]
+    cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    qkv = torch.randn(int(cu_h[-1]), 3 * nh * hd, generator=GEN).half()
+    o = torch.empty(int(cu_h[-1]), nh * hd, dtype=torch.float16, device=DEV)
+    ee.ee_attention_varlen(qkv.to(DEV), torch.tensor(cu_h, device=DEV), 4, 256, nh, hd, o)
+    perm = [2, 0, 3, 1]
+    lp = [lens[i] for i in perm]
+    cu_p = np.concatenate([[0], np.cumsum(lp)]).astype(np.int32)
+    qkv_p = torch.cat([qkv[cu_h[i]:cu_h[i + 1]] for i in perm])
+    o_p = torch.empty_like(o)
+    ee.ee_attention_varlen(qkv_p.to(DEV), torch.tensor(cu_p, device=DEV), 4, 256, nh, hd, o_p)
+    torch.cuda.synchronize()
+    for j, i in enumerate(perm):
+        assert torch.equal(o_p[cu_p[j]:cu_p[j + 1]], o[cu_h[i]:cu_h[i + 1]])

@@ -1,0 +1,255 @@
+"""Python binding of libee (include/ee.h): argument marshalling only.
+
+Every function here converts torch tensors / Python values into the C ABI's
+plain pointers and sizes and calls libee; all work of the padding-removed layer
+forward runs in libee's HIP kernels.  torch supplies device memory and streams.
+There is no fallback: if libee.so is not built, loading raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, List, Optional, Sequence
+
+__all__ = [
+    "EEError", "lib", "F32", "F16", "GELU_TANH", "GELU_ERF",
+    "EPI_NONE", "EPI_BIAS", "EPI_BIAS_RESIDUAL", "EPI_BIAS_GELU",
+    "ee_compute_offsets", "ee_compute_offsets_mask", "ee_padding_workspace_size",
+    "ee_remove_padding", "ee_rebuild_padding", "ee_layernorm", "ee_linear", "ee_bias_gelu",
+    "ee_attention_varlen", "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_collect",
+    "EXPORTED_SYMBOLS", "lib_path",
+]
+
+F32, F16 = 0, 1
+GELU_TANH, GELU_ERF = 0, 1
+EPI_NONE, EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3
+MAX_BATCH = 512
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, "libee.so")
+
+
+class EEError(RuntimeError):
+    def __init__(self, status: int, func: str, msg: str):
+        super().__init__(f"{func}: {_STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_STATUS = {0: "EE_OK", 1: "EE_ERR_INVALID_ARG", 2: "EE_ERR_UNSUPPORTED", 3: "EE_ERR_WORKSPACE",
+           4: "EE_ERR_OOM", 5: "EE_ERR_HIP"}
+
+
+class LayerDesc(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
+                ("ln_eps", C.c_float), ("dtype", C.c_int), ("gelu", C.c_int), ("fuse_gelu", C.c_int32)]
+
+
+WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_out", "b_out",
+                 "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
+
+
+class LayerWeights(C.Structure):
+    _fields_ = [(n, C.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class KernelStat(C.Structure):
+    _fields_ = [("name", C.c_char * 32), ("launches", C.c_int64), ("total_ms", C.c_double)]
+
+
+_VP, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
+_PI32 = C.POINTER(C.c_int32)
+
+# name -> (restype, argtypes); the list of exported functions of include/ee.h
+_SIGS = {
+    "ee_status_string": (C.c_char_p, [C.c_int]),
+    "ee_last_error": (C.c_char_p, []),
+    "ee_version": (C.c_char_p, []),
+    "ee_layer_create": (C.c_int, [C.POINTER(LayerDesc), C.POINTER(LayerWeights), C.POINTER(_VP)]),
+    "ee_layer_destroy": (C.c_int, [_VP]),
+    "ee_layer_workspace_size": (C.c_int, [_VP, _I32, _I32, _I64, C.POINTER(_SZ)]),
+    "ee_layer_forward": (C.c_int, [_VP, _VP, _PI32, _I32, _I32, _VP, _VP, _SZ, _VP]),
+    "ee_stack_forward": (C.c_int, [C.POINTER(_VP), _I32, _VP, _PI32, _I32, _I32, _VP, _VP, _SZ, _VP]),
+    "ee_compute_offsets": (C.c_int, [_PI32, _I32, _I32, _VP, _VP, _VP, _PI32, _VP]),
+    "ee_compute_offsets_mask": (C.c_int, [_VP, _I32, _I32, _VP, _VP, _VP, _VP, _VP]),
+    "ee_padding_workspace_size": (C.c_int, [_I32, _I32, C.POINTER(_SZ)]),
+    "ee_remove_padding": (C.c_int, [_VP, _PI32, _I32, _I32, _I32, C.c_int, _VP, _VP, _SZ, _VP]),
+    "ee_rebuild_padding": (C.c_int, [_VP, _PI32, _I32, _I32, _I32, C.c_int, _VP, _VP, _SZ, _VP]),
+    "ee_layernorm": (C.c_int, [_VP, _VP, _VP, _I64, _I32, C.c_float, C.c_int, _VP, _VP]),
+    "ee_linear": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP, _VP]),
+    "ee_bias_gelu": (C.c_int, [_VP, _VP, _I64, _I32, C.c_int, C.c_int, _VP, _VP]),
+    "ee_attention_varlen": (C.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I64, C.c_int, _VP, _VP]),
+    "ee_profile_enable": (C.c_int, [_I32]),
+    "ee_profile_collect": (C.c_int, [C.POINTER(KernelStat), _I32, _PI32]),
+}
+EXPORTED_SYMBOLS = tuple(_SIGS)
+
+_lib = None
+
+
+def lib():
+    """The loaded libee (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built; run `python -m variable_length_padding_amd.build`")
+        L = C.CDLL(path)
+        for name, (res, args) in _SIGS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(status: int, func: str):
+    if status != 0:
+        raise EEError(status, func, lib().ee_last_error().decode())
+
+
+# ---------------------------------------------------------------- helpers
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _lens(lens: Sequence[int]):
+    arr = (C.c_int32 * max(1, len(lens)))(*[int(n) for n in lens])
+    return arr
+
+
+# ---------------------------------------------------------------- offsets
+def ee_compute_offsets(lens: Sequence[int], pad_len: int, cu, token_src, pad2pack, stream=None) -> int:
+    """Host lengths -> device cu [B+1], token_src [B*P], pad2pack [B*P] (int32); returns T."""
+    total = C.c_int32(0)
+    _check(lib().ee_compute_offsets(_lens(lens), len(lens), pad_len, _ptr(cu), _ptr(token_src), _ptr(pad2pack),
+                                    C.byref(total), _stream(stream)), "ee_compute_offsets")
+    return total.value
+
+
+def ee_compute_offsets_mask(mask, cu, token_src, pad2pack, total, stream=None):
+    """Device uint8 mask [B, P] -> cu, token_src, pad2pack, total (device int32)."""
+    B, P = mask.shape
+    _check(lib().ee_compute_offsets_mask(_ptr(mask), B, P, _ptr(cu), _ptr(token_src), _ptr(pad2pack), _ptr(total),
+                                         _stream(stream)), "ee_compute_offsets_mask")
+
+
+def ee_padding_workspace_size(batch: int, pad_len: int) -> int:
+    n = C.c_size_t(0)
+    _check(lib().ee_padding_workspace_size(batch, pad_len, C.byref(n)), "ee_padding_workspace_size")
+    return n.value
+
+
+def ee_remove_padding(padded, lens: Sequence[int], packed, workspace, stream=None):
+    B, P, H = padded.shape
+    _check(lib().ee_remove_padding(_ptr(padded), _lens(lens), B, P, H, _dtype_code(padded), _ptr(packed),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "ee_remove_padding")
+
+
+def ee_rebuild_padding(packed, lens: Sequence[int], padded, workspace, stream=None):
+    B, P, H = padded.shape
+    _check(lib().ee_rebuild_padding(_ptr(packed), _lens(lens), B, P, H, _dtype_code(padded), _ptr(padded),
+                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
+           "ee_rebuild_padding")
+
+
+# ---------------------------------------------------------------- row ops
+def ee_layernorm(x, gamma, beta, eps: float, y, stream=None):
+    rows, H = x.shape
+    _check(lib().ee_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), rows, H, eps, _dtype_code(x), _ptr(y),
+                              _stream(stream)), "ee_layernorm")
+
+
+def ee_linear(A, W, bias, residual, epi: int, C_out, gelu: int = GELU_TANH, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().ee_linear(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
+                           _ptr(C_out), _stream(stream)), "ee_linear")
+
+
+def ee_bias_gelu(u, bias, g, gelu: int = GELU_TANH, stream=None):
+    rows, cols = u.shape
+    _check(lib().ee_bias_gelu(_ptr(u), _ptr(bias), rows, cols, _dtype_code(u), gelu, _ptr(g), _stream(stream)),
+           "ee_bias_gelu")
+
+
+def ee_attention_varlen(qkv, cu, batch: int, max_len: int, n_heads: int, head_dim: int, o, stream=None):
+    _check(lib().ee_attention_varlen(_ptr(qkv), _ptr(cu), batch, max_len, n_heads, head_dim, qkv.shape[0],
+                                     _dtype_code(qkv), _ptr(o), _stream(stream)), "ee_attention_varlen")
+
+
+# ---------------------------------------------------------------- layer
+class Layer:
+    """A layer handle: borrows the weight tensors (kept alive by this object)."""
+
+    def __init__(self, hidden: int, n_heads: int, head_dim: int, ffn: int, weights: Dict, dtype: int = F16,
+                 ln_eps: float = 1e-5, gelu: int = GELU_TANH, fuse_gelu: bool = True):
+        self.desc = LayerDesc(hidden, n_heads, head_dim, ffn, ln_eps, dtype, gelu, 1 if fuse_gelu else 0)
+        self._weights = {k: weights[k] for k in WEIGHT_FIELDS}
+        w = LayerWeights(*[_ptr(self._weights[k]) for k in WEIGHT_FIELDS])
+        h = C.c_void_p()
+        _check(lib().ee_layer_create(C.byref(self.desc), C.byref(w), C.byref(h)), "ee_layer_create")
+        self.handle = h
+
+    def workspace_size(self, batch: int, pad_len: int, max_tokens: int = -1) -> int:
+        n = C.c_size_t(0)
+        _check(lib().ee_layer_workspace_size(self.handle, batch, pad_len, max_tokens, C.byref(n)),
+               "ee_layer_workspace_size")
+        return n.value
+
+    def forward(self, x, lens: Sequence[int], y, workspace, stream=None):
+        B, P, _ = x.shape
+        _check(lib().ee_layer_forward(self.handle, _ptr(x), _lens(lens), B, P, _ptr(y), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream)),
+               "ee_layer_forward")
+
+    def close(self):
+        if self.handle:
+            lib().ee_layer_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def ee_stack_forward(layers: List[Layer], x, lens: Sequence[int], y, workspace, stream=None):
+    B, P, _ = x.shape
+    arr = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
+    _check(lib().ee_stack_forward(arr, len(layers), _ptr(x), _lens(lens), B, P, _ptr(y), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(stream)), "ee_stack_forward")
+
+
+# ---------------------------------------------------------------- timing
+def ee_profile_enable(on: bool = True):
+    _check(lib().ee_profile_enable(1 if on else 0), "ee_profile_enable")
+
+
+def ee_profile_collect() -> Dict[str, Dict[str, float]]:
+    cap = 64
+    arr = (KernelStat * cap)()
+    n = C.c_int32(0)
+    _check(lib().ee_profile_collect(arr, cap, C.byref(n)), "ee_profile_collect")
+    return {arr[i].name.decode(): {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms)}
+            for i in range(n.value)}

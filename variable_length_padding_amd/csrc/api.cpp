@@ -1,0 +1,569 @@
+// C ABI of libee (declared in include/ee.h): host-side validation, workspace
+// planning, kernel sequencing and per-launch event timing.  Every check runs
+// before the first HIP call of an entry point, so a rejected call enqueues
+// nothing.  The forward path allocates nothing and never synchronises.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <new>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "ee.h"
+#include "internal.h"
+
+using namespace ee;
+
+struct ee_layer {
+  ee_layer_desc desc;
+  ee_layer_weights w;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+ee_status fail(ee_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return s;
+}
+
+ee_status hip_fail(hipError_t e, const char* what) {
+  return fail(EE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+}
+
+size_t dtype_size(ee_dtype d) { return d == EE_F16 ? 2 : 4; }
+bool dtype_ok(int d) { return d == EE_F32 || d == EE_F16; }
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ee_status check_ptr(const void* p, const char* name) {
+  if (!p) return fail(EE_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(EE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return EE_OK;
+}
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+#define EE_TRY(expr)                 \
+  do {                               \
+    const ee_status s_ = (expr);     \
+    if (s_ != EE_OK) return s_;      \
+  } while (0)
+
+// ---------------------------------------------------------------- profiling
+struct Profiler {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  size_t used = 0;
+  std::vector<std::pair<std::string, size_t>> recs;  // (site, pool index)
+};
+Profiler& prof() {
+  static Profiler* p = new Profiler();  // never destroyed: events may outlive static teardown order
+  return *p;
+}
+
+// Runs `launch` (which returns the launch's hipError_t); while profiling is on,
+// brackets it with two events recorded on `s`.
+template <class F>
+hipError_t timed(const char* site, hipStream_t s, F&& launch) {
+  Profiler& p = prof();
+  if (!p.on) return launch();
+  std::lock_guard<std::mutex> lk(p.mu);
+  if (p.used == p.pool.size()) {
+    std::pair<hipEvent_t, hipEvent_t> e{};
+    hipError_t r = hipEventCreate(&e.first);
+    if (r == hipSuccess) r = hipEventCreate(&e.second);
+    if (r != hipSuccess) return r;
+    p.pool.push_back(e);
+  }
+  const size_t i = p.used++;
+  hipError_t r = hipEventRecord(p.pool[i].first, s);
+  if (r != hipSuccess) return r;
+  r = launch();
+  if (r != hipSuccess) return r;
+  r = hipEventRecord(p.pool[i].second, s);
+  if (r != hipSuccess) return r;
+  p.recs.emplace_back(site, i);
+  return hipSuccess;
+}
+
+#define EE_LAUNCH(site, stream, call)                                        \
+  do {                                                                       \
+    const hipError_t e_ = timed(site, stream, [&]() { return (call); });    \
+    if (e_ != hipSuccess) return hip_fail(e_, site);                         \
+  } while (0)
+
+// ---------------------------------------------------------------- validation
+ee_status check_lengths(const int32_t* lens, int32_t B, int32_t P, int64_t* total, int32_t* max_len) {
+  if (!lens) return fail(EE_ERR_INVALID_ARG, "seq_lens is NULL");
+  if (B < 1 || B > EE_MAX_BATCH) return fail(EE_ERR_INVALID_ARG, "batch %d outside [1, %d]", B, EE_MAX_BATCH);
+  if (P < 1) return fail(EE_ERR_INVALID_ARG, "pad_len %d < 1", P);
+  if ((int64_t)B * P > INT32_MAX) return fail(EE_ERR_INVALID_ARG, "batch*pad_len exceeds 2^31-1");
+  int64_t T = 0;
+  int32_t mx = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    if (lens[b] < 0 || lens[b] > P)
+      return fail(EE_ERR_INVALID_ARG, "seq_lens[%d] = %d outside [0, pad_len=%d]", b, lens[b], P);
+    T += lens[b];
+    mx = std::max(mx, lens[b]);
+  }
+  *total = T;
+  if (max_len) *max_len = mx;
+  return EE_OK;
+}
+
+ee_status check_desc(const ee_layer_desc* d) {
+  if (!d) return fail(EE_ERR_INVALID_ARG, "desc is NULL");
+  if (!dtype_ok(d->dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
+  if (d->gelu != EE_GELU_TANH && d->gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)d->gelu);
+  if (d->fuse_gelu != 0 && d->fuse_gelu != 1) return fail(EE_ERR_INVALID_ARG, "fuse_gelu must be 0 or 1");
+  if (d->hidden < 1 || d->n_heads < 1 || d->ffn < 1)
+    return fail(EE_ERR_INVALID_ARG, "hidden, n_heads and ffn must be >= 1");
+  if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps)) return fail(EE_ERR_INVALID_ARG, "ln_eps must be finite and > 0");
+  const int hd = d->head_dim;
+  if (hd != 16 && hd != 32 && hd != 64 && hd != 128)
+    return fail(EE_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", hd);
+  if (d->n_heads > 65535) return fail(EE_ERR_UNSUPPORTED, "n_heads %d > 65535", d->n_heads);
+  const size_t s = dtype_size(d->dtype);
+  if ((size_t)d->hidden * s % 16 || (size_t)d->ffn * s % 16)
+    return fail(EE_ERR_UNSUPPORTED, "hidden and ffn rows must be multiples of 16 bytes");
+  if (d->hidden > layernorm_max_hidden(d->dtype))
+    return fail(EE_ERR_UNSUPPORTED, "hidden %d above the LayerNorm kernel's %d", d->hidden,
+                layernorm_max_hidden(d->dtype));
+  if ((int64_t)d->n_heads * hd > (1 << 24) || d->ffn > (1 << 24) || d->hidden > (1 << 24))
+    return fail(EE_ERR_UNSUPPORTED, "layer dimension too large");
+  return EE_OK;
+}
+
+bool desc_equal(const ee_layer_desc& a, const ee_layer_desc& b) {
+  return a.hidden == b.hidden && a.n_heads == b.n_heads && a.head_dim == b.head_dim && a.ffn == b.ffn &&
+         a.ln_eps == b.ln_eps && a.dtype == b.dtype && a.gelu == b.gelu && a.fuse_gelu == b.fuse_gelu;
+}
+
+// ---------------------------------------------------------------- workspace
+struct Plan {
+  size_t cu, token_src, pad2pack, x, ln, big, o, h, total;
+};
+
+Plan plan_offsets_only(int32_t B, int32_t P) {
+  Plan p{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off += align256(n);
+    return o;
+  };
+  p.cu = take(4 * (size_t)(B + 1));
+  p.token_src = take(4 * (size_t)B * P);
+  p.pad2pack = take(4 * (size_t)B * P);
+  p.total = off;
+  return p;
+}
+
+Plan plan_layer(const ee_layer_desc& d, int32_t B, int32_t P, int64_t T) {
+  Plan p = plan_offsets_only(B, P);
+  size_t off = p.total;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off += align256(n);
+    return o;
+  };
+  const size_t s = dtype_size(d.dtype), t = (size_t)T;
+  const size_t H = d.hidden, Hp = (size_t)d.n_heads * d.head_dim, F = d.ffn;
+  p.x = take(t * H * s);
+  p.ln = take(t * H * s);
+  p.big = take(t * std::max(3 * Hp, F) * s);
+  p.o = take(t * Hp * s);
+  p.h = take(t * H * s);
+  p.total = off;
+  return p;
+}
+
+char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
+
+// ---------------------------------------------------------------- launch helpers
+hipError_t gemm(ee_dtype dt, const void* A, const void* W, const void* bias, const void* R, int64_t M, int N, int K,
+                ee_epilogue epi, ee_gelu g, void* C, hipStream_t s) {
+  if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K)) return launch_gemm_f16_mfma(A, W, bias, R, M, N, K, epi, g, C, s);
+  return launch_gemm_valu(dt, A, W, bias, R, M, N, K, epi, g, C, s);
+}
+
+ee_status offsets_from_host(const int32_t* lens, int32_t B, int32_t P, int32_t* cu, int32_t* token_src,
+                            int32_t* pad2pack, hipStream_t s) {
+  LensArg la;
+  std::memset(&la, 0, sizeof la);
+  std::memcpy(la.v, lens, sizeof(int32_t) * (size_t)B);
+  EE_LAUNCH("offsets", s, launch_offsets(la, B, P, cu, token_src, pad2pack, s));
+  return EE_OK;
+}
+
+// The packed layer on T rows held in ws.x; the output replaces ws.x.
+ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, int32_t B, int32_t max_len,
+                       hipStream_t s) {
+  const ee_layer_desc& d = L->desc;
+  const ee_layer_weights& w = L->w;
+  const int H = d.hidden, Hp = d.n_heads * d.head_dim, F = d.ffn;
+  void* x = at(ws, p.x);
+  void* ln = at(ws, p.ln);
+  void* big = at(ws, p.big);
+  void* o = at(ws, p.o);
+  void* h = at(ws, p.h);
+  const int32_t* cu = reinterpret_cast<const int32_t*>(at(ws, p.cu));
+  EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
+  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
+  EE_LAUNCH("attention", s, launch_attention(d.dtype, big, cu, B, max_len, d.n_heads, d.head_dim, o, s));
+  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s));
+  EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
+  if (d.fuse_gelu) {
+    EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, ln, w.w_fc1, w.b_fc1, nullptr, T, F, H, EE_EPI_BIAS_GELU, d.gelu, big, s));
+  } else {
+    EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, ln, w.w_fc1, nullptr, nullptr, T, F, H, EE_EPI_NONE, d.gelu, big, s));
+    EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, d.gelu, big, s));
+  }
+  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s));
+  return EE_OK;
+}
+
+ee_status stack_impl(ee_layer* const* layers, int32_t n_layers, const void* x_padded, const int32_t* seq_lens,
+                     int32_t B, int32_t P, void* y_padded, void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || n_layers < 1) return fail(EE_ERR_INVALID_ARG, "need at least one layer");
+  for (int32_t i = 0; i < n_layers; ++i) {
+    if (!layers[i]) return fail(EE_ERR_INVALID_ARG, "layers[%d] is NULL", i);
+    if (!desc_equal(layers[i]->desc, layers[0]->desc))
+      return fail(EE_ERR_INVALID_ARG, "layers[%d] has a different descriptor from layers[0]", i);
+  }
+  const ee_layer_desc& d = layers[0]->desc;
+  int64_t T = 0;
+  int32_t max_len = 0;
+  EE_TRY(check_lengths(seq_lens, B, P, &T, &max_len));
+  EE_TRY(check_ptr(x_padded, "x_padded"));
+  EE_TRY(check_ptr(y_padded, "y_padded"));
+  EE_TRY(check_ptr(ws, "workspace"));
+  const Plan p = plan_layer(d, B, P, T);
+  if (ws_bytes < p.total)
+    return fail(EE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu for T=%lld", ws_bytes, p.total, (long long)T);
+  const size_t io = (size_t)B * P * d.hidden * dtype_size(d.dtype);
+  if (overlap(x_padded, io, y_padded, io)) return fail(EE_ERR_INVALID_ARG, "x_padded and y_padded overlap");
+  if (overlap(ws, p.total, x_padded, io) || overlap(ws, p.total, y_padded, io))
+    return fail(EE_ERR_INVALID_ARG, "workspace overlaps x_padded or y_padded");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* cu = reinterpret_cast<int32_t*>(at(ws, p.cu));
+  int32_t* tsrc = reinterpret_cast<int32_t*>(at(ws, p.token_src));
+  int32_t* p2p = reinterpret_cast<int32_t*>(at(ws, p.pad2pack));
+  const int64_t row_bytes = (int64_t)d.hidden * (int64_t)dtype_size(d.dtype);
+  EE_TRY(offsets_from_host(seq_lens, B, P, cu, tsrc, p2p, s));
+  if (T > 0) {
+    EE_LAUNCH("remove", s, launch_remove(x_padded, tsrc, T, row_bytes, at(ws, p.x), s));
+    for (int32_t i = 0; i < n_layers; ++i) EE_TRY(packed_layer(layers[i], ws, p, T, B, max_len, s));
+  }
+  EE_LAUNCH("rebuild", s, launch_rebuild(at(ws, p.x), p2p, (int64_t)B * P, row_bytes, y_padded, s));
+  return EE_OK;
+}
+
+}  // namespace
+
+// ======================================================================= ABI
+extern "C" {
+
+const char* ee_status_string(ee_status s) {
+  switch (s) {
+    case EE_OK: return "EE_OK";
+    case EE_ERR_INVALID_ARG: return "EE_ERR_INVALID_ARG";
+    case EE_ERR_UNSUPPORTED: return "EE_ERR_UNSUPPORTED";
+    case EE_ERR_WORKSPACE: return "EE_ERR_WORKSPACE";
+    case EE_ERR_OOM: return "EE_ERR_OOM";
+    case EE_ERR_HIP: return "EE_ERR_HIP";
+  }
+  return "EE_UNKNOWN_STATUS";
+}
+
+const char* ee_last_error(void) { return g_err.c_str(); }
+
+const char* ee_version(void) { return "ee 0.1 (gfx950)"; }
+
+ee_status ee_layer_create(const ee_layer_desc* desc, const ee_layer_weights* weights, ee_layer** out) {
+  if (!out) return fail(EE_ERR_INVALID_ARG, "out is NULL");
+  *out = nullptr;
+  EE_TRY(check_desc(desc));
+  if (!weights) return fail(EE_ERR_INVALID_ARG, "weights is NULL");
+  const void* const ptrs[] = {weights->ln1_g, weights->ln1_b, weights->w_qkv, weights->b_qkv,
+                              weights->w_out, weights->b_out, weights->ln2_g, weights->ln2_b,
+                              weights->w_fc1, weights->b_fc1, weights->w_fc2, weights->b_fc2};
+  static const char* const names[] = {"ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_out", "b_out",
+                                      "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2"};
+  for (int i = 0; i < 12; ++i) EE_TRY(check_ptr(ptrs[i], names[i]));
+  ee_layer* L = new (std::nothrow) ee_layer;
+  if (!L) return fail(EE_ERR_OOM, "host allocation of the layer handle failed");
+  L->desc = *desc;
+  L->w = *weights;
+  *out = L;
+  return EE_OK;
+}
+
+ee_status ee_layer_destroy(ee_layer* layer) {
+  delete layer;
+  return EE_OK;
+}
+
+ee_status ee_layer_workspace_size(const ee_layer* layer, int32_t batch, int32_t pad_len, int64_t max_tokens,
+                                  size_t* bytes) {
+  if (!layer || !bytes) return fail(EE_ERR_INVALID_ARG, "layer and bytes must be non-NULL");
+  if (batch < 1 || batch > EE_MAX_BATCH || pad_len < 1 || (int64_t)batch * pad_len > INT32_MAX)
+    return fail(EE_ERR_INVALID_ARG, "bad batch %d / pad_len %d", batch, pad_len);
+  const int64_t cap = (int64_t)batch * pad_len;
+  if (max_tokens < 0 || max_tokens > cap) max_tokens = cap;
+  *bytes = plan_layer(layer->desc, batch, pad_len, max_tokens).total;
+  return EE_OK;
+}
+
+ee_status ee_layer_forward(ee_layer* layer, const void* x_padded, const int32_t* seq_lens, int32_t batch,
+                           int32_t pad_len, void* y_padded, void* workspace, size_t ws_bytes, void* stream) {
+  if (!layer) return fail(EE_ERR_INVALID_ARG, "layer is NULL");
+  ee_layer* const one[1] = {layer};
+  return stack_impl(one, 1, x_padded, seq_lens, batch, pad_len, y_padded, workspace, ws_bytes, stream);
+}
+
+ee_status ee_stack_forward(ee_layer* const* layers, int32_t n_layers, const void* x_padded, const int32_t* seq_lens,
+                           int32_t batch, int32_t pad_len, void* y_padded, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  return stack_impl(layers, n_layers, x_padded, seq_lens, batch, pad_len, y_padded, workspace, ws_bytes, stream);
+}
+
+ee_status ee_compute_offsets(const int32_t* seq_lens, int32_t batch, int32_t pad_len, int32_t* d_cu,
+                             int32_t* d_token_src, int32_t* d_pad2pack, int32_t* total_tokens, void* stream) {
+  int64_t T = 0;
+  EE_TRY(check_lengths(seq_lens, batch, pad_len, &T, nullptr));
+  if (!d_cu || !d_token_src || !d_pad2pack || !total_tokens)
+    return fail(EE_ERR_INVALID_ARG, "output pointers must be non-NULL");
+  const size_t n = 4 * (size_t)batch * pad_len;
+  if (overlap(d_cu, 4 * (size_t)(batch + 1), d_token_src, n) || overlap(d_cu, 4 * (size_t)(batch + 1), d_pad2pack, n) ||
+      overlap(d_token_src, n, d_pad2pack, n))
+    return fail(EE_ERR_INVALID_ARG, "offset output arrays overlap");
+  *total_tokens = (int32_t)T;
+  return offsets_from_host(seq_lens, batch, pad_len, d_cu, d_token_src, d_pad2pack, static_cast<hipStream_t>(stream));
+}
+
+ee_status ee_compute_offsets_mask(const uint8_t* d_mask, int32_t batch, int32_t pad_len, int32_t* d_cu,
+                                  int32_t* d_token_src, int32_t* d_pad2pack, int32_t* d_total, void* stream) {
+  if (!d_mask || !d_cu || !d_token_src || !d_pad2pack || !d_total)
+    return fail(EE_ERR_INVALID_ARG, "pointers must be non-NULL");
+  if (batch < 1 || pad_len < 1 || (int64_t)batch * pad_len > INT32_MAX)
+    return fail(EE_ERR_INVALID_ARG, "bad batch %d / pad_len %d", batch, pad_len);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("offsets_mask", s, launch_offsets_mask(d_mask, batch, pad_len, d_cu, d_token_src, d_pad2pack, d_total, s));
+  return EE_OK;
+}
+
+ee_status ee_padding_workspace_size(int32_t batch, int32_t pad_len, size_t* bytes) {
+  if (!bytes) return fail(EE_ERR_INVALID_ARG, "bytes is NULL");
+  if (batch < 1 || batch > EE_MAX_BATCH || pad_len < 1 || (int64_t)batch * pad_len > INT32_MAX)
+    return fail(EE_ERR_INVALID_ARG, "bad batch %d / pad_len %d", batch, pad_len);
+  *bytes = plan_offsets_only(batch, pad_len).total;
+  return EE_OK;
+}
+
+static ee_status padding_common(const void* src, const int32_t* seq_lens, int32_t batch, int32_t pad_len,
+                                int32_t hidden, ee_dtype dtype, void* dst, void* ws, size_t ws_bytes, int64_t* T,
+                                Plan* p) {
+  EE_TRY(check_lengths(seq_lens, batch, pad_len, T, nullptr));
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (hidden < 1 || (size_t)hidden * dtype_size(dtype) % 16)
+    return fail(EE_ERR_UNSUPPORTED, "hidden*sizeof(dtype) must be a positive multiple of 16 bytes");
+  EE_TRY(check_ptr(src, "source"));
+  EE_TRY(check_ptr(dst, "destination"));
+  EE_TRY(check_ptr(ws, "workspace"));
+  *p = plan_offsets_only(batch, pad_len);
+  if (ws_bytes < p->total) return fail(EE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, p->total);
+  return EE_OK;
+}
+
+// The padded buffer spans batch*pad_len rows, the packed one T rows.
+static ee_status check_padding_overlaps(const void* padded, const void* packed, const void* ws, size_t ws_total,
+                                        int32_t batch, int32_t pad_len, int64_t T, int32_t hidden, ee_dtype dtype) {
+  const size_t row = (size_t)hidden * dtype_size(dtype);
+  const size_t np = (size_t)batch * pad_len * row, nk = (size_t)T * row;
+  if (overlap(padded, np, packed, nk)) return fail(EE_ERR_INVALID_ARG, "padded and packed buffers overlap");
+  if (overlap(ws, ws_total, padded, np) || overlap(ws, ws_total, packed, nk))
+    return fail(EE_ERR_INVALID_ARG, "workspace overlaps the padded or packed buffer");
+  return EE_OK;
+}
+
+ee_status ee_remove_padding(const void* d_padded, const int32_t* seq_lens, int32_t batch, int32_t pad_len,
+                            int32_t hidden, ee_dtype dtype, void* d_packed, void* workspace, size_t ws_bytes,
+                            void* stream) {
+  int64_t T = 0;
+  Plan p{};
+  EE_TRY(padding_common(d_padded, seq_lens, batch, pad_len, hidden, dtype, d_packed, workspace, ws_bytes, &T, &p));
+  EE_TRY(check_padding_overlaps(d_padded, d_packed, workspace, p.total, batch, pad_len, T, hidden, dtype));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* cu = reinterpret_cast<int32_t*>(at(workspace, p.cu));
+  int32_t* tsrc = reinterpret_cast<int32_t*>(at(workspace, p.token_src));
+  int32_t* p2p = reinterpret_cast<int32_t*>(at(workspace, p.pad2pack));
+  EE_TRY(offsets_from_host(seq_lens, batch, pad_len, cu, tsrc, p2p, s));
+  EE_LAUNCH("remove", s, launch_remove(d_padded, tsrc, T, (int64_t)hidden * dtype_size(dtype), d_packed, s));
+  return EE_OK;
+}
+
+ee_status ee_rebuild_padding(const void* d_packed, const int32_t* seq_lens, int32_t batch, int32_t pad_len,
+                             int32_t hidden, ee_dtype dtype, void* d_padded, void* workspace, size_t ws_bytes,
+                             void* stream) {
+  int64_t T = 0;
+  Plan p{};
+  EE_TRY(padding_common(d_packed, seq_lens, batch, pad_len, hidden, dtype, d_padded, workspace, ws_bytes, &T, &p));
+  EE_TRY(check_padding_overlaps(d_padded, d_packed, workspace, p.total, batch, pad_len, T, hidden, dtype));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* cu = reinterpret_cast<int32_t*>(at(workspace, p.cu));
+  int32_t* tsrc = reinterpret_cast<int32_t*>(at(workspace, p.token_src));
+  int32_t* p2p = reinterpret_cast<int32_t*>(at(workspace, p.pad2pack));
+  EE_TRY(offsets_from_host(seq_lens, batch, pad_len, cu, tsrc, p2p, s));
+  EE_LAUNCH("rebuild", s,
+            launch_rebuild(d_packed, p2p, (int64_t)batch * pad_len, (int64_t)hidden * dtype_size(dtype), d_padded, s));
+  return EE_OK;
+}
+
+ee_status ee_layernorm(const void* x, const void* gamma, const void* beta, int64_t rows, int32_t hidden, float eps,
+                       ee_dtype dtype, void* y, void* stream) {
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (rows < 0) return fail(EE_ERR_INVALID_ARG, "rows < 0");
+  if (hidden < 1 || (size_t)hidden * dtype_size(dtype) % 16)
+    return fail(EE_ERR_UNSUPPORTED, "hidden*sizeof(dtype) must be a positive multiple of 16 bytes");
+  if (hidden > layernorm_max_hidden(dtype)) return fail(EE_ERR_UNSUPPORTED, "hidden %d too large", hidden);
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(EE_ERR_INVALID_ARG, "eps must be finite and > 0");
+  EE_TRY(check_ptr(gamma, "gamma"));
+  EE_TRY(check_ptr(beta, "beta"));
+  if (rows == 0) return EE_OK;
+  EE_TRY(check_ptr(x, "x"));
+  EE_TRY(check_ptr(y, "y"));
+  const size_t n = (size_t)rows * hidden * dtype_size(dtype);
+  if (overlap(x, n, y, n)) return fail(EE_ERR_INVALID_ARG, "x and y overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("layernorm", s, launch_layernorm(dtype, x, gamma, beta, rows, hidden, eps, y, s));
+  return EE_OK;
+}
+
+ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual, int64_t M, int32_t N,
+                    int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, void* C, void* stream) {
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (epi < EE_EPI_NONE || epi > EE_EPI_BIAS_GELU) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi);
+  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+  if (M < 0 || N < 1 || K < 1) return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
+  if (M > 4000000) return fail(EE_ERR_UNSUPPORTED, "M = %lld above 4,000,000", (long long)M);
+  EE_TRY(check_ptr(W, "W"));
+  if (epi != EE_EPI_NONE) EE_TRY(check_ptr(bias, "bias"));
+  if (M == 0) return EE_OK;
+  EE_TRY(check_ptr(A, "A"));
+  EE_TRY(check_ptr(C, "C"));
+  if (epi == EE_EPI_BIAS_RESIDUAL) EE_TRY(check_ptr(residual, "residual"));
+  const size_t s = dtype_size(dtype);
+  const size_t nc = (size_t)M * N * s;
+  if (overlap(C, nc, A, (size_t)M * K * s) || overlap(C, nc, W, (size_t)N * K * s) ||
+      (epi != EE_EPI_NONE && overlap(C, nc, bias, (size_t)N * s)) ||
+      (epi == EE_EPI_BIAS_RESIDUAL && overlap(C, nc, residual, nc)))
+    return fail(EE_ERR_INVALID_ARG, "C overlaps an input");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("linear", st, gemm(dtype, A, W, bias, residual, M, N, K, epi, gelu, C, st));
+  return EE_OK;
+}
+
+ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t cols, ee_dtype dtype, ee_gelu gelu,
+                       void* g, void* stream) {
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+  if (rows < 0 || cols < 1) return fail(EE_ERR_INVALID_ARG, "need rows >= 0, cols >= 1");
+  if ((size_t)cols * dtype_size(dtype) % 16) return fail(EE_ERR_UNSUPPORTED, "cols*sizeof(dtype) % 16 != 0");
+  EE_TRY(check_ptr(bias, "bias"));
+  if (rows == 0) return EE_OK;
+  EE_TRY(check_ptr(u, "u"));
+  EE_TRY(check_ptr(g, "g"));
+  const size_t n = (size_t)rows * cols * dtype_size(dtype);
+  if (overlap(u, n, g, n)) return fail(EE_ERR_INVALID_ARG, "u and g overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("bias_gelu", s, launch_bias_gelu(dtype, u, bias, rows, cols, gelu, g, s));
+  return EE_OK;
+}
+
+ee_status ee_attention_varlen(const void* qkv, const int32_t* d_cu, int32_t batch, int32_t max_len, int32_t n_heads,
+                              int32_t head_dim, int64_t total_tokens, ee_dtype dtype, void* o, void* stream) {
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(EE_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", head_dim);
+  if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 65535 || max_len < 0 || total_tokens < 0)
+    return fail(EE_ERR_INVALID_ARG, "bad batch/n_heads/max_len/total_tokens");
+  if (!d_cu) return fail(EE_ERR_INVALID_ARG, "d_cu is NULL");
+  if (total_tokens == 0 || max_len == 0) return EE_OK;
+  EE_TRY(check_ptr(qkv, "qkv"));
+  EE_TRY(check_ptr(o, "o"));
+  const size_t s = dtype_size(dtype), Hp = (size_t)n_heads * head_dim;
+  if (overlap(qkv, (size_t)total_tokens * 3 * Hp * s, o, (size_t)total_tokens * Hp * s))
+    return fail(EE_ERR_INVALID_ARG, "qkv and o overlap");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("attention", st, launch_attention(dtype, qkv, d_cu, batch, max_len, n_heads, head_dim, o, st));
+  return EE_OK;
+}
+
+ee_status ee_profile_enable(int32_t on) {
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.on = on != 0;
+  return EE_OK;
+}
+
+ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* count) {
+  if (!count || (capacity > 0 && !out)) return fail(EE_ERR_INVALID_ARG, "out/count must be non-NULL");
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  std::vector<std::string> order;
+  std::map<std::string, std::pair<int64_t, double>> agg;
+  for (const auto& r : p.recs) {
+    const auto& ev = p.pool[r.second];
+    hipError_t e = hipEventSynchronize(ev.second);
+    float ms = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev.first, ev.second);
+    if (e != hipSuccess) {
+      p.recs.clear();
+      p.used = 0;
+      return hip_fail(e, "profile event");
+    }
+    if (!agg.count(r.first)) order.push_back(r.first);
+    auto& a = agg[r.first];
+    a.first += 1;
+    a.second += ms;
+  }
+  int32_t n = 0;
+  for (const auto& name : order) {
+    if (n < capacity) {
+      ee_kernel_stat& k = out[n];
+      std::memset(&k, 0, sizeof k);
+      std::strncpy(k.name, name.c_str(), sizeof k.name - 1);
+      k.launches = agg[name].first;
+      k.total_ms = agg[name].second;
+    }
+    ++n;
+  }
+  *count = std::min(n, capacity);
+  p.recs.clear();
+  p.used = 0;
+  return EE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Internal interface between the C-ABI layer (api.cpp) and the HIP kernels.
+// Not installed; every symbol lives in namespace ee and is hidden from the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ee.h"
+
+namespace ee {
+
+// Host lengths travel to the device as a by-value kernel argument: no
+// host-to-device copy, so the caller's array is free once the call returns.
+struct LensArg {
+  int32_t v[EE_MAX_BATCH];
+};
+
+// ---- offsets.hip ----
+hipError_t launch_offsets(const LensArg& lens, int B, int P, int32_t* cu, int32_t* token_src,
+                          int32_t* pad2pack, hipStream_t s);
+hipError_t launch_offsets_mask(const uint8_t* mask, int B, int P, int32_t* cu, int32_t* token_src,
+                               int32_t* pad2pack, int32_t* total, hipStream_t s);
+
+// ---- padding.hip ----  (row_bytes % 16 == 0, pointers 16-byte aligned)
+hipError_t launch_remove(const void* padded, const int32_t* token_src, int64_t T, int64_t row_bytes,
+                         void* packed, hipStream_t s);
+hipError_t launch_rebuild(const void* packed, const int32_t* pad2pack, int64_t rows, int64_t row_bytes,
+                          void* padded, hipStream_t s);
+
+// ---- layernorm.hip ----
+int layernorm_max_hidden(ee_dtype dt);
+hipError_t launch_layernorm(ee_dtype dt, const void* x, const void* g, const void* b, int64_t rows, int H,
+                            float eps, void* y, hipStream_t s);
+
+// ---- bias_gelu.hip ----
+hipError_t launch_bias_gelu(ee_dtype dt, const void* u, const void* bias, int64_t rows, int cols,
+                            ee_gelu form, void* g, hipStream_t s);
+
+// ---- gemm_f16.hip / gemm_f32.hip ----
+bool gemm_f16_mfma_ok(int64_t M, int N, int K);
+hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M,
+                                int N, int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s);
+hipError_t launch_gemm_valu(ee_dtype dt, const void* A, const void* W, const void* bias, const void* R,
+                            int64_t M, int N, int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s);
+
+// ---- attention.hip ----
+bool attention_mfma_ok(ee_dtype dt, int head_dim);
+hipError_t launch_attention(ee_dtype dt, const void* qkv, const int32_t* cu, int B, int max_len, int nh,
+                            int hd, void* o, hipStream_t s);
+
+}  // namespace ee

@@ -1,0 +1,135 @@
+// LayerNorm over packed rows: y = (x - mean) / sqrt(var + eps) * gamma + beta,
+// biased variance, fp32 statistics.  (LayerNorm is part of the add bias +
+// input + LayerNorm step in the announcement article's "Ease of use" listing;
+// the pre-LN placement inside the decoder block is this library's reading.)
+//
+// HBM-bound: one workgroup (4 waves) per row.  The row is read once into
+// registers with 16-byte loads, reduced twice (mean, then the centred sum of
+// squares, so no cancellation) through wave shuffles and a 4-entry LDS
+// exchange, and written once.  gamma/beta are re-read from L2 by every row.
+#include "device_common.h"
+#include "internal.h"
+
+namespace ee {
+namespace {
+
+constexpr int kLnThreads = 256;
+
+__device__ __forceinline__ float block_sum(float v, float* s_red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+  if (lane == 0) s_red[wave] = v;
+  __syncthreads();
+  float r = 0.f;
+#pragma unroll
+  for (int w = 0; w < kLnThreads / kWave; ++w) r += s_red[w];
+  __syncthreads();  // s_red is reused by the next reduction
+  return r;
+}
+
+template <typename T>
+struct Vec16;  // one 16-byte vector of T
+template <>
+struct Vec16<f16> {
+  typedef half8 type;
+  static constexpr int n = 8;
+};
+template <>
+struct Vec16<float> {
+  typedef floatx4 type;
+  static constexpr int n = 4;
+};
+
+// VPT: 16-byte vectors per thread (compile-time upper bound; nvec <= VPT*256).
+template <typename T, int VPT>
+__global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
+                                                               const T* __restrict__ beta, int64_t rows, int H,
+                                                               float eps, T* __restrict__ y) {
+  typedef typename Vec16<T>::type V;
+  constexpr int E = Vec16<T>::n;
+  __shared__ float s_red[kLnThreads / kWave];
+  const int nvec = H / E;
+  const float inv_h = 1.0f / (float)H;
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const V* xr = reinterpret_cast<const V*>(x + row * H);
+    float v[VPT][E];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * kLnThreads;
+      if (c < nvec) {
+        const V a = __builtin_nontemporal_load(xr + c);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          v[i][e] = to_f32(a[e]);
+          s += v[i][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[i][e] = 0.f;
+      }
+    }
+    const float mean = block_sum(s, s_red) * inv_h;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      if (threadIdx.x + i * kLnThreads < nvec) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = v[i][e] - mean;
+          q += d * d;
+        }
+      }
+    }
+    const float var = block_sum(q, s_red) * inv_h;
+    const float rstd = 1.0f / sqrtf(var + eps);
+    V* yr = reinterpret_cast<V*>(y + row * H);
+    const V* gv = reinterpret_cast<const V*>(gamma);
+    const V* bv = reinterpret_cast<const V*>(beta);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * kLnThreads;
+      if (c < nvec) {
+        const V g = gv[c], b = bv[c];
+        V o;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = from_f32<T>((v[i][e] - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
+        yr[c] = o;
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_ln_t(const void* x, const void* g, const void* b, int64_t rows, int H, float eps, void* y,
+                       hipStream_t s) {
+  const int nvec = H / Vec16<T>::n;
+  const unsigned grid = (unsigned)(rows > (1 << 20) ? (1 << 20) : rows);
+  const T* xp = static_cast<const T*>(x);
+  const T* gp = static_cast<const T*>(g);
+  const T* bp = static_cast<const T*>(b);
+  T* yp = static_cast<T*>(y);
+  if (nvec <= 256)
+    hipLaunchKernelGGL((layernorm_kernel<T, 1>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+  else if (nvec <= 512)
+    hipLaunchKernelGGL((layernorm_kernel<T, 2>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+  else if (nvec <= 1024)
+    hipLaunchKernelGGL((layernorm_kernel<T, 4>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+  else if (nvec <= 2048)
+    hipLaunchKernelGGL((layernorm_kernel<T, 8>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+  else
+    hipLaunchKernelGGL((layernorm_kernel<T, 16>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+int layernorm_max_hidden(ee_dtype dt) { return 16 * kLnThreads * (dt == EE_F16 ? 8 : 4); }
+
+hipError_t launch_layernorm(ee_dtype dt, const void* x, const void* g, const void* b, int64_t rows, int H, float eps,
+                            void* y, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return dt == EE_F16 ? launch_ln_t<f16>(x, g, b, rows, H, eps, y, s) : launch_ln_t<float>(x, g, b, rows, H, eps, y, s);
+}
+
+}  // namespace ee
