@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Throughput of the padding-removed GPT layer forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one pass of the whole hot path over one batch: offsets, remove,
+L packed layers (LayerNorm, QKV GEMM, varlen causal attention, out GEMM,
+LayerNorm, FC1 GEMM + GeLU, FC2 GEMM), rebuild -- one ee_stack_forward call.
+Inputs (lengths, padded activations, every layer's weights) are generated
+and resident in HBM before the timed region.  Prints one JSON line.
+
+Metric: valid tokens/s per layer = T * L / (seconds per step).
+roofline: the FC1 GEMM kernel (gelu epilogue, the largest single contraction;
+the GEMMs together take ~95% of a step), algorithmic flops 2*T*H*F per launch
+over its hipEvent-measured average duration on the launch stream.
+cpu_baseline: the CPU oracle's packed layer forward on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "valid tokens/s per GPT layer fwd (packed) + % HBM/MFMA roofline, 1 GPU"
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+ROOFLINE_KERNEL = "gemm_fc1"
+ROOFLINE_SYMBOL = "gemm_f16_mfma_kernel<256, 256, EE_EPI_BIAS_GELU>"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fc1_gpt3-12l_pmc.json")
+GEMM_SOURCE = os.path.join(ROOT, "variable_length_padding_amd", "csrc", "gemm_f16.hip")
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt3-12l")
+    ap.add_argument("--seed", type=int, default=1234)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-seqs", type=int, default=4)
+    ap.add_argument("--no-fuse-gelu", action="store_true", help="unfused bias+GeLU (ablation)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (scale reference for HBM byte counters)")
+    return ap.parse_args()
+
+
+def _log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _site_work(w, T, B, P, site):
+    """(algorithmic flops, algorithmic HBM bytes) of one launch at a site."""
+    s = w.elem_bytes
+    H, Hp, F = w.hidden, w.inner, w.ffn
+    gemm = {"gemm_qkv": (H, 3 * Hp), "gemm_out": (Hp, H), "gemm_fc1": (H, F), "gemm_fc2": (F, H)}
+    if site in gemm:
+        K, N = gemm[site]
+        res = T * N * s if site in ("gemm_out", "gemm_fc2") else 0
+        return 2.0 * T * K * N, float((T * K + N * K + T * N) * s + res)
+    if site in ("ln1", "ln2"):
+        return 0.0, 2.0 * T * H * s
+    if site == "remove":
+        return 0.0, 2.0 * T * H * s
+    if site == "rebuild":
+        return 0.0, float((T + B * P) * H * s)
+    if site == "attention":
+        return 0.0, 4.0 * T * Hp * s
+    if site == "bias_gelu":
+        return 0.0, 2.0 * T * F * s
+    return 0.0, 0.0
+
+
+def _attention_flops(w, lens):
+    # QK^T and PV over the causal triangle: 2 * 2 * hd * nh * len(len+1)/2 per sequence
+    return sum(2.0 * w.inner * n * (n + 1) for n in lens)
+
+
+def _traffic():
+    """HBM bytes per FC1 launch from the committed counter summary, if it was
+    taken on the current GEMM source."""
+    try:
+        with open(PMC_SUMMARY) as f:
+            s = json.load(f)
+        with open(GEMM_SOURCE, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+        if s.get("gemm_source_sha256") != h:
+            return None
+        return s["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def _cpu_baseline(w, lens, x_host, params_dev, nseq):
+    """Times the oracle (numpy float64, as it stands) on `nseq` sequences of the
+    batch through layer 0."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    params64 = oracle.to_f64_params(params_dev)          # input preparation, untimed
+    pick = list(range(min(nseq, len(lens))))
+    rows = [x_host[b, :lens[b]].double().numpy() for b in pick]
+    xs = np.concatenate(rows, axis=0)
+    cu = np.concatenate([[0], np.cumsum([lens[b] for b in pick])])
+    t0 = time.perf_counter()
+    oracle.layer_forward_packed(xs, cu, params64, w.n_heads, w.head_dim)
+    dt = time.perf_counter() - t0
+    ntok = int(cu[-1])
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": ntok / dt, "unit": "valid tokens/s per layer", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pick)} sequences ({ntok} valid tokens) of the {w.name} batch through layer 0, "
+                      f"float64 numpy oracle, {dt:.1f} s"}
+
+
+def _copy_calibration():
+    import torch
+    n = 1 << 30
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    y = torch.empty_like(x)
+    x.fill_(1)
+    for _ in range(5):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}), flush=True)
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.copy_calibration:
+        _copy_calibration()
+        return
+
+    import torch
+
+    import variable_length_padding_amd as ee
+    import workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload)
+    if w.requests:
+        raise SystemExit("the request-stream workload is not a bench line")
+    lens = workloads.lengths(w, args.seed)
+    B, P, L = w.batch, w.pad_len, w.layers
+    T = sum(lens)
+    _log(f"workload {w.name}: B={B} P={P} T={T} H={w.hidden} nh={w.n_heads} hd={w.head_dim} F={w.ffn} L={L}")
+
+    x = workloads.activations(w, args.seed, B, P, lens, device=dev)
+    params = [workloads.layer_params(w, args.seed, l, device=dev) for l in range(L)]
+    torch.cuda.synchronize()
+    dt = ee.F16 if w.dtype == "f16" else ee.F32
+    layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=dt, fuse_gelu=not args.no_fuse_gelu)
+              for p in params]
+    ws = torch.empty(layers[0].workspace_size(B, P, T), dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    _log(f"weights {sum(t.numel() * t.element_size() for p in params for t in p.values()) / 1e9:.1f} GB resident; "
+         f"workspace {ws.numel() / 1e6:.0f} MB")
+
+    for _ in range(args.warmup):
+        ee.ee_stack_forward(layers, x, lens, y, ws, stream)
+    torch.cuda.synchronize()
+    _log(f"warmup done ({args.warmup} steps)")
+
+    ee.ee_profile_enable(True)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        ee.ee_stack_forward(layers, x, lens, y, ws, stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ee.ee_profile_enable(False)
+    stats = ee.ee_profile_collect()
+    ms_step = e0.elapsed_time(e1) / args.steps
+    _log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host clock {1e3 * t_host / args.steps:.3f})")
+
+    value = T * L / (ms_step / 1e3)
+    kernels = {}
+    for site, st in stats.items():
+        n = st["launches"]
+        avg_ms = st["total_ms"] / n
+        fl, by = _site_work(w, T, B, P, site)
+        if site == "attention":
+            fl = _attention_flops(w, lens)
+        k = {"launches_per_step": n / args.steps, "avg_ms": round(avg_ms, 5),
+             "share": round(st["total_ms"] / (ms_step * args.steps), 4)}
+        if fl:
+            k["tflops"] = round(fl / (avg_ms * 1e-3) / 1e12, 1)
+            k["mfma_frac"] = round(k["tflops"] / PEAK_F16_TFLOPS, 4)
+        if by:
+            k["gbs"] = round(by / (avg_ms * 1e-3) / 1e9, 1)
+            k["hbm_frac"] = round(k["gbs"] / PEAK_HBM_GBS, 4)
+        kernels[site] = k
+
+    fc1 = stats[ROOFLINE_KERNEL]
+    fc1_ms = fc1["total_ms"] / fc1["launches"]
+    fc1_flops = _site_work(w, T, B, P, ROOFLINE_KERNEL)[0]
+    achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": ROOFLINE_SYMBOL, "achieved": round(achieved, 1),
+                "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                "traffic": _traffic(), "avg_launch_ms": round(fc1_ms, 4),
+                "flops_per_launch": fc1_flops}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        _log("timing the CPU oracle on a bounded sample")
+        cpu = _cpu_baseline(w, lens, x.cpu(), params[0], args.cpu_sample_seqs)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "valid tokens/s per layer", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16" if w.dtype == "f16" else "f32",
+        "data": "synthetic (seeded lengths, N(0,1) activations, N(0,0.02) random-init weights)",
+        "config": {"workload": w.name, "batch": B, "pad_len": P, "valid_tokens": T, "layers": L,
+                   "hidden": w.hidden, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": w.ffn,
+                   "fuse_gelu": not args.no_fuse_gelu},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

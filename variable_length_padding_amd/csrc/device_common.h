@@ -17,15 +17,33 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 
-// GeLU of the add-bias + activation step.  tanh form:
-// 0.5 u (1 + tanh(sqrt(2/pi) (u + 0.044715 u^3))); erf form: 0.5 u (1 + erf(u / sqrt 2)).
-// tanhf / erff are the ROCm device library's.
+constexpr float kLog2e = 1.4426950408889634f;
+
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, 7.1.26:
+// erf(x) = 1 - (a1 t + ... + a5 t^5) exp(-x^2), t = 1 / (1 + p x), x >= 0,
+// absolute error <= 1.5e-7; odd extension for x < 0.  Straight-line code on the
+// hardware exp2 / reciprocal, so it inlines into GEMM epilogues without calls.
+__device__ __forceinline__ float erf_as(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(1.0f + 0.3275911f * ax);
+  const float poly =
+      t * (0.254829592f + t * (-0.284496736f + t * (1.421413741f + t * (-1.453152027f + t * 1.061405429f))));
+  const float y = 1.0f - poly * __builtin_amdgcn_exp2f(-ax * ax * kLog2e);
+  return copysignf(y, x);
+}
+
+// GeLU of the add-bias + activation step.
+//   tanh form: 0.5 u (1 + tanh(z)), z = sqrt(2/pi) (u + 0.044715 u^3), evaluated
+//              as u / (1 + exp(-2 z)) since 0.5 (1 + tanh z) = 1 / (1 + e^{-2z});
+//              exp(-2z) -> +inf gives u * 0 = 0 and exp -> 0 gives u (the limits);
+//   erf form:  0.5 u (1 + erf(u / sqrt 2)).
 __device__ __forceinline__ float gelu_f(float u, int form) {
   if (form == EE_GELU_TANH) {
-    const float k = 0.7978845608028654f;  // sqrt(2/pi)
-    return 0.5f * u * (1.0f + tanhf(k * (u + 0.044715f * u * u * u)));
+    const float z = 0.7978845608028654f * (u + 0.044715f * u * u * u);  // sqrt(2/pi)
+    const float e = __builtin_amdgcn_exp2f(-2.0f * kLog2e * z);
+    return u * __builtin_amdgcn_rcpf(1.0f + e);
   }
-  return 0.5f * u * (1.0f + erff(u * 0.7071067811865476f));  // 1/sqrt(2)
+  return 0.5f * u * (1.0f + erf_as(u * 0.7071067811865476f));  // 1/sqrt(2)
 }
 
 // Storage <-> fp32.  fp32 -> fp16 conversion rounds to nearest even.

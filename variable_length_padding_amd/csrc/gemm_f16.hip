@@ -10,9 +10,13 @@
 //     registers want: every lane reads 8 consecutive K values (16 bytes).
 //   * Workgroup tile BM x BN x 64 with 4 waves in a 2 x 2 grid; a wave owns a
 //     (BM/2) x (BN/2) block of 32 x 32 v_mfma_f32_32x32x16_f16 fragments.
-//   * Two LDS stages (BM=BN=256: 2 x 64 KiB of the 160 KiB per CU); the next
-//     K tile is fetched into registers while the current one feeds the MFMAs,
-//     then stored to the other stage: one barrier per K tile.
+//   * Two LDS stages (BM=BN=256: 2 x 64 KiB of the 160 KiB per CU) filled by
+//     gfx950's 16-byte direct-to-LDS loads (global_load_lds_dwordx4): no
+//     register staging and no LDS store instructions.  Tile kt+2 is requested
+//     right after the barrier that retires tile kt's stage, so a load has a
+//     whole K tile of MFMA work to land; one barrier per K tile.
+//   * MFMA fragments are double-buffered in registers: the LDS reads of K step
+//     kk+1 are in flight while the 16 MFMAs of step kk issue.
 //   * LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row r is stored at
 //     chunk c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), so the 16 rows
 //     read by a quarter-wave land on distinct banks whether the LDS serves
@@ -34,6 +38,15 @@ constexpr int kBK = 64;
 
 __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
+#define EE_GLOBAL(p) ((__attribute__((address_space(1))) void*)(p))
+#define EE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
+
+// Waits until this wave's direct-to-LDS loads have written LDS.  Needed before
+// the barrier that publishes them: the workgroup-scope fence of __syncthreads
+// only waits for LDS instructions (lgkmcnt), and the compiler does not count
+// global_load_lds as an LDS write.  The memory clobber keeps LDS reads below it.
+__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __restrict__ A, const f16* __restrict__ W,
                                                                  const f16* __restrict__ bias,
@@ -42,7 +55,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
                                                                  int tiles_n) {
   constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int AL = BM / 32, BL = BN / 32;  // 16-byte loads per thread per K tile
+  constexpr int AJ = BM / 32, BJ = BN / 32;  // direct-to-LDS loads per wave per K tile (8 rows each)
   constexpr int STAGE = (BM + BN) * kBK;     // halves per LDS stage
   __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
 
@@ -59,25 +72,63 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
   const int m0 = (first_m + ig % gm) * BM;
   const int n0 = (ig / gm) * BN;
 
-  // ---- global -> register -> LDS mapping: 32 rows x 8 chunks per pass
   const int t = threadIdx.x;
-  const int lrow = t >> 3, lch = t & 7;
-  const f16* ag[AL];
-  const f16* bg[BL];
+  const int lane = t & 63, wave = t >> 6;
+
+  // ---- global -> LDS: each wave fills rows [wave*BM/4, (wave+1)*BM/4) of the A
+  // tile (and likewise of W) with 16-byte direct-to-LDS loads.  One load of a
+  // wave writes 1 KiB of LDS = 8 rows; lane l lands in row l/8, physical chunk
+  // l%8, so it fetches the logical chunk (l%8) ^ f(row) from global memory.
+  const int lr = lane >> 3, lp = lane & 7;
+  const f16* asrc[AJ];
+  const f16* bsrc[BJ];
 #pragma unroll
-  for (int i = 0; i < AL; ++i) ag[i] = A + (int64_t)min(m0 + lrow + 32 * i, M - 1) * K + lch * 8;
+  for (int j = 0; j < AJ; ++j) {
+    const int r = wave * (BM / 4) + 8 * j + lr;
+    asrc[j] = A + (int64_t)min(m0 + r, M - 1) * K + ((lp ^ lds_swizzle(r)) * 8);
+  }
 #pragma unroll
-  for (int j = 0; j < BL; ++j) bg[j] = W + (int64_t)min(n0 + lrow + 32 * j, N - 1) * K + lch * 8;
-  const int soff = lrow * kBK + ((lch ^ lds_swizzle(lrow)) * 8);
-  half8 ra[AL], rb[BL];
+  for (int j = 0; j < BJ; ++j) {
+    const int r = wave * (BN / 4) + 8 * j + lr;
+    bsrc[j] = W + (int64_t)min(n0 + r, N - 1) * K + ((lp ^ lds_swizzle(r)) * 8);
+  }
+  // load q of a K tile: q < AJ -> rows of A, else rows of W
+  auto dma_one = [&](int stage, int k0, int q) {
+    if (q < AJ) {
+      f16* sa = smem + stage * STAGE + (wave * (BM / 4) + 8 * q) * kBK;
+      __builtin_amdgcn_global_load_lds(EE_GLOBAL(asrc[q] + k0), EE_LOCAL(sa), 16, 0, 0);
+    } else {
+      f16* sb = smem + stage * STAGE + BM * kBK + (wave * (BN / 4) + 8 * (q - AJ)) * kBK;
+      __builtin_amdgcn_global_load_lds(EE_GLOBAL(bsrc[q - AJ] + k0), EE_LOCAL(sb), 16, 0, 0);
+    }
+  };
+  auto dma = [&](int stage, int k0) {
+#pragma unroll
+    for (int q = 0; q < AJ + BJ; ++q) dma_one(stage, k0, q);
+  };
 
   // ---- wave / lane roles for the MFMA fragments
-  const int lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int hk = lane >> 5;  // which 8-wide K half of a 16-wide MFMA step this lane feeds
   const int rsw = lds_swizzle(lane & 15);
   const int abase = (wm * WTM + (lane & 31)) * kBK;
-  const int bbase = (wn * WTN + (lane & 31)) * kBK;
+  const int bbase = BM * kBK + (wn * WTN + (lane & 31)) * kBK;
+  // Reads are issued in the order the MFMAs below consume them (a0, b0..bN, a1..aM),
+  // so each MFMA waits only for its own operands.
+  auto frag_one = [&](int stage, int kk, int r, half8 (&af)[FM], half8 (&bf)[FN]) {
+    const f16* s = smem + stage * STAGE;
+    const int ch = ((kk * 2 + hk) ^ rsw) * 8;
+    if (r == 0)
+      af[0] = *reinterpret_cast<const half8*>(s + abase + ch);
+    else if (r <= FN)
+      bf[r - 1] = *reinterpret_cast<const half8*>(s + bbase + (r - 1) * 32 * kBK + ch);
+    else
+      af[r - FN] = *reinterpret_cast<const half8*>(s + abase + (r - FN) * 32 * kBK + ch);
+  };
+  auto frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
+#pragma unroll
+    for (int r = 0; r < FM + FN; ++r) frag_one(stage, kk, r, af, bf);
+  };
 
   floatx16 acc[FM][FN];
 #pragma unroll
@@ -86,58 +137,67 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+  auto mfmas = [&](const half8 (&af)[FM], const half8 (&bf)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+  };
 
+  // ---- main loop.  Stage kt&1 holds K tile kt.  The barrier at the end of
+  // tile kt both publishes tile kt+1 (each wave waited for its own loads) and
+  // retires every read of stage kt&1, which then receives tile kt+2 (clamped
+  // to the last tile: a redundant load into a stage nobody reads again keeps
+  // the loop body free of branches).  The 16 MFMAs of the tile's last K step
+  // issue after the barrier, from fragments already in registers, while the
+  // next tile's first fragments and the new loads are in flight.
+  //
+  // Within a K step the order is written out and fenced with sched_barrier:
+  // MFMA m is preceded by LDS read m of the next step (reads in consumption
+  // order: a0, b0..b3, a1..a3) and, after the barrier, by its share of the
+  // tile's direct-to-LDS loads.  The next step's operands are then requested
+  // 8+ MFMAs (256+ cycles) before their first use, and no wait bunches up.
+  constexpr int NF = FM + FN;  // LDS reads per K step
+  constexpr int NM = FM * FN;  // MFMAs per K step
+  constexpr int NL = AJ + BJ;  // direct-to-LDS loads per K tile
+  // MFMAs of step X interleaved with the reads of step (rstage, rkk) into Y,
+  // and with loads of K offset dk into stage dstage when dk >= 0.
+  auto step = [&](const half8 (&xa)[FM], const half8 (&xb)[FN], int rstage, int rkk, half8 (&ya)[FM],
+                  half8 (&yb)[FN], int dstage, int dk) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      if (dk >= 0) {
+#pragma unroll
+        for (int q = m * NL / NM; q < (m + 1) * NL / NM; ++q) dma_one(dstage, dk, q);
+      }
+      if (m < NF) frag_one(rstage, rkk, m, ya, yb);
+      const int i = m / FN, j = m % FN;
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   const int nk = K / kBK;
-#pragma unroll
-  for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const half8*>(ag[i]);
-#pragma unroll
-  for (int j = 0; j < BL; ++j) rb[j] = *reinterpret_cast<const half8*>(bg[j]);
-  {
-    f16* sa = smem;
-    f16* sb = smem + BM * kBK;
-#pragma unroll
-    for (int i = 0; i < AL; ++i) *reinterpret_cast<half8*>(sa + soff + i * 32 * kBK) = ra[i];
-#pragma unroll
-    for (int j = 0; j < BL; ++j) *reinterpret_cast<half8*>(sb + soff + j * 32 * kBK) = rb[j];
-  }
+  half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
+  dma(0, 0);
+  if (nk > 1) dma(1, kBK);
+  wait_dma();
   __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      const int k0 = (kt + 1) * kBK;
-#pragma unroll
-      for (int i = 0; i < AL; ++i) ra[i] = *reinterpret_cast<const half8*>(ag[i] + k0);
-#pragma unroll
-      for (int j = 0; j < BL; ++j) rb[j] = *reinterpret_cast<const half8*>(bg[j] + k0);
-    }
-    const f16* sa = smem + cur * STAGE;
-    const f16* sb = sa + BM * kBK;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      const int ch = ((kk * 2 + hk) ^ rsw) * 8;
-      half8 af[FM], bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const half8*>(sa + abase + i * 32 * kBK + ch);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bf[j] = *reinterpret_cast<const half8*>(sb + bbase + j * 32 * kBK + ch);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      f16* da = smem + (cur ^ 1) * STAGE;
-      f16* db = da + BM * kBK;
-#pragma unroll
-      for (int i = 0; i < AL; ++i) *reinterpret_cast<half8*>(da + soff + i * 32 * kBK) = ra[i];
-#pragma unroll
-      for (int j = 0; j < BL; ++j) *reinterpret_cast<half8*>(db + soff + j * 32 * kBK) = rb[j];
-    }
+  frags(0, 0, fa0, fb0);
+  int cur = 0;
+  for (int kt = 0; kt + 1 < nk; ++kt) {
+    step(fa0, fb0, cur, 1, fa1, fb1, 0, -1);
+    step(fa1, fb1, cur, 2, fa0, fb0, 0, -1);
+    step(fa0, fb0, cur, 3, fa1, fb1, 0, -1);
+    wait_dma();
     __syncthreads();
+    step(fa1, fb1, cur ^ 1, 0, fa0, fb0, cur, min(kt + 2, nk - 1) * kBK);
+    cur ^= 1;
   }
+  step(fa0, fb0, cur, 1, fa1, fb1, 0, -1);
+  step(fa1, fb1, cur, 2, fa0, fb0, 0, -1);
+  step(fa0, fb0, cur, 3, fa1, fb1, 0, -1);
+  mfmas(fa1, fb1);
+  wait_dma();  // no load may still be writing LDS when the workgroup retires
 
   // ---- epilogue.  Fragment element e of lane l is row (e/4)*8 + (l/32)*4 + e%4,
   // column l%32 of its 32 x 32 block.
