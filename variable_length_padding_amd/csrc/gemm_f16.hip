@@ -8,8 +8,9 @@
 // Design (gfx950, wave64):
 //   * Both operands are K-contiguous, which is the layout the MFMA operand
 //     registers want: every lane reads 8 consecutive K values (16 bytes).
-//   * Workgroup tile BM x BN x 64 with 4 waves in a 2 x 2 grid; a wave owns a
-//     (BM/2) x (BN/2) block of 32 x 32 v_mfma_f32_32x32x16_f16 fragments.
+//   * Workgroup tile BM x BN x 64 with a grid of waves (256 x 256: 2 x 4 waves,
+//     two per SIMD; 128 x 128: 2 x 2); a wave owns a block of 32 x 32
+//     v_mfma_f32_32x32x16_f16 fragments with fp32 accumulators in registers.
 //   * Two LDS stages (BM=BN=256: 2 x 64 KiB of the 160 KiB per CU) filled by
 //     gfx950's 16-byte direct-to-LDS loads (global_load_lds_dwordx4): no
 //     register staging and no LDS store instructions.  Tile kt+2 is requested
@@ -27,13 +28,20 @@
 //     share an XCD's L2 share A and W panels.
 //   * Ragged M (and N): out-of-range rows load a clamped in-range row, and
 //     their results are never stored.  K must be a multiple of 64.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
 namespace ee {
 namespace {
 
-constexpr int kThreads = 256;
+// Wave grid of the 256 x 256 tile: 2 x 4 waves of 128 x 64 (two waves per SIMD,
+// which measured faster than 2 x 2 waves of 128 x 128 at one wave per SIMD).
+#ifndef EE_GEMM_WGM
+#define EE_GEMM_WGM 2
+#define EE_GEMM_WGN 4
+#endif
 constexpr int kBK = 64;
 
 __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
@@ -47,15 +55,16 @@ __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r 
 // global_load_lds as an LDS write.  The memory clobber keeps LDS reads below it.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int BM, int BN, int EPI>
-__global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __restrict__ A, const f16* __restrict__ W,
+template <int BM, int BN, int WGM, int WGN, int EPI>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16* __restrict__ A, const f16* __restrict__ W,
                                                                  const f16* __restrict__ bias,
                                                                  const f16* __restrict__ R, f16* __restrict__ C,
                                                                  int M, int N, int K, int gelu_form, int tiles_m,
                                                                  int tiles_n) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;  // wave tile
+  constexpr int NW = WGM * WGN;                // waves: WGM x WGN grid over the tile
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
   constexpr int FM = WTM / 32, FN = WTN / 32;
-  constexpr int AJ = BM / 32, BJ = BN / 32;  // direct-to-LDS loads per wave per K tile (8 rows each)
+  constexpr int AJ = BM / (8 * NW), BJ = BN / (8 * NW);  // direct-to-LDS loads per wave per K tile (8 rows each)
   constexpr int STAGE = (BM + BN) * kBK;     // halves per LDS stage
   __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
 
@@ -73,9 +82,10 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
   const int n0 = (ig / gm) * BN;
 
   const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: keeps LDS bases scalar
 
-  // ---- global -> LDS: each wave fills rows [wave*BM/4, (wave+1)*BM/4) of the A
+  // ---- global -> LDS: each wave fills rows [wave*BM/NW, (wave+1)*BM/NW) of the A
   // tile (and likewise of W) with 16-byte direct-to-LDS loads.  One load of a
   // wave writes 1 KiB of LDS = 8 rows; lane l lands in row l/8, physical chunk
   // l%8, so it fetches the logical chunk (l%8) ^ f(row) from global memory.
@@ -84,21 +94,21 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
   const f16* bsrc[BJ];
 #pragma unroll
   for (int j = 0; j < AJ; ++j) {
-    const int r = wave * (BM / 4) + 8 * j + lr;
+    const int r = wave * (BM / NW) + 8 * j + lr;
     asrc[j] = A + (int64_t)min(m0 + r, M - 1) * K + ((lp ^ lds_swizzle(r)) * 8);
   }
 #pragma unroll
   for (int j = 0; j < BJ; ++j) {
-    const int r = wave * (BN / 4) + 8 * j + lr;
+    const int r = wave * (BN / NW) + 8 * j + lr;
     bsrc[j] = W + (int64_t)min(n0 + r, N - 1) * K + ((lp ^ lds_swizzle(r)) * 8);
   }
   // load q of a K tile: q < AJ -> rows of A, else rows of W
   auto dma_one = [&](int stage, int k0, int q) {
     if (q < AJ) {
-      f16* sa = smem + stage * STAGE + (wave * (BM / 4) + 8 * q) * kBK;
+      f16* sa = smem + stage * STAGE + (wave * (BM / NW) + 8 * q) * kBK;
       __builtin_amdgcn_global_load_lds(EE_GLOBAL(asrc[q] + k0), EE_LOCAL(sa), 16, 0, 0);
     } else {
-      f16* sb = smem + stage * STAGE + BM * kBK + (wave * (BN / 4) + 8 * (q - AJ)) * kBK;
+      f16* sb = smem + stage * STAGE + BM * kBK + (wave * (BN / NW) + 8 * (q - AJ)) * kBK;
       __builtin_amdgcn_global_load_lds(EE_GLOBAL(bsrc[q - AJ] + k0), EE_LOCAL(sb), 16, 0, 0);
     }
   };
@@ -108,7 +118,7 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
   };
 
   // ---- wave / lane roles for the MFMA fragments
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int hk = lane >> 5;  // which 8-wide K half of a 16-wide MFMA step this lane feeds
   const int rsw = lds_swizzle(lane & 15);
   const int abase = (wm * WTM + (lane & 31)) * kBK;
@@ -153,24 +163,27 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
   // next tile's first fragments and the new loads are in flight.
   //
   // Within a K step the order is written out and fenced with sched_barrier:
-  // MFMA m is preceded by LDS read m of the next step (reads in consumption
-  // order: a0, b0..b3, a1..a3) and, after the barrier, by its share of the
-  // tile's direct-to-LDS loads.  The next step's operands are then requested
-  // 8+ MFMAs (256+ cycles) before their first use, and no wait bunches up.
+  // every other MFMA is preceded by one LDS read of the next step (reads in
+  // consumption order: a0, b0..b3, a1..a3) and, after the barrier, every MFMA
+  // by its share of the tile's direct-to-LDS loads.  LDS demand stays even
+  // (no bursts) and each operand is requested 10+ MFMAs (320+ cycles) before
+  // its first use.
   constexpr int NF = FM + FN;  // LDS reads per K step
   constexpr int NM = FM * FN;  // MFMAs per K step
   constexpr int NL = AJ + BJ;  // direct-to-LDS loads per K tile
   // MFMAs of step X interleaved with the reads of step (rstage, rkk) into Y,
   // and with loads of K offset dk into stage dstage when dk >= 0.
-  auto step = [&](const half8 (&xa)[FM], const half8 (&xb)[FN], int rstage, int rkk, half8 (&ya)[FM],
-                  half8 (&yb)[FN], int dstage, int dk) {
+  // (with_dma is a compile-time flag so the step stays one basic block)
+  auto step = [&](auto with_dma, const half8 (&xa)[FM], const half8 (&xb)[FN], int rstage, int rkk,
+                  half8 (&ya)[FM], half8 (&yb)[FN], int dstage, int dk) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
-      if (dk >= 0) {
+      if constexpr (decltype(with_dma)::value) {
 #pragma unroll
         for (int q = m * NL / NM; q < (m + 1) * NL / NM; ++q) dma_one(dstage, dk, q);
       }
-      if (m < NF) frag_one(rstage, rkk, m, ya, yb);
+#pragma unroll
+      for (int r = m * NF / NM; r < (m + 1) * NF / NM; ++r) frag_one(rstage, rkk, r, ya, yb);
       const int i = m / FN, j = m % FN;
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[i], xb[j], acc[i][j], 0, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
@@ -183,19 +196,21 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
   wait_dma();
   __syncthreads();
   frags(0, 0, fa0, fb0);
+  const std::integral_constant<bool, false> no_dma;
+  const std::integral_constant<bool, true> with_dma;
   int cur = 0;
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    step(fa0, fb0, cur, 1, fa1, fb1, 0, -1);
-    step(fa1, fb1, cur, 2, fa0, fb0, 0, -1);
-    step(fa0, fb0, cur, 3, fa1, fb1, 0, -1);
+    step(no_dma, fa0, fb0, cur, 1, fa1, fb1, 0, 0);
+    step(no_dma, fa1, fb1, cur, 2, fa0, fb0, 0, 0);
+    step(no_dma, fa0, fb0, cur, 3, fa1, fb1, 0, 0);
     wait_dma();
     __syncthreads();
-    step(fa1, fb1, cur ^ 1, 0, fa0, fb0, cur, min(kt + 2, nk - 1) * kBK);
+    step(with_dma, fa1, fb1, cur ^ 1, 0, fa0, fb0, cur, min(kt + 2, nk - 1) * kBK);
     cur ^= 1;
   }
-  step(fa0, fb0, cur, 1, fa1, fb1, 0, -1);
-  step(fa1, fb1, cur, 2, fa0, fb0, 0, -1);
-  step(fa0, fb0, cur, 3, fa1, fb1, 0, -1);
+  step(no_dma, fa0, fb0, cur, 1, fa1, fb1, 0, 0);
+  step(no_dma, fa1, fb1, cur, 2, fa0, fb0, 0, 0);
+  step(no_dma, fa0, fb0, cur, 3, fa1, fb1, 0, 0);
   mfmas(fa1, fb1);
   wait_dma();  // no load may still be writing LDS when the workgroup retires
 
@@ -223,11 +238,11 @@ __global__ __launch_bounds__(kThreads) void gemm_f16_mfma_kernel(const f16* __re
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int WGM, int WGN>
 hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K,
                       ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  const dim3 grid((unsigned)(tm * tn)), block(kThreads);
+  const dim3 grid((unsigned)(tm * tn)), block(64 * WGM * WGN);
   const f16* a = static_cast<const f16*>(A);
   const f16* w = static_cast<const f16*>(W);
   const f16* b = static_cast<const f16*>(bias);
@@ -235,19 +250,19 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
   f16* c = static_cast<f16*>(C);
   switch (epi) {
     case EE_EPI_NONE:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, EE_EPI_NONE>), grid, block, 0, s, a, w, b, r, c, M, N, K,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_NONE>), grid, block, 0, s, a, w, b, r, c, M, N, K,
                          (int)form, tm, tn);
       break;
     case EE_EPI_BIAS:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, EE_EPI_BIAS>), grid, block, 0, s, a, w, b, r, c, M, N, K,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_BIAS>), grid, block, 0, s, a, w, b, r, c, M, N, K,
                          (int)form, tm, tn);
       break;
     case EE_EPI_BIAS_RESIDUAL:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, EE_EPI_BIAS_RESIDUAL>), grid, block, 0, s, a, w, b, r, c, M,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_BIAS_RESIDUAL>), grid, block, 0, s, a, w, b, r, c, M,
                          N, K, (int)form, tm, tn);
       break;
     case EE_EPI_BIAS_GELU:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, EE_EPI_BIAS_GELU>), grid, block, 0, s, a, w, b, r, c, M, N,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_BIAS_GELU>), grid, block, 0, s, a, w, b, r, c, M, N,
                          K, (int)form, tm, tn);
       break;
   }
@@ -264,8 +279,8 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
                                 int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles_big >= 256) return launch_cfg<256, 256>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
-  return launch_cfg<128, 128>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
+  if (tiles_big >= 256) return launch_cfg<256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
+  return launch_cfg<128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
 }
 
 }  // namespace ee
