@@ -1,0 +1,113 @@
+"""Parity at the full GPT-3-width sizes, in the launch configuration the bench
+times (ee_stack_forward over the whole batch), on sampled outputs the CPU
+oracle computes one sequence at a time (sequences are independent, so a
+sampled sequence's rows are exact rows of the batch), plus properties that
+hold at any size.  These tests hold tens to ~180 GB of weights in HBM."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import variable_length_padding_amd as ee
+import workloads
+from gpu_helpers import DEV, normwise_rel, say, to_host64
+
+pytestmark = [pytest.mark.gpu, pytest.mark.slow]
+
+SEED = 1234  # the bench's default seed
+
+
+def _setup(w, seed, lens, layers, device_batch=None):
+    B = len(lens)
+    P = w.pad_len if device_batch is None else device_batch
+    x = workloads.activations(w, seed, B, P, lens, device=DEV)
+    params = [workloads.layer_params(w, seed, l, device=DEV) for l in range(layers)]
+    hs = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=ee.F16) for p in params]
+    return x, params, hs
+
+
+def _stack(hs, x, lens):
+    B, P, _ = x.shape
+    ws = torch.empty(hs[0].workspace_size(B, P, sum(lens)), dtype=torch.uint8, device=DEV)
+    y = torch.full_like(x, 7.0)
+    ee.ee_stack_forward(hs, x, lens, y, ws)
+    torch.cuda.synchronize()
+    return y
+
+
+def _pads_zero(y, lens):
+    for b, n in enumerate(lens):
+        pad = y[b, n:]
+        assert torch.all(pad == 0) and not torch.any(torch.signbit(pad)), f"pads of sequence {b}"
+
+
+def _oracle_rows(w, x, params, lens, picks):
+    """The oracle's output rows of the picked sequences through every layer."""
+    rows = np.concatenate([x[b, :lens[b]].double().cpu().numpy() for b in picks])
+    cu = np.concatenate([[0], np.cumsum([lens[b] for b in picks])])
+    for l, p in enumerate(params):
+        rows = oracle.layer_forward_packed(rows, cu, p, w.n_heads, w.head_dim)
+        say(f"  oracle layer {l + 1}/{len(params)} done")
+    return rows, cu
+
+
+@pytest.mark.timeout(900)
+def test_gpt3_12l_stack_sampled_sequences():
+    torch.cuda.empty_cache()
+    w = workloads.get("gpt3-12l")
+    lens = workloads.lengths(w, SEED)
+    x, params, hs = _setup(w, SEED, lens, w.layers)
+    y = _stack(hs, x, lens)
+    _pads_zero(y, lens)
+    assert torch.isfinite(y).all()
+    picks = [0, len(lens) - 1]
+    ref, cu = _oracle_rows(w, x, params, lens, picks)
+    for i, b in enumerate(picks):
+        err = normwise_rel(to_host64(y[b, :lens[b]]), ref[cu[i]:cu[i + 1]])
+        say(f"gpt3-12l sequence {b} (len {lens[b]}) through 12 layers: rel {err:.3e}")
+        assert err <= 2e-2
+
+
+@pytest.mark.timeout(600)
+def test_gpt3_tp4_shard_sampled_sequences():
+    torch.cuda.empty_cache()
+    w = workloads.get("gpt3-tp4-shard")
+    lens = workloads.lengths(w, SEED)
+    x, params, hs = _setup(w, SEED, lens, 1)
+    y = _stack(hs, x, lens)
+    _pads_zero(y, lens)
+    order = sorted(range(len(lens)), key=lambda b: lens[b])
+    picks = sorted({0, len(lens) - 1, order[0], order[-1]})
+    ref, cu = _oracle_rows(w, x, params, lens, picks)
+    for i, b in enumerate(picks):
+        err = normwise_rel(to_host64(y[b, :lens[b]]), ref[cu[i]:cu[i + 1]])
+        say(f"gpt3-tp4-shard sequence {b} (len {lens[b]}): rel {err:.3e}")
+        assert err <= 2e-2
+
+
+@pytest.mark.timeout(900)
+def test_gpt3_48l_stream_sequence_independence():
+    """The 48-layer request stream: two FIFO batches (the first and the last)
+    through all 48 layers; the shortest and longest sequence of each, run alone
+    and unpadded, must reproduce their rows of the batch bit for bit (the GEMM
+    K order does not depend on M or the tile, attention and LayerNorm are per
+    sequence / per row).  Pads +0.0, outputs finite."""
+    torch.cuda.empty_cache()
+    w = workloads.get("gpt3-48l-stream")
+    groups = workloads.request_stream(w, SEED)
+    params = [workloads.layer_params(w, SEED, l, device=DEV) for l in range(w.layers)]
+    hs = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=ee.F16) for p in params]
+    for gi in (0, len(groups) - 1):
+        lens = groups[gi]
+        P = max(lens)                                  # padded to the batch's own maximum
+        x = workloads.activations(w, SEED, len(lens), P, lens, device=DEV, stream=1 + 1000 * (gi + 1))
+        y = _stack(hs, x, lens)
+        _pads_zero(y, lens)
+        assert torch.isfinite(y).all()
+        order = sorted(range(len(lens)), key=lambda b: lens[b])
+        for b in (order[0], order[-1]):
+            n = lens[b]
+            y1 = _stack(hs, x[b:b + 1, :n].contiguous(), [n])
+            same = torch.equal(y1[0], y[b, :n])
+            say(f"gpt3-48l-stream batch {gi} (T={sum(lens)}, P={P}) sequence {b} (len {n}) alone == in batch: {same}")
+            assert same

@@ -101,8 +101,9 @@ def test_nan_pads_do_not_reach_valid_rows():
 
 def test_each_sequence_alone_matches_batch():
     """Sequences are independent: running one alone, unpadded, gives its rows of
-    the batch (same kernels; compared to the oracle bound, not bitwise, since the
-    GEMM tiling of T rows differs)."""
+    the batch bit for bit (every GEMM output element accumulates its K tiles in
+    the same order whatever M and the tile shape are; attention is per
+    sequence, LayerNorm per row)."""
     w = workloads.get("gpt2-small")
     lens = workloads.lengths(w, 21)
     x = workloads.activations(w, 21, w.batch, w.pad_len, lens)
@@ -112,7 +113,7 @@ def test_each_sequence_alone_matches_batch():
         n = lens[b]
         w1 = dataclasses.replace(w, batch=1, pad_len=n)
         y1 = to_host64(_run_layer(w1, [n], x[b:b + 1, :n].contiguous(), p))
-        assert normwise_rel(y1[0], y[b, :n]) <= 5e-3
+        assert np.array_equal(y1[0], y[b, :n])
 
 
 def test_stack_matches_oracle():
