@@ -3,10 +3,12 @@
 // input + LayerNorm step in the announcement article's "Ease of use" listing;
 // the pre-LN placement inside the decoder block is this library's reading.)
 //
-// HBM-bound: one workgroup (4 waves) per row.  The row is read once into
-// registers with 16-byte loads, reduced twice (mean, then the centred sum of
-// squares, so no cancellation) through wave shuffles and a 4-entry LDS
-// exchange, and written once.  gamma/beta are re-read from L2 by every row.
+// HBM-bound.  Rows of up to 8 x 64 16-byte vectors (H <= 4096 in fp16, 2048
+// in fp32) go one wave per row; wider rows one workgroup (4 waves) per row,
+// which measured faster there (a wave holding a 12288-wide row needs all 256
+// VGPRs and leaves too few rows in flight).  Either way the row is read once into registers with 16-byte loads,
+// reduced twice (mean, then the centred sum of squares, so no cancellation)
+// and written once; gamma/beta are re-read from L2 by every row.
 #include "device_common.h"
 #include "internal.h"
 
@@ -41,6 +43,9 @@ struct Vec16<float> {
 };
 
 // VPT: 16-byte vectors per thread (compile-time upper bound; nvec <= VPT*256).
+// A workgroup walks rows blockIdx.x, +gridDim.x, ...; the next row's vectors
+// are requested before the current row's two reductions and store, so the
+// loads of one row overlap the barriers and stores of the previous one.
 template <typename T, int VPT>
 __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
                                                                const T* __restrict__ beta, int64_t rows, int H,
@@ -50,39 +55,37 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restri
   __shared__ float s_red[kLnThreads / kWave];
   const int nvec = H / E;
   const float inv_h = 1.0f / (float)H;
-  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+  V cur[VPT], nxt[VPT];
+  auto load = [&](V (&dst)[VPT], int64_t row) {
     const V* xr = reinterpret_cast<const V*>(x + row * H);
-    float v[VPT][E];
-    float s = 0.f;
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = threadIdx.x + i * kLnThreads;
-      if (c < nvec) {
-        const V a = __builtin_nontemporal_load(xr + c);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          v[i][e] = to_f32(a[e]);
-          s += v[i][e];
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[i][e] = 0.f;
-      }
+      if (c < nvec) dst[i] = __builtin_nontemporal_load(xr + c);
     }
+  };
+  int64_t row = blockIdx.x;
+  if (row < rows) load(cur, row);
+  for (; row < rows; row += gridDim.x) {
+    const int64_t next = row + gridDim.x;
+    if (next < rows) load(nxt, next);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (threadIdx.x + i * kLnThreads < nvec)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s += to_f32(cur[i][e]);
     const float mean = block_sum(s, s_red) * inv_h;
     float q = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      if (threadIdx.x + i * kLnThreads < nvec) {
+    for (int i = 0; i < VPT; ++i)
+      if (threadIdx.x + i * kLnThreads < nvec)
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float d = v[i][e] - mean;
+          const float d = to_f32(cur[i][e]) - mean;
           q += d * d;
         }
-      }
-    }
-    const float var = block_sum(q, s_red) * inv_h;
-    const float rstd = 1.0f / sqrtf(var + eps);
+    const float rstd = 1.0f / sqrtf(block_sum(q, s_red) * inv_h + eps);
     V* yr = reinterpret_cast<V*>(y + row * H);
     const V* gv = reinterpret_cast<const V*>(gamma);
     const V* bv = reinterpret_cast<const V*>(beta);
@@ -93,7 +96,66 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restri
         const V g = gv[c], b = bv[c];
         V o;
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = from_f32<T>((v[i][e] - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
+        for (int e = 0; e < E; ++e) o[e] = from_f32<T>((to_f32(cur[i][e]) - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
+        yr[c] = o;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
+  }
+}
+
+// One wave per row (4 rows per workgroup): the row is held in registers in
+// its storage type (VPL 16-byte vectors per lane), the two reductions are wave
+// shuffles, so rows never wait on each other at a barrier.
+template <typename T, int VPL>
+__global__ __launch_bounds__(kLnThreads) void layernorm_wave_kernel(const T* __restrict__ x,
+                                                                    const T* __restrict__ gamma,
+                                                                    const T* __restrict__ beta, int64_t rows,
+                                                                    int H, float eps, T* __restrict__ y) {
+  typedef typename Vec16<T>::type V;
+  constexpr int E = Vec16<T>::n;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int nvec = H / E;
+  const float inv_h = 1.0f / (float)H;
+  const int64_t row0 = (int64_t)blockIdx.x * (kLnThreads / kWave) + (threadIdx.x / kWave);
+  const int64_t stride = (int64_t)gridDim.x * (kLnThreads / kWave);
+  for (int64_t row = row0; row < rows; row += stride) {
+    const V* xr = reinterpret_cast<const V*>(x + row * H);
+    V v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nvec) v[i] = __builtin_nontemporal_load(xr + c);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (lane + i * kWave < nvec)
+#pragma unroll
+        for (int e = 0; e < E; ++e) s += to_f32(v[i][e]);
+    const float mean = wave_sum(s) * inv_h;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+      if (lane + i * kWave < nvec)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = to_f32(v[i][e]) - mean;
+          q += d * d;
+        }
+    const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_h + eps);
+    V* yr = reinterpret_cast<V*>(y + row * H);
+    const V* gv = reinterpret_cast<const V*>(gamma);
+    const V* bv = reinterpret_cast<const V*>(beta);
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+      const int c = lane + i * kWave;
+      if (c < nvec) {
+        const V g = gv[c], b = bv[c];
+        V o;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = from_f32<T>((to_f32(v[i][e]) - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
         yr[c] = o;
       }
     }
@@ -104,11 +166,26 @@ template <typename T>
 hipError_t launch_ln_t(const void* x, const void* g, const void* b, int64_t rows, int H, float eps, void* y,
                        hipStream_t s) {
   const int nvec = H / Vec16<T>::n;
-  const unsigned grid = (unsigned)(rows > (1 << 20) ? (1 << 20) : rows);
+  // block kernel: a few workgroups per CU, each walking several rows
+  const unsigned grid = (unsigned)(rows > 2048 ? 2048 : rows);
   const T* xp = static_cast<const T*>(x);
   const T* gp = static_cast<const T*>(g);
   const T* bp = static_cast<const T*>(b);
   T* yp = static_cast<T*>(y);
+  if (nvec <= 8 * kWave) {  // narrow rows: one wave per row
+    const int64_t wgs = (rows + 3) / 4;
+    const dim3 wg((unsigned)(wgs > (1 << 20) ? (1 << 20) : wgs)), blk(kLnThreads);
+    const int vpl = (nvec + kWave - 1) / kWave;
+    if (vpl <= 1)
+      hipLaunchKernelGGL((layernorm_wave_kernel<T, 1>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+    else if (vpl <= 2)
+      hipLaunchKernelGGL((layernorm_wave_kernel<T, 2>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+    else if (vpl <= 4)
+      hipLaunchKernelGGL((layernorm_wave_kernel<T, 4>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+    else
+      hipLaunchKernelGGL((layernorm_wave_kernel<T, 8>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+    return hipGetLastError();
+  }
   if (nvec <= 256)
     hipLaunchKernelGGL((layernorm_kernel<T, 1>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
   else if (nvec <= 512)
