@@ -55,6 +55,53 @@ __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r 
 // global_load_lds as an LDS write.  The memory clobber keeps LDS reads below it.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Tile origin of this workgroup: XCD-contiguous ranges of workgroup ids,
+// walked in groups of 4 M-tiles (see the file comment).
+template <int BM, int BN>
+__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int& m0, int& n0) {
+  int bid = blockIdx.x;
+  const int nblk = gridDim.x;
+  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
+  constexpr int GM = 4;
+  const int per_group = GM * tiles_n;
+  const int group = bid / per_group;
+  const int first_m = group * GM;
+  const int gm = min(tiles_m - first_m, GM);
+  const int ig = bid - group * per_group;
+  m0 = (first_m + ig % gm) * BM;
+  n0 = (ig / gm) * BN;
+}
+
+// Epilogue of a wave's FM x FN block of 32 x 32 fragments whose top-left
+// output element is (row0, col0).  Fragment element e of lane l is row
+// (e/4)*8 + (l/32)*4 + e%4, column l%32 of its block.
+template <int FM, int FN, int EPI>
+__device__ __forceinline__ void store_tile(const floatx16 (&acc)[FM][FN], int row0, int col0, int lane,
+                                           const f16* __restrict__ bias, const f16* __restrict__ R,
+                                           f16* __restrict__ C, int M, int N, int gelu_form) {
+  const int hk = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = col0 + j * 32 + (lane & 31);
+    if (col >= N) continue;
+    const float bcol = (EPI != EE_EPI_NONE) ? (float)bias[col] : 0.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int rbase = row0 + i * 32 + hk * 4;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = rbase + (e >> 2) * 8 + (e & 3);
+        if (row < M) {
+          float v = acc[i][j][e] + bcol;
+          if (EPI == EE_EPI_BIAS_RESIDUAL) v += (float)R[(int64_t)row * N + col];
+          if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
+          C[(int64_t)row * N + col] = (f16)v;
+        }
+      }
+    }
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16* __restrict__ A, const f16* __restrict__ W,
                                                                  const f16* __restrict__ bias,
@@ -68,18 +115,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   constexpr int STAGE = (BM + BN) * kBK;     // halves per LDS stage
   __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
 
-  // ---- tile assignment: XCD-contiguous ranges, grouped 4 M-tiles at a time
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  constexpr int GM = 4;
-  const int per_group = GM * tiles_n;
-  const int group = bid / per_group;
-  const int first_m = group * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int ig = bid - group * per_group;
-  const int m0 = (first_m + ig % gm) * BM;
-  const int n0 = (ig / gm) * BN;
+  int m0, n0;
+  tile_origin<BM, BN>(tiles_m, tiles_n, m0, n0);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -214,28 +251,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   mfmas(fa1, fb1);
   wait_dma();  // no load may still be writing LDS when the workgroup retires
 
-  // ---- epilogue.  Fragment element e of lane l is row (e/4)*8 + (l/32)*4 + e%4,
-  // column l%32 of its 32 x 32 block.
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = n0 + wn * WTN + j * 32 + (lane & 31);
-    if (col >= N) continue;
-    const float bcol = (EPI != EE_EPI_NONE) ? (float)bias[col] : 0.f;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int rbase = m0 + wm * WTM + i * 32 + hk * 4;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = rbase + (e >> 2) * 8 + (e & 3);
-        if (row < M) {
-          float v = acc[i][j][e] + bcol;
-          if (EPI == EE_EPI_BIAS_RESIDUAL) v += (float)R[(int64_t)row * N + col];
-          if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
-          C[(int64_t)row * N + col] = (f16)v;
-        }
-      }
-    }
-  }
+  store_tile<FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
 }
 
 template <int BM, int BN, int WGM, int WGN>
