@@ -56,6 +56,13 @@ def build(verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    # resolve every symbol now: an undefined one (e.g. a kernel stub the host
+    # pass did not emit) fails the build here rather than at first use
+    import ctypes
+    try:
+        ctypes.CDLL(tmp, mode=os.RTLD_NOW)
+    except OSError as e:
+        raise RuntimeError(f"linked library does not load: {e}") from None
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}", flush=True)

@@ -12,7 +12,7 @@
 //     two per SIMD; 128 x 128: 2 x 2); a wave owns a block of 32 x 32
 //     v_mfma_f32_32x32x16_f16 fragments with fp32 accumulators in registers.
 //   * Two LDS stages (BM=BN=256: 2 x 64 KiB of the 160 KiB per CU) filled by
-//     gfx950's 16-byte direct-to-LDS loads (global_load_lds_dwordx4): no
+//     16-byte direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no
 //     register staging and no LDS store instructions.  Tile kt+2 is requested
 //     right after the barrier that retires tile kt's stage, so a load has a
 //     whole K tile of MFMA work to land; one barrier per K tile.
@@ -26,8 +26,9 @@
 //     the 8 XCDs, so ids are remapped to give each XCD a contiguous range, and
 //     that range walks tiles in groups of 4 M-tiles, so the workgroups that
 //     share an XCD's L2 share A and W panels.
-//   * Ragged M (and N): out-of-range rows load a clamped in-range row, and
-//     their results are never stored.  K must be a multiple of 64.
+//   * Ragged M (and N): the buffer descriptors end at the last valid row, so
+//     out-of-range rows load zeros; their results are never stored.  K must be
+//     a multiple of 64, and 256 rows x K x 2 bytes must fit 32-bit offsets.
 #include <type_traits>
 
 #include "device_common.h"
@@ -46,13 +47,22 @@ constexpr int kBK = 64;
 
 __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-#define EE_GLOBAL(p) ((__attribute__((address_space(1))) void*)(p))
+// 16-byte direct-to-LDS buffer load, wrapped in a device-only function: the
+// builtin needs a device target feature, and calling it from a lambda (which
+// HIP compiles for both sides) makes the host pass drop the kernel's stub.
+__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset, int soffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
+}
+
+// Word 3 of a raw (unformatted, stride 0) buffer descriptor on gfx9-family GPUs.
+constexpr int kBufferFlags = 0x00020000;
+
 #define EE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
 
 // Waits until this wave's direct-to-LDS loads have written LDS.  Needed before
 // the barrier that publishes them: the workgroup-scope fence of __syncthreads
 // only waits for LDS instructions (lgkmcnt), and the compiler does not count
-// global_load_lds as an LDS write.  The memory clobber keeps LDS reads below it.
+// a direct-to-LDS load as an LDS write.  The memory clobber keeps LDS reads below it.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // Tile origin of this workgroup: XCD-contiguous ranges of workgroup ids,
@@ -123,30 +133,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);  // wave-uniform: keeps LDS bases scalar
 
   // ---- global -> LDS: each wave fills rows [wave*BM/NW, (wave+1)*BM/NW) of the A
-  // tile (and likewise of W) with 16-byte direct-to-LDS loads.  One load of a
-  // wave writes 1 KiB of LDS = 8 rows; lane l lands in row l/8, physical chunk
-  // l%8, so it fetches the logical chunk (l%8) ^ f(row) from global memory.
+  // tile (and likewise of W) with 16-byte direct-to-LDS buffer loads.  One load
+  // of a wave writes 1 KiB of LDS = 8 rows; lane l lands in row l/8, physical
+  // chunk l%8, so it fetches the logical chunk (l%8) ^ f(row).  The buffer
+  // descriptors start at the tile's first row and end at the last valid row
+  // (M or N), so rows past the end read as zeros and offsets stay 32-bit.
   const int lr = lane >> 3, lp = lane & 7;
-  const f16* asrc[AJ];
-  const f16* bsrc[BJ];
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + (int64_t)m0 * K), (short)0, min(BM, M - m0) * K * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(W + (int64_t)n0 * K), (short)0, min(BN, N - n0) * K * 2, kBufferFlags);
+  int aoff[AJ], boff[BJ];  // byte offsets of this lane's 16-byte chunk, K tile 0
 #pragma unroll
   for (int j = 0; j < AJ; ++j) {
     const int r = wave * (BM / NW) + 8 * j + lr;
-    asrc[j] = A + (int64_t)min(m0 + r, M - 1) * K + ((lp ^ lds_swizzle(r)) * 8);
+    aoff[j] = (r * K + ((lp ^ lds_swizzle(r)) * 8)) * 2;
   }
 #pragma unroll
   for (int j = 0; j < BJ; ++j) {
     const int r = wave * (BN / NW) + 8 * j + lr;
-    bsrc[j] = W + (int64_t)min(n0 + r, N - 1) * K + ((lp ^ lds_swizzle(r)) * 8);
+    boff[j] = (r * K + ((lp ^ lds_swizzle(r)) * 8)) * 2;
   }
   // load q of a K tile: q < AJ -> rows of A, else rows of W
   auto dma_one = [&](int stage, int k0, int q) {
     if (q < AJ) {
       f16* sa = smem + stage * STAGE + (wave * (BM / NW) + 8 * q) * kBK;
-      __builtin_amdgcn_global_load_lds(EE_GLOBAL(asrc[q] + k0), EE_LOCAL(sa), 16, 0, 0);
+      buffer_load_lds16(arsrc, sa, aoff[q], k0 * 2);
     } else {
       f16* sb = smem + stage * STAGE + BM * kBK + (wave * (BN / NW) + 8 * (q - AJ)) * kBK;
-      __builtin_amdgcn_global_load_lds(EE_GLOBAL(bsrc[q - AJ] + k0), EE_LOCAL(sb), 16, 0, 0);
+      buffer_load_lds16(wrsrc, sb, boff[q - AJ], k0 * 2);
     }
   };
   auto dma = [&](int stage, int k0) {
@@ -288,7 +303,7 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
 }  // namespace
 
 bool gemm_f16_mfma_ok(int64_t M, int N, int K) {
-  return M >= 1 && M <= (1 << 30) && N >= 1 && K >= kBK && K % kBK == 0;
+  return M >= 1 && M <= (1 << 30) && N >= 1 && K >= kBK && K % kBK == 0 && (int64_t)256 * K * 2 < (1ll << 31);
 }
 
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
