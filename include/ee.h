@@ -81,6 +81,22 @@ typedef enum {
   EE_EPI_BIAS_GELU = 3
 } ee_epilogue;
 
+/* Block form.  GPT_PRELN: the pre-LN causal decoder block,
+ *   a = LN1(x); h = x + Out(Attn(QKV(a))); y = h + FC2(gelu(FC1(LN2(h)))).
+ * BERT_POSTLN: the post-LN bidirectional encoder block (the EnergonAI README
+ * lists BERT among its models), with the add bias + input + LayerNorm step of
+ * the announcement article's "Ease of use" listing after each sublayer:
+ *   h = LN1(x + Out(Attn(QKV(x)))); y = LN2(h + FC2(gelu(FC1(h)))). */
+typedef enum { EE_BLOCK_GPT_PRELN = 0, EE_BLOCK_BERT_POSTLN = 1 } ee_block;
+
+/* Attention form.  VARLEN: per sequence directly over the packed rows.
+ * PADDED: the page-literal form of the announcement article's "Runtime"
+ * section (remove/rebuild around the MLP layers): a transposing rebuild scatters
+ * the packed q|k|v into head-major padded [B, nh, P, hd] tensors, attention runs
+ * on them with the key mask, a transposing remove gathers the output back.
+ * Valid rows are the same either way. */
+typedef enum { EE_ATTN_VARLEN = 0, EE_ATTN_PADDED = 1 } ee_attention;
+
 typedef struct {
   int32_t hidden;    /* H */
   int32_t n_heads;   /* nh */
@@ -90,6 +106,8 @@ typedef struct {
   ee_dtype dtype;
   ee_gelu gelu;
   int32_t fuse_gelu; /* 1: bias+GeLU in the FC1 GEMM epilogue; 0: separate bias+GeLU kernel */
+  ee_block block;
+  ee_attention attention;
 } ee_layer_desc;
 
 /* Device pointers, all of the descriptor's dtype, borrowed (not copied) by
@@ -193,13 +211,45 @@ EE_API ee_status ee_linear(const void* A, const void* W, const void* bias, const
 EE_API ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t cols, ee_dtype dtype,
                        ee_gelu gelu, void* g, void* stream);
 
-/* Causal attention per sequence over packed offsets.  qkv [T, 3H'] (q | k | v,
+/* Attention per sequence over packed offsets.  qkv [T, 3H'] (q | k | v,
  * head-major), d_cu [batch+1] device int32 (e.g. from ee_compute_offsets),
- * o [T, H'].  Query i of sequence b attends to keys cu[b] .. cu[b]+i with
- * weights softmax(q.k / sqrt(head_dim)); max_len >= every sequence length. */
+ * o [T, H'].  Query i of sequence b attends with weights
+ * softmax(q.k / sqrt(head_dim)) to keys cu[b] .. cu[b]+i (causal != 0) or to
+ * all keys of its sequence (causal == 0); max_len >= every sequence length. */
 EE_API ee_status ee_attention_varlen(const void* qkv, const int32_t* d_cu, int32_t batch, int32_t max_len,
-                              int32_t n_heads, int32_t head_dim, int64_t total_tokens,
+                              int32_t n_heads, int32_t head_dim, int64_t total_tokens, int32_t causal,
                               ee_dtype dtype, void* o, void* stream);
+
+/* The same attention on padded head-major tensors q, k, v, o [batch, n_heads,
+ * pad_len, head_dim], lengths from d_cu [batch+1]: keys j < len[b] (and j <= i
+ * when causal) of the same (sequence, head); rows p >= len[b] of o are not
+ * written. */
+EE_API ee_status ee_attention_padded(const void* q, const void* k, const void* v, const int32_t* d_cu,
+                                     int32_t batch, int32_t pad_len, int32_t n_heads, int32_t head_dim,
+                                     int32_t causal, ee_dtype dtype, void* o, void* stream);
+
+/* Transposing rebuild (announcement article, "Runtime"): packed [T, n_mats *
+ * n_heads * head_dim] (n_mats column blocks, each head-major) -> d_heads
+ * [n_mats, batch, n_heads, pad_len, head_dim], pads +0.0.  seq_lens host;
+ * workspace: ee_padding_workspace_size bytes.  head_dim*sizeof(dtype) % 16 == 0. */
+EE_API ee_status ee_transpose_padding_rebuild_heads(const void* d_packed, const int32_t* seq_lens, int32_t batch,
+                                                    int32_t pad_len, int32_t n_mats, int32_t n_heads,
+                                                    int32_t head_dim, ee_dtype dtype, void* d_heads,
+                                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* Transposing remove: d_heads [batch, n_heads, pad_len, head_dim] -> packed
+ * [T, n_heads * head_dim] (valid rows only). */
+EE_API ee_status ee_transpose_padding_remove_heads(const void* d_heads, const int32_t* seq_lens, int32_t batch,
+                                                   int32_t pad_len, int32_t n_heads, int32_t head_dim,
+                                                   ee_dtype dtype, void* d_packed, void* workspace,
+                                                   size_t ws_bytes, void* stream);
+
+/* y = LN(u + bias + residual) per row (the add bias + input + LayerNorm step
+ * of the announcement article's "Ease of use" listing); the sum is formed in
+ * fp32 and not stored.  u, residual, y [rows, hidden]; bias, gamma, beta [hidden]. */
+EE_API ee_status ee_add_bias_residual_layernorm(const void* u, const void* bias, const void* residual,
+                                                const void* gamma, const void* beta, int64_t rows, int32_t hidden,
+                                                float eps, ee_dtype dtype, void* y, void* stream);
 
 /* ---- per-kernel timing ----------------------------------------------------- */
 /* While enabled, every kernel that the calls above launch from this process is

@@ -213,12 +213,19 @@ def _block(x: np.ndarray, attn_fn, p: Dict[str, np.ndarray], eps: float, gelu_fo
 
 
 def layer_forward_packed(x_packed: np.ndarray, cu: Sequence[int], params: Dict, n_heads: int, head_dim: int,
-                         eps: float = 1e-5, gelu_form: str = "tanh", keep: Dict = None) -> np.ndarray:
+                         eps: float = 1e-5, gelu_form: str = "tanh", keep: Dict = None, attention: str = "varlen",
+                         pad_len: int = 0) -> np.ndarray:
     """The RCE form: every row operation on the T packed valid rows; attention
-    per sequence over cu.  `keep` (a dict) receives every intermediate."""
+    per sequence over cu ("varlen"), or, in the page-literal form ("padded"),
+    through the transposing rebuild, padded attention and transposing remove.
+    `keep` (a dict) receives every intermediate."""
     p = to_f64_params(params)
     x = np.asarray(x_packed, _F64)
-    return _block(x, lambda qkv: causal_attention_packed(qkv, cu, n_heads, head_dim), p, eps, gelu_form, keep)
+    if attention == "varlen":
+        attn = lambda qkv: causal_attention_packed(qkv, cu, n_heads, head_dim)  # noqa: E731
+    else:
+        attn = lambda qkv: attention_via_padded_heads(qkv, cu, pad_len, n_heads, head_dim, causal=True)  # noqa: E731
+    return _block(x, attn, p, eps, gelu_form, keep)
 
 
 def layer_forward_padded(x_padded: np.ndarray, lens: Sequence[int], params: Dict, n_heads: int, head_dim: int,
@@ -255,3 +262,149 @@ def stack_forward_packed(x_padded, lens, params_list: List[Dict], n_heads: int, 
     for params in params_list:
         y = layer_forward_packed(y, cu, params, n_heads, head_dim, eps, gelu_form)
     return rebuild_padding(y, lens, x_padded.shape[1])
+
+
+# ---------------------------------------------------------------------------
+# The page-literal form of RCE (announcement article, "Runtime": the
+# remove/rebuild ops serve the MLP layers of encoders and decoders), read as:
+# attention stays padded.  A transposing rebuild scatters the packed q|k|v rows
+# into head-major padded tensors [B, nh, P, hd] (pads zero), attention runs on
+# the padded tensors with a key mask, and a transposing remove gathers the
+# valid rows back into the packed [T, nh*hd] layout.
+# ---------------------------------------------------------------------------
+def transpose_padding_rebuild_heads(packed: np.ndarray, lens: Sequence[int], pad_len: int, n_heads: int,
+                                    head_dim: int) -> np.ndarray:
+    """packed [T, n*nh*hd] (n blocks of nh*hd columns, each head-major) ->
+    [n, B, nh, P, hd]: out[m, b, h, p, d] = packed[cu[b]+p, m*nh*hd + h*hd + d]
+    for p < len[b], else 0."""
+    packed = np.asarray(packed)
+    Hp = n_heads * head_dim
+    n = packed.shape[1] // Hp
+    B = len(lens)
+    out = np.zeros((n, B, n_heads, pad_len, head_dim), dtype=packed.dtype)
+    t = 0
+    for b in range(B):
+        for p in range(int(lens[b])):
+            for m in range(n):
+                for h in range(n_heads):
+                    out[m, b, h, p] = packed[t, m * Hp + h * head_dim:m * Hp + (h + 1) * head_dim]
+            t += 1
+    return out
+
+
+def transpose_padding_remove_heads(x: np.ndarray, lens: Sequence[int]) -> np.ndarray:
+    """[B, nh, P, hd] -> packed [T, nh*hd]: row cu[b]+p holds x[b, h, p, :] for
+    every head h, in head order."""
+    x = np.asarray(x)
+    B, nh, P, hd = x.shape
+    rows = []
+    for b in range(B):
+        for p in range(int(lens[b])):
+            rows.append(np.concatenate([x[b, h, p] for h in range(nh)]))
+    if not rows:
+        return np.zeros((0, nh * hd), dtype=x.dtype)
+    return np.stack(rows)
+
+
+def attention_padded_heads(q: np.ndarray, k: np.ndarray, v: np.ndarray, lens: Sequence[int],
+                           causal: bool) -> np.ndarray:
+    """Attention on padded head-major tensors [B, nh, P, hd]: valid query p of
+    sequence b attends to the keys j < len[b] (and j <= p when causal); pad
+    query positions give 0."""
+    q, k, v = (np.asarray(a, _F64) for a in (q, k, v))
+    B, nh, P, hd = q.shape
+    o = np.zeros((B, nh, P, hd), dtype=_F64)
+    scale = 1.0 / math.sqrt(hd)
+    for b in range(B):
+        n = int(lens[b])
+        for h in range(nh):
+            for p in range(n):
+                jmax = p + 1 if causal else n
+                o[b, h, p] = _attend_one_query(q[b, h, p], k[b, h, :jmax], v[b, h, :jmax], scale)
+    return o
+
+
+def add_bias_residual_layernorm(u: np.ndarray, bias: np.ndarray, residual: np.ndarray, gamma: np.ndarray,
+                                beta: np.ndarray, eps: float) -> np.ndarray:
+    """LN(u + bias + residual): the add bias + input + LayerNorm step of the
+    announcement article's "Ease of use" listing (post-LN blocks)."""
+    return layer_norm(np.asarray(u, _F64) + np.asarray(bias, _F64) + np.asarray(residual, _F64), gamma, beta, eps)
+
+
+def attention_packed_bidirectional(qkv: np.ndarray, cu: Sequence[int], n_heads: int, head_dim: int) -> np.ndarray:
+    """Encoder attention per sequence over the packed offsets: every query of
+    sequence b attends to all of that sequence's keys (key-padding mask only)."""
+    qkv = np.asarray(qkv, _F64)
+    q, k, v = _split_qkv(qkv, n_heads, head_dim)
+    o = np.zeros((qkv.shape[0], n_heads * head_dim), dtype=_F64)
+    scale = 1.0 / math.sqrt(head_dim)
+    for b in range(len(cu) - 1):
+        s0, s1 = int(cu[b]), int(cu[b + 1])
+        for n in range(n_heads):
+            c = slice(n * head_dim, (n + 1) * head_dim)
+            for i in range(s1 - s0):
+                o[s0 + i, c] = _attend_one_query(q[s0 + i, c], k[s0:s1, c], v[s0:s1, c], scale)
+    return o
+
+
+def attention_via_padded_heads(qkv: np.ndarray, cu: Sequence[int], pad_len: int, n_heads: int, head_dim: int,
+                               causal: bool) -> np.ndarray:
+    """The page-literal attention on packed qkv: transposing rebuild, padded
+    attention, transposing remove."""
+    lens = [int(cu[b + 1]) - int(cu[b]) for b in range(len(cu) - 1)]
+    heads = transpose_padding_rebuild_heads(np.asarray(qkv, _F64), lens, pad_len, n_heads, head_dim)
+    o = attention_padded_heads(heads[0], heads[1], heads[2], lens, causal)
+    return transpose_padding_remove_heads(o, lens)
+
+
+def encoder_layer_forward_packed(x_packed: np.ndarray, cu: Sequence[int], params: Dict, n_heads: int,
+                                 head_dim: int, eps: float = 1e-5, gelu_form: str = "erf",
+                                 attention: str = "varlen", pad_len: int = 0, keep: Dict = None) -> np.ndarray:
+    """Post-LN encoder block (BERT-style; the EnergonAI README lists BERT among
+    its models) on the packed rows, with the chain of the "Ease of use" listing:
+      h = LN1(x + Out(Attn(QKV(x))))          (add bias + input + LayerNorm)
+      y = LN2(h + FC2(gelu(FC1(h))))          (GEMM, add bias + GELU, GEMM, add bias + input + LayerNorm)
+    Attention is bidirectional within each sequence.  The parameter names are
+    the decoder's: ln1_* is the attention-output LayerNorm, ln2_* the FFN one."""
+    p = to_f64_params(params)
+    x = np.asarray(x_packed, _F64)
+    qkv = linear(x, p["w_qkv"], p["b_qkv"])
+    if attention == "varlen":
+        o = attention_packed_bidirectional(qkv, cu, n_heads, head_dim)
+    else:
+        o = attention_via_padded_heads(qkv, cu, pad_len, n_heads, head_dim, causal=False)
+    a = o @ p["w_out"].T
+    h = add_bias_residual_layernorm(a, p["b_out"], x, p["ln1_g"], p["ln1_b"], eps)
+    g = gelu(linear(h, p["w_fc1"], p["b_fc1"]), gelu_form)
+    u = g @ p["w_fc2"].T
+    y = add_bias_residual_layernorm(u, p["b_fc2"], h, p["ln2_g"], p["ln2_b"], eps)
+    if keep is not None:
+        keep.update(qkv=qkv, o=o, h=h, g=g, y=y)
+    return y
+
+
+def encoder_layer_forward_padded(x_padded: np.ndarray, lens: Sequence[int], params: Dict, n_heads: int,
+                                 head_dim: int, eps: float = 1e-5, gelu_form: str = "erf") -> np.ndarray:
+    """The encoder definition on the padded batch: every padded row goes
+    through the block, keys masked to the valid ones, pads of the output +0.0."""
+    p = to_f64_params(params)
+    x = np.asarray(x_padded, _F64)
+    B, P, H = x.shape
+    out = np.zeros((B, P, H), dtype=_F64)
+    for b in range(B):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        xb = x[b]
+        qkv = linear(xb, p["w_qkv"], p["b_qkv"])
+        q, k, v = _split_qkv(qkv, n_heads, head_dim)
+        o = np.zeros((P, n_heads * head_dim))
+        for hh in range(n_heads):
+            c = slice(hh * head_dim, (hh + 1) * head_dim)
+            for i in range(P):
+                o[i, c] = _attend_one_query(q[i, c], k[:n, c], v[:n, c], 1.0 / math.sqrt(head_dim))
+        h = add_bias_residual_layernorm(o @ p["w_out"].T, p["b_out"], xb, p["ln1_g"], p["ln1_b"], eps)
+        g = gelu(linear(h, p["w_fc1"], p["b_fc1"]), gelu_form)
+        y = add_bias_residual_layernorm(g @ p["w_fc2"].T, p["b_fc2"], h, p["ln2_g"], p["ln2_b"], eps)
+        out[b, :n] = y[:n]
+    return out

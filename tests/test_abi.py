@@ -35,7 +35,8 @@ def test_status_strings_and_version():
 
 
 def _desc(**kw):
-    d = dict(hidden=64, n_heads=4, head_dim=16, ffn=256, ln_eps=1e-5, dtype=ee.F32, gelu=ee.GELU_TANH, fuse_gelu=1)
+    d = dict(hidden=64, n_heads=4, head_dim=16, ffn=256, ln_eps=1e-5, dtype=ee.F32, gelu=ee.GELU_TANH, fuse_gelu=1,
+             block=ee.BLOCK_GPT_PRELN, attention=ee.ATTN_VARLEN)
     d.update(kw)
     return ee.LayerDesc(*[d[k] for k, _ in ee.LayerDesc._fields_])
 
@@ -53,7 +54,7 @@ def _create(desc, weights):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=24), 2), (dict(head_dim=256), 2), (dict(hidden=0), 1), (dict(ln_eps=0.0), 1),
     (dict(dtype=7), 1), (dict(gelu=5), 1), (dict(fuse_gelu=2), 1), (dict(hidden=66), 2),
-    (dict(hidden=65536 * 4, ffn=256), 2),
+    (dict(hidden=65536 * 4, ffn=256), 2), (dict(block=2), 1), (dict(attention=3), 1),
 ])
 def test_layer_create_rejects_bad_descriptors(kw, status):
     st, h = _create(_desc(**kw), _weights())
@@ -126,7 +127,19 @@ def test_op_entry_points_validate():
     # M = 0 is a valid no-op
     assert lib.ee_linear(None, 1 << 31, None, None, 0, 64, 64, ee.F16, ee.EPI_NONE, 0, None, None) == 0
     # attention: unsupported head_dim
-    assert lib.ee_attention_varlen(1 << 30, 1 << 31, 2, 8, 4, 48, 10, ee.F16, 1 << 32, None) == 2
+    assert lib.ee_attention_varlen(1 << 30, 1 << 31, 2, 8, 4, 48, 10, 1, ee.F16, 1 << 32, None) == 2
+    assert lib.ee_attention_padded(1 << 30, 1 << 31, 1 << 32, 1 << 33, 2, 8, 4, 24, 1, ee.F16, 1 << 34, None) == 2
+    assert lib.ee_attention_padded(1 << 30, 1 << 31, 1 << 32, (1 << 30) + 64, 2, 8, 4, 16, 1, ee.F16, 1 << 30,
+                                   None) == 1                               # o overlaps q
+    n = C.c_size_t(0)
+    assert lib.ee_padding_workspace_size(2, 8, C.byref(n)) == 0
+    # head rows must be 16-byte multiples; lengths within pad_len
+    assert lib.ee_transpose_padding_rebuild_heads(1 << 30, lens, 2, 8, 3, 4, 4, ee.F16, 1 << 31, 1 << 32, n.value,
+                                                  None) == 2
+    assert lib.ee_transpose_padding_remove_heads(1 << 30, (C.c_int32 * 2)(3, 9), 2, 8, 4, 16, ee.F16, 1 << 31,
+                                                 1 << 32, n.value, None) == 1
+    assert lib.ee_add_bias_residual_layernorm(1 << 30, 1 << 31, 1 << 32, 1 << 33, 1 << 34, 4, 64, 1e-5, ee.F16,
+                                              1 << 30, None) == 1           # y aliases u
     # layernorm: hidden too large / eps <= 0
     assert lib.ee_layernorm(1 << 30, 1 << 31, 1 << 32, 4, 1 << 20, 1e-5, ee.F16, 1 << 33, None) == 2
     assert lib.ee_layernorm(1 << 30, 1 << 31, 1 << 32, 4, 64, -1.0, ee.F16, 1 << 33, None) == 1

@@ -16,13 +16,18 @@ __all__ = [
     "EPI_NONE", "EPI_BIAS", "EPI_BIAS_RESIDUAL", "EPI_BIAS_GELU",
     "ee_compute_offsets", "ee_compute_offsets_mask", "ee_padding_workspace_size",
     "ee_remove_padding", "ee_rebuild_padding", "ee_layernorm", "ee_linear", "ee_bias_gelu",
-    "ee_attention_varlen", "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_collect",
+    "ee_attention_varlen", "ee_attention_padded", "ee_transpose_padding_rebuild_heads",
+    "ee_transpose_padding_remove_heads", "ee_add_bias_residual_layernorm",
+    "BLOCK_GPT_PRELN", "BLOCK_BERT_POSTLN", "ATTN_VARLEN", "ATTN_PADDED",
+    "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_collect",
     "EXPORTED_SYMBOLS", "lib_path",
 ]
 
 F32, F16 = 0, 1
 GELU_TANH, GELU_ERF = 0, 1
 EPI_NONE, EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3
+BLOCK_GPT_PRELN, BLOCK_BERT_POSTLN = 0, 1
+ATTN_VARLEN, ATTN_PADDED = 0, 1
 MAX_BATCH = 512
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -44,7 +49,8 @@ _STATUS = {0: "EE_OK", 1: "EE_ERR_INVALID_ARG", 2: "EE_ERR_UNSUPPORTED", 3: "EE_
 
 class LayerDesc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
-                ("ln_eps", C.c_float), ("dtype", C.c_int), ("gelu", C.c_int), ("fuse_gelu", C.c_int32)]
+                ("ln_eps", C.c_float), ("dtype", C.c_int), ("gelu", C.c_int), ("fuse_gelu", C.c_int32),
+                ("block", C.c_int), ("attention", C.c_int)]
 
 
 WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_out", "b_out",
@@ -80,7 +86,14 @@ _SIGS = {
     "ee_layernorm": (C.c_int, [_VP, _VP, _VP, _I64, _I32, C.c_float, C.c_int, _VP, _VP]),
     "ee_linear": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP, _VP]),
     "ee_bias_gelu": (C.c_int, [_VP, _VP, _I64, _I32, C.c_int, C.c_int, _VP, _VP]),
-    "ee_attention_varlen": (C.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I64, C.c_int, _VP, _VP]),
+    "ee_attention_varlen": (C.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I64, _I32, C.c_int, _VP, _VP]),
+    "ee_attention_padded": (C.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_int, _VP, _VP]),
+    "ee_transpose_padding_rebuild_heads": (C.c_int, [_VP, _PI32, _I32, _I32, _I32, _I32, _I32, C.c_int, _VP, _VP,
+                                                     _SZ, _VP]),
+    "ee_transpose_padding_remove_heads": (C.c_int, [_VP, _PI32, _I32, _I32, _I32, _I32, C.c_int, _VP, _VP, _SZ,
+                                                    _VP]),
+    "ee_add_bias_residual_layernorm": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I32, C.c_float, C.c_int, _VP,
+                                                 _VP]),
     "ee_profile_enable": (C.c_int, [_I32]),
     "ee_profile_collect": (C.c_int, [C.POINTER(KernelStat), _I32, _PI32]),
 }
@@ -192,9 +205,43 @@ def ee_bias_gelu(u, bias, g, gelu: int = GELU_TANH, stream=None):
            "ee_bias_gelu")
 
 
-def ee_attention_varlen(qkv, cu, batch: int, max_len: int, n_heads: int, head_dim: int, o, stream=None):
+def ee_attention_varlen(qkv, cu, batch: int, max_len: int, n_heads: int, head_dim: int, o, causal: bool = True,
+                        stream=None):
     _check(lib().ee_attention_varlen(_ptr(qkv), _ptr(cu), batch, max_len, n_heads, head_dim, qkv.shape[0],
-                                     _dtype_code(qkv), _ptr(o), _stream(stream)), "ee_attention_varlen")
+                                     1 if causal else 0, _dtype_code(qkv), _ptr(o), _stream(stream)),
+           "ee_attention_varlen")
+
+
+def ee_attention_padded(q, k, v, cu, o, causal: bool = True, stream=None):
+    """q, k, v, o: [B, nh, P, hd] head-major padded; cu [B+1] device int32."""
+    B, nh, P, hd = q.shape
+    _check(lib().ee_attention_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, P, nh, hd, 1 if causal else 0,
+                                     _dtype_code(q), _ptr(o), _stream(stream)), "ee_attention_padded")
+
+
+def ee_transpose_padding_rebuild_heads(packed, lens: Sequence[int], heads, workspace, stream=None):
+    """packed [T, n*nh*hd] -> heads [n, B, nh, P, hd] (pads zero)."""
+    n, B, nh, P, hd = heads.shape
+    _check(lib().ee_transpose_padding_rebuild_heads(_ptr(packed), _lens(lens), B, P, n, nh, hd, _dtype_code(heads),
+                                                    _ptr(heads), _ptr(workspace),
+                                                    workspace.numel() * workspace.element_size(), _stream(stream)),
+           "ee_transpose_padding_rebuild_heads")
+
+
+def ee_transpose_padding_remove_heads(heads, lens: Sequence[int], packed, workspace, stream=None):
+    """heads [B, nh, P, hd] -> packed [T, nh*hd]."""
+    B, nh, P, hd = heads.shape
+    _check(lib().ee_transpose_padding_remove_heads(_ptr(heads), _lens(lens), B, P, nh, hd, _dtype_code(heads),
+                                                   _ptr(packed), _ptr(workspace),
+                                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "ee_transpose_padding_remove_heads")
+
+
+def ee_add_bias_residual_layernorm(u, bias, residual, gamma, beta, eps: float, y, stream=None):
+    rows, H = u.shape
+    _check(lib().ee_add_bias_residual_layernorm(_ptr(u), _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(beta), rows, H,
+                                                eps, _dtype_code(u), _ptr(y), _stream(stream)),
+           "ee_add_bias_residual_layernorm")
 
 
 # ---------------------------------------------------------------- layer
@@ -202,8 +249,10 @@ class Layer:
     """A layer handle: borrows the weight tensors (kept alive by this object)."""
 
     def __init__(self, hidden: int, n_heads: int, head_dim: int, ffn: int, weights: Dict, dtype: int = F16,
-                 ln_eps: float = 1e-5, gelu: int = GELU_TANH, fuse_gelu: bool = True):
-        self.desc = LayerDesc(hidden, n_heads, head_dim, ffn, ln_eps, dtype, gelu, 1 if fuse_gelu else 0)
+                 ln_eps: float = 1e-5, gelu: int = GELU_TANH, fuse_gelu: bool = True, block: int = BLOCK_GPT_PRELN,
+                 attention: int = ATTN_VARLEN):
+        self.desc = LayerDesc(hidden, n_heads, head_dim, ffn, ln_eps, dtype, gelu, 1 if fuse_gelu else 0, block,
+                              attention)
         self._weights = {k: weights[k] for k in WEIGHT_FIELDS}
         w = LayerWeights(*[_ptr(self._weights[k]) for k in WEIGHT_FIELDS])
         h = C.c_void_p()

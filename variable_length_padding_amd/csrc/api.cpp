@@ -136,6 +136,10 @@ ee_status check_desc(const ee_layer_desc* d) {
   if (!dtype_ok(d->dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
   if (d->gelu != EE_GELU_TANH && d->gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)d->gelu);
   if (d->fuse_gelu != 0 && d->fuse_gelu != 1) return fail(EE_ERR_INVALID_ARG, "fuse_gelu must be 0 or 1");
+  if (d->block != EE_BLOCK_GPT_PRELN && d->block != EE_BLOCK_BERT_POSTLN)
+    return fail(EE_ERR_INVALID_ARG, "unknown block %d", (int)d->block);
+  if (d->attention != EE_ATTN_VARLEN && d->attention != EE_ATTN_PADDED)
+    return fail(EE_ERR_INVALID_ARG, "unknown attention form %d", (int)d->attention);
   if (d->hidden < 1 || d->n_heads < 1 || d->ffn < 1)
     return fail(EE_ERR_INVALID_ARG, "hidden, n_heads and ffn must be >= 1");
   if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps)) return fail(EE_ERR_INVALID_ARG, "ln_eps must be finite and > 0");
@@ -156,12 +160,13 @@ ee_status check_desc(const ee_layer_desc* d) {
 
 bool desc_equal(const ee_layer_desc& a, const ee_layer_desc& b) {
   return a.hidden == b.hidden && a.n_heads == b.n_heads && a.head_dim == b.head_dim && a.ffn == b.ffn &&
-         a.ln_eps == b.ln_eps && a.dtype == b.dtype && a.gelu == b.gelu && a.fuse_gelu == b.fuse_gelu;
+         a.ln_eps == b.ln_eps && a.dtype == b.dtype && a.gelu == b.gelu && a.fuse_gelu == b.fuse_gelu &&
+         a.block == b.block && a.attention == b.attention;
 }
 
 // ---------------------------------------------------------------- workspace
 struct Plan {
-  size_t cu, token_src, pad2pack, x, ln, big, o, h, total;
+  size_t cu, token_src, pad2pack, x, ln, big, o, h, heads, o_heads, total;
 };
 
 Plan plan_offsets_only(int32_t B, int32_t P) {
@@ -194,6 +199,11 @@ Plan plan_layer(const ee_layer_desc& d, int32_t B, int32_t P, int64_t T) {
   p.big = take(t * std::max(3 * Hp, F) * s);
   p.o = take(t * Hp * s);
   p.h = take(t * H * s);
+  if (d.attention == EE_ATTN_PADDED) {  // head-major padded q|k|v and output
+    const size_t pad_rows = (size_t)B * P;
+    p.heads = take(3 * pad_rows * Hp * s);
+    p.o_heads = take(pad_rows * Hp * s);
+  }
   p.total = off;
   return p;
 }
@@ -216,8 +226,26 @@ ee_status offsets_from_host(const int32_t* lens, int32_t B, int32_t P, int32_t* 
   return EE_OK;
 }
 
+// Attention of the layer on packed qkv -> o, in the descriptor's form.
+ee_status attend(const ee_layer_desc& d, void* ws, const Plan& p, const void* qkv, void* o, int32_t B, int32_t P,
+                 int32_t max_len, bool causal, hipStream_t s) {
+  const int32_t* cu = reinterpret_cast<const int32_t*>(at(ws, p.cu));
+  if (d.attention == EE_ATTN_VARLEN) {
+    EE_LAUNCH("attention", s, launch_attention(d.dtype, qkv, cu, B, max_len, d.n_heads, d.head_dim, causal, o, s));
+    return EE_OK;
+  }
+  const int head_bytes = d.head_dim * (int)dtype_size(d.dtype);
+  char* heads = at(ws, p.heads);
+  const size_t mat = (size_t)B * P * d.n_heads * d.head_dim * dtype_size(d.dtype);
+  EE_LAUNCH("rebuild_heads", s, launch_rebuild_heads(qkv, cu, B, d.n_heads, P, head_bytes, 3, heads, s));
+  EE_LAUNCH("attention", s, launch_attention_padded(d.dtype, heads, heads + mat, heads + 2 * mat, cu, B, P, d.n_heads,
+                                                    d.head_dim, causal, at(ws, p.o_heads), s));
+  EE_LAUNCH("remove_heads", s, launch_remove_heads(at(ws, p.o_heads), cu, B, d.n_heads, P, head_bytes, o, s));
+  return EE_OK;
+}
+
 // The packed layer on T rows held in ws.x; the output replaces ws.x.
-ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, int32_t B, int32_t max_len,
+ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, int32_t B, int32_t P, int32_t max_len,
                        hipStream_t s) {
   const ee_layer_desc& d = L->desc;
   const ee_layer_weights& w = L->w;
@@ -227,19 +255,35 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, in
   void* big = at(ws, p.big);
   void* o = at(ws, p.o);
   void* h = at(ws, p.h);
-  const int32_t* cu = reinterpret_cast<const int32_t*>(at(ws, p.cu));
-  EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
-  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
-  EE_LAUNCH("attention", s, launch_attention(d.dtype, big, cu, B, max_len, d.n_heads, d.head_dim, o, s));
-  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s));
-  EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
-  if (d.fuse_gelu) {
-    EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, ln, w.w_fc1, w.b_fc1, nullptr, T, F, H, EE_EPI_BIAS_GELU, d.gelu, big, s));
-  } else {
-    EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, ln, w.w_fc1, nullptr, nullptr, T, F, H, EE_EPI_NONE, d.gelu, big, s));
-    EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, d.gelu, big, s));
+  auto fc1 = [&](const void* in) -> ee_status {
+    if (d.fuse_gelu) {
+      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, EE_EPI_BIAS_GELU, d.gelu, big, s));
+    } else {
+      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, EE_EPI_NONE, d.gelu, big, s));
+      EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, d.gelu, big, s));
+    }
+    return EE_OK;
+  };
+  if (d.block == EE_BLOCK_GPT_PRELN) {
+    EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
+    EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
+    EE_TRY(attend(d, ws, p, big, o, B, P, max_len, true, s));
+    EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s));
+    EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
+    EE_TRY(fc1(ln));
+    EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s));
+    return EE_OK;
   }
-  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s));
+  // post-LN encoder: GEMM, then bias + residual + LayerNorm in one pass
+  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
+  EE_TRY(attend(d, ws, p, big, o, B, P, max_len, false, s));
+  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, EE_EPI_NONE, d.gelu, ln, s));
+  EE_LAUNCH("add_ln1", s,
+            launch_add_bias_residual_layernorm(d.dtype, ln, w.b_out, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, h, s));
+  EE_TRY(fc1(h));
+  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, EE_EPI_NONE, d.gelu, ln, s));
+  EE_LAUNCH("add_ln2", s,
+            launch_add_bias_residual_layernorm(d.dtype, ln, w.b_fc2, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, x, s));
   return EE_OK;
 }
 
@@ -274,7 +318,7 @@ ee_status stack_impl(ee_layer* const* layers, int32_t n_layers, const void* x_pa
   EE_TRY(offsets_from_host(seq_lens, B, P, cu, tsrc, p2p, s));
   if (T > 0) {
     EE_LAUNCH("remove", s, launch_remove(x_padded, tsrc, T, row_bytes, at(ws, p.x), s));
-    for (int32_t i = 0; i < n_layers; ++i) EE_TRY(packed_layer(layers[i], ws, p, T, B, max_len, s));
+    for (int32_t i = 0; i < n_layers; ++i) EE_TRY(packed_layer(layers[i], ws, p, T, B, P, max_len, s));
   }
   EE_LAUNCH("rebuild", s, launch_rebuild(at(ws, p.x), p2p, (int64_t)B * P, row_bytes, y_padded, s));
   return EE_OK;
@@ -503,7 +547,8 @@ ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t co
 }
 
 ee_status ee_attention_varlen(const void* qkv, const int32_t* d_cu, int32_t batch, int32_t max_len, int32_t n_heads,
-                              int32_t head_dim, int64_t total_tokens, ee_dtype dtype, void* o, void* stream) {
+                              int32_t head_dim, int64_t total_tokens, int32_t causal, ee_dtype dtype, void* o,
+                              void* stream) {
   if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
     return fail(EE_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", head_dim);
@@ -517,7 +562,101 @@ ee_status ee_attention_varlen(const void* qkv, const int32_t* d_cu, int32_t batc
   if (overlap(qkv, (size_t)total_tokens * 3 * Hp * s, o, (size_t)total_tokens * Hp * s))
     return fail(EE_ERR_INVALID_ARG, "qkv and o overlap");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  EE_LAUNCH("attention", st, launch_attention(dtype, qkv, d_cu, batch, max_len, n_heads, head_dim, o, st));
+  EE_LAUNCH("attention", st, launch_attention(dtype, qkv, d_cu, batch, max_len, n_heads, head_dim, causal != 0, o, st));
+  return EE_OK;
+}
+
+ee_status ee_attention_padded(const void* q, const void* k, const void* v, const int32_t* d_cu, int32_t batch,
+                              int32_t pad_len, int32_t n_heads, int32_t head_dim, int32_t causal, ee_dtype dtype,
+                              void* o, void* stream) {
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
+    return fail(EE_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", head_dim);
+  if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 65535 || pad_len < 1)
+    return fail(EE_ERR_INVALID_ARG, "bad batch/n_heads/pad_len");
+  if (!d_cu) return fail(EE_ERR_INVALID_ARG, "d_cu is NULL");
+  EE_TRY(check_ptr(q, "q"));
+  EE_TRY(check_ptr(k, "k"));
+  EE_TRY(check_ptr(v, "v"));
+  EE_TRY(check_ptr(o, "o"));
+  const size_t n = (size_t)batch * n_heads * pad_len * head_dim * dtype_size(dtype);
+  if (overlap(o, n, q, n) || overlap(o, n, k, n) || overlap(o, n, v, n))
+    return fail(EE_ERR_INVALID_ARG, "o overlaps q, k or v");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("attention", st,
+            launch_attention_padded(dtype, q, k, v, d_cu, batch, pad_len, n_heads, head_dim, causal != 0, o, st));
+  return EE_OK;
+}
+
+ee_status ee_transpose_padding_rebuild_heads(const void* d_packed, const int32_t* seq_lens, int32_t batch,
+                                             int32_t pad_len, int32_t n_mats, int32_t n_heads, int32_t head_dim,
+                                             ee_dtype dtype, void* d_heads, void* workspace, size_t ws_bytes,
+                                             void* stream) {
+  if (n_mats < 1 || n_heads < 1 || head_dim < 1) return fail(EE_ERR_INVALID_ARG, "n_mats, n_heads, head_dim >= 1");
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if ((size_t)head_dim * dtype_size(dtype) % 16) return fail(EE_ERR_UNSUPPORTED, "head_dim*sizeof(dtype) % 16 != 0");
+  int64_t T = 0;
+  Plan p{};
+  const int32_t width = n_mats * n_heads * head_dim;
+  EE_TRY(padding_common(d_packed, seq_lens, batch, pad_len, width, dtype, d_heads, workspace, ws_bytes, &T, &p));
+  const size_t es = dtype_size(dtype);
+  if (overlap(d_packed, (size_t)T * width * es, d_heads, (size_t)batch * pad_len * width * es) ||
+      overlap(workspace, p.total, d_heads, (size_t)batch * pad_len * width * es) ||
+      overlap(workspace, p.total, d_packed, (size_t)T * width * es))
+    return fail(EE_ERR_INVALID_ARG, "buffers overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* cu = reinterpret_cast<int32_t*>(at(workspace, p.cu));
+  EE_TRY(offsets_from_host(seq_lens, batch, pad_len, cu, reinterpret_cast<int32_t*>(at(workspace, p.token_src)),
+                           reinterpret_cast<int32_t*>(at(workspace, p.pad2pack)), s));
+  EE_LAUNCH("rebuild_heads", s,
+            launch_rebuild_heads(d_packed, cu, batch, n_heads, pad_len, head_dim * (int)es, n_mats, d_heads, s));
+  return EE_OK;
+}
+
+ee_status ee_transpose_padding_remove_heads(const void* d_heads, const int32_t* seq_lens, int32_t batch,
+                                            int32_t pad_len, int32_t n_heads, int32_t head_dim, ee_dtype dtype,
+                                            void* d_packed, void* workspace, size_t ws_bytes, void* stream) {
+  if (n_heads < 1 || head_dim < 1) return fail(EE_ERR_INVALID_ARG, "n_heads, head_dim >= 1");
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if ((size_t)head_dim * dtype_size(dtype) % 16) return fail(EE_ERR_UNSUPPORTED, "head_dim*sizeof(dtype) % 16 != 0");
+  int64_t T = 0;
+  Plan p{};
+  const int32_t width = n_heads * head_dim;
+  EE_TRY(padding_common(d_heads, seq_lens, batch, pad_len, width, dtype, d_packed, workspace, ws_bytes, &T, &p));
+  const size_t es = dtype_size(dtype);
+  if (overlap(d_packed, (size_t)T * width * es, d_heads, (size_t)batch * pad_len * width * es) ||
+      overlap(workspace, p.total, d_heads, (size_t)batch * pad_len * width * es) ||
+      overlap(workspace, p.total, d_packed, (size_t)T * width * es))
+    return fail(EE_ERR_INVALID_ARG, "buffers overlap");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* cu = reinterpret_cast<int32_t*>(at(workspace, p.cu));
+  EE_TRY(offsets_from_host(seq_lens, batch, pad_len, cu, reinterpret_cast<int32_t*>(at(workspace, p.token_src)),
+                           reinterpret_cast<int32_t*>(at(workspace, p.pad2pack)), s));
+  EE_LAUNCH("remove_heads", s, launch_remove_heads(d_heads, cu, batch, n_heads, pad_len, head_dim * (int)es, d_packed, s));
+  return EE_OK;
+}
+
+ee_status ee_add_bias_residual_layernorm(const void* u, const void* bias, const void* residual, const void* gamma,
+                                         const void* beta, int64_t rows, int32_t hidden, float eps, ee_dtype dtype,
+                                         void* y, void* stream) {
+  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (rows < 0) return fail(EE_ERR_INVALID_ARG, "rows < 0");
+  if (hidden < 1 || (size_t)hidden * dtype_size(dtype) % 16)
+    return fail(EE_ERR_UNSUPPORTED, "hidden*sizeof(dtype) must be a positive multiple of 16 bytes");
+  if (hidden > layernorm_max_hidden(dtype)) return fail(EE_ERR_UNSUPPORTED, "hidden %d too large", hidden);
+  if (!(eps > 0.f) || !std::isfinite(eps)) return fail(EE_ERR_INVALID_ARG, "eps must be finite and > 0");
+  EE_TRY(check_ptr(bias, "bias"));
+  EE_TRY(check_ptr(gamma, "gamma"));
+  EE_TRY(check_ptr(beta, "beta"));
+  if (rows == 0) return EE_OK;
+  EE_TRY(check_ptr(u, "u"));
+  EE_TRY(check_ptr(residual, "residual"));
+  EE_TRY(check_ptr(y, "y"));
+  const size_t n = (size_t)rows * hidden * dtype_size(dtype);
+  if (overlap(y, n, u, n) || overlap(y, n, residual, n)) return fail(EE_ERR_INVALID_ARG, "y overlaps an input");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("add_bias_residual_ln", s,
+            launch_add_bias_residual_layernorm(dtype, u, bias, residual, gamma, beta, rows, hidden, eps, y, s));
   return EE_OK;
 }
 

@@ -1,6 +1,9 @@
-// Causal self-attention run per sequence over the packed token offsets: query i
-// of sequence b attends to keys cu[b] .. cu[b]+i with weights
-// softmax(q.k / sqrt(head_dim)).  Packing means no query or key of padding
+// Self-attention run per sequence: query i of sequence b attends, with weights
+// softmax(q.k / sqrt(head_dim)), to keys 0..i of its sequence (causal, the GPT
+// decoder) or to all of its sequence's keys (bidirectional, the BERT-style
+// encoder).  Rows are read either from the packed q|k|v buffer over the token
+// offsets cu, or from padded head-major [B, nh, P, hd] tensors (the
+// page-literal form, with lengths still from cu).  Packing means no query or key of padding
 // exists at all; sequences never see each other.  (The pages give no
 // attention kernel; the packed layout follows from removing the padding for
 // the whole layer, the announcement article's "Runtime" section.)
@@ -29,6 +32,22 @@ constexpr int kQB = 128;  // queries per workgroup (MFMA kernel)
 constexpr int kKB = 32;   // keys per LDS tile
 constexpr int kVtPitch = kKB + 4;  // halves per transposed-V row: 72 B, 8-byte aligned, conflict-free b64 reads
 
+// Where the rows of q, k, v and o live.  Row `row` of (sequence b, head h) of
+// tensor X sits at X + (seq ? cu[b] : 0) * row_stride + b * batch_stride
+// + h * head_stride + row * row_stride (elements).  Packed q|k|v rows:
+// seq = 1, batch_stride = 0, head_stride = hd, row_stride = 3H' (o: H').
+// Padded head-major [B, nh, P, hd]: seq = 0, batch_stride = nh*P*hd,
+// head_stride = P*hd, row_stride = hd.  Lengths always come from cu.
+struct AttnAddr {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t in_batch_stride, in_head_stride, in_row_stride;
+  int64_t out_batch_stride, out_head_stride, out_row_stride;
+  int seq;
+};
+
 template <int HD>
 __device__ __forceinline__ int k_swizzle(int r) {
   constexpr int KCH = HD / 8;  // 16-byte chunks per key row
@@ -37,9 +56,9 @@ __device__ __forceinline__ int k_swizzle(int r) {
   return r & (KCH - 1);
 }
 
-template <int HD>
-__global__ __launch_bounds__(256) void attn_mfma_kernel(const f16* __restrict__ qkv, const int32_t* __restrict__ cu,
-                                                        int nh, float scale_log2, f16* __restrict__ o) {
+template <int HD, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_mfma_kernel(AttnAddr ad, const int32_t* __restrict__ cu,
+                                                        float scale_log2) {
   constexpr int KCH = HD / 8;
   constexpr int NKK = HD / 16;  // MFMA K steps for S
   constexpr int NDB = HD / 32;  // 32-row blocks of O^T
@@ -51,7 +70,11 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const f16* __restrict__ 
   const int L = cu[b + 1] - s0;
   const int q_start = blockIdx.x * kQB;
   if (q_start >= L) return;  // uniform over the workgroup
-  const int Hp = nh * HD, ld = 3 * Hp;
+  const int64_t in_base = (ad.seq ? (int64_t)s0 * ad.in_row_stride : 0) + b * ad.in_batch_stride + head * ad.in_head_stride;
+  const int64_t ld = ad.in_row_stride;
+  const f16* qb = static_cast<const f16*>(ad.q) + in_base;
+  const f16* kb = static_cast<const f16*>(ad.k) + in_base;
+  const f16* vb = static_cast<const f16*>(ad.v) + in_base;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6, hk = lane >> 5;
   const int q0 = q_start + wave * 32;
   const int qi = q0 + (lane & 31);
@@ -59,7 +82,7 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const f16* __restrict__ 
 
   half8 qf[NKK];
   {
-    const f16* qrow = qkv + (int64_t)(s0 + qc) * ld + head * HD + hk * 8;
+    const f16* qrow = qb + qc * ld + hk * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const half8*>(qrow + kk * 16);
   }
@@ -70,23 +93,24 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const f16* __restrict__ 
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kend = min(L, q_start + kQB);
-  const int wave_last_q = min(q0 + 31, L - 1);
+  // keys this workgroup needs: up to its last query (causal) or all of them
+  const int kend = CAUSAL ? min(L, q_start + kQB) : L;
+  const int wave_last_key = CAUSAL ? min(q0 + 31, L - 1) : L - 1;
+  const bool wave_active = q0 < L;
   const int kswz = k_swizzle<HD>(lane & 31);
 
   for (int k0 = 0; k0 < kend; k0 += kKB) {
     for (int c = t; c < kKB * KCH; c += 256) {
       const int r = c / KCH, ch = c % KCH;
-      const int key = min(k0 + r, L - 1);
-      const f16* base = qkv + (int64_t)(s0 + key) * ld + head * HD + ch * 8;
-      const half8 kv = *reinterpret_cast<const half8*>(base + Hp);
-      const half8 vv = *reinterpret_cast<const half8*>(base + 2 * Hp);
+      const int64_t key_off = (int64_t)min(k0 + r, L - 1) * ld + ch * 8;
+      const half8 kv = *reinterpret_cast<const half8*>(kb + key_off);
+      const half8 vv = *reinterpret_cast<const half8*>(vb + key_off);
       *reinterpret_cast<half8*>(sK + r * HD + ((ch ^ k_swizzle<HD>(r)) * 8)) = kv;
 #pragma unroll
       for (int i = 0; i < 8; ++i) sVt[(ch * 8 + i) * kVtPitch + r] = vv[i];
     }
     __syncthreads();
-    if (k0 <= wave_last_q) {
+    if (wave_active && k0 <= wave_last_key) {
       floatx16 s;
 #pragma unroll
       for (int e = 0; e < 16; ++e) s[e] = 0.f;
@@ -101,7 +125,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const f16* __restrict__ 
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + (e >> 2) * 8 + hk * 4 + (e & 3);
-        const float v = key <= qi ? s[e] * scale_log2 : -INFINITY;
+        const bool keep = CAUSAL ? key <= qi : key < L;
+        const float v = keep ? s[e] * scale_log2 : -INFINITY;
         s[e] = v;
         mloc = fmaxf(mloc, v);
       }
@@ -128,17 +153,18 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const f16* __restrict__ 
         const half4 a1 = *reinterpret_cast<const half4*>(vrow + 8);
         const half4 a2 = *reinterpret_cast<const half4*>(vrow + 16);
         const half4 a3 = *reinterpret_cast<const half4*>(vrow + 24);
-        const half8 va = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-        const half8 vb = {a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, p0, oacc[d], 0, 0, 0);
-        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vb, p1, oacc[d], 0, 0, 0);
+        const half8 v_lo = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+        const half8 v_hi = {a2[0], a2[1], a2[2], a2[3], a3[0], a3[1], a3[2], a3[3]};
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_lo, p0, oacc[d], 0, 0, 0);
+        oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(v_hi, p1, oacc[d], 0, 0, 0);
       }
     }
     __syncthreads();
   }
   if (qi < L) {
     const float inv = 1.0f / l_run;
-    f16* orow = o + (int64_t)(s0 + qi) * Hp + head * HD + hk * 4;
+    f16* orow = static_cast<f16*>(ad.o) + (ad.seq ? (int64_t)s0 * ad.out_row_stride : 0) + b * ad.out_batch_stride +
+                head * ad.out_head_stride + (int64_t)qi * ad.out_row_stride + hk * 4;
 #pragma unroll
     for (int d = 0; d < NDB; ++d)
 #pragma unroll
@@ -154,9 +180,8 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(const f16* __restrict__ 
 // ---- vector-ALU fallback: one query per lane, 64 queries per workgroup ----
 constexpr int kVQ = 64;
 
-template <typename T, int HD>
-__global__ __launch_bounds__(kVQ) void attn_valu_kernel(const T* __restrict__ qkv, const int32_t* __restrict__ cu,
-                                                        int nh, float scale, T* __restrict__ o) {
+template <typename T, int HD, bool CAUSAL>
+__global__ __launch_bounds__(kVQ) void attn_valu_kernel(AttnAddr ad, const int32_t* __restrict__ cu, float scale) {
   __shared__ float sK[kVQ][HD + 1];
   __shared__ float sV[kVQ][HD + 1];
   const int b = blockIdx.y, head = blockIdx.z;
@@ -164,26 +189,30 @@ __global__ __launch_bounds__(kVQ) void attn_valu_kernel(const T* __restrict__ qk
   const int L = cu[b + 1] - s0;
   const int q_start = blockIdx.x * kVQ;
   if (q_start >= L) return;
-  const int Hp = nh * HD, ld = 3 * Hp;
+  const int64_t in_base = (ad.seq ? (int64_t)s0 * ad.in_row_stride : 0) + b * ad.in_batch_stride + head * ad.in_head_stride;
+  const int64_t ld = ad.in_row_stride;
+  const T* qb = static_cast<const T*>(ad.q) + in_base;
+  const T* kb = static_cast<const T*>(ad.k) + in_base;
+  const T* vb = static_cast<const T*>(ad.v) + in_base;
   const int qi = q_start + (int)threadIdx.x;
   float q[HD], acc[HD];
-  const T* qrow = qkv + (int64_t)(s0 + min(qi, L - 1)) * ld + head * HD;
+  const T* qrow = qb + min(qi, L - 1) * ld;
 #pragma unroll
   for (int d = 0; d < HD; ++d) {
     q[d] = to_f32(qrow[d]);
     acc[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int kend = min(L, q_start + kVQ);
+  const int kend = CAUSAL ? min(L, q_start + kVQ) : L;
   for (int k0 = 0; k0 < kend; k0 += kVQ) {
     for (int idx = threadIdx.x; idx < kVQ * HD; idx += kVQ) {
       const int r = idx / HD, d = idx % HD;
-      const T* base = qkv + (int64_t)(s0 + min(k0 + r, L - 1)) * ld + head * HD + d;
-      sK[r][d] = to_f32(base[Hp]);
-      sV[r][d] = to_f32(base[2 * Hp]);
+      const int64_t off = (int64_t)min(k0 + r, L - 1) * ld + d;
+      sK[r][d] = to_f32(kb[off]);
+      sV[r][d] = to_f32(vb[off]);
     }
     __syncthreads();
-    const int jn = min(kVQ, qi - k0 + 1);
+    const int jn = CAUSAL ? min(kVQ, qi - k0 + 1) : min(kVQ, L - k0);
     for (int j = 0; j < jn; ++j) {
       float s = 0.f;
 #pragma unroll
@@ -200,25 +229,49 @@ __global__ __launch_bounds__(kVQ) void attn_valu_kernel(const T* __restrict__ qk
     __syncthreads();
   }
   if (qi < L) {
-    T* orow = o + (int64_t)(s0 + qi) * Hp + head * HD;
+    T* orow = static_cast<T*>(ad.o) + (ad.seq ? (int64_t)s0 * ad.out_row_stride : 0) + b * ad.out_batch_stride +
+              head * ad.out_head_stride + (int64_t)qi * ad.out_row_stride;
     const float inv = 1.0f / l;
 #pragma unroll
     for (int d = 0; d < HD; ++d) orow[d] = from_f32<T>(acc[d] * inv);
   }
 }
 
-template <typename T>
-hipError_t launch_valu(const void* qkv, const int32_t* cu, int B, int max_len, int nh, int hd, void* o,
-                       hipStream_t s) {
+template <typename T, bool CAUSAL>
+void launch_valu(const AttnAddr& ad, const int32_t* cu, int B, int max_len, int nh, int hd, hipStream_t s) {
   const dim3 grid((unsigned)((max_len + kVQ - 1) / kVQ), (unsigned)B, (unsigned)nh), block(kVQ);
   const float scale = 1.0f / sqrtf((float)hd);
-  const T* q = static_cast<const T*>(qkv);
-  T* out = static_cast<T*>(o);
   switch (hd) {
-    case 16: hipLaunchKernelGGL((attn_valu_kernel<T, 16>), grid, block, 0, s, q, cu, nh, scale, out); break;
-    case 32: hipLaunchKernelGGL((attn_valu_kernel<T, 32>), grid, block, 0, s, q, cu, nh, scale, out); break;
-    case 64: hipLaunchKernelGGL((attn_valu_kernel<T, 64>), grid, block, 0, s, q, cu, nh, scale, out); break;
-    default: hipLaunchKernelGGL((attn_valu_kernel<T, 128>), grid, block, 0, s, q, cu, nh, scale, out); break;
+    case 16: hipLaunchKernelGGL((attn_valu_kernel<T, 16, CAUSAL>), grid, block, 0, s, ad, cu, scale); break;
+    case 32: hipLaunchKernelGGL((attn_valu_kernel<T, 32, CAUSAL>), grid, block, 0, s, ad, cu, scale); break;
+    case 64: hipLaunchKernelGGL((attn_valu_kernel<T, 64, CAUSAL>), grid, block, 0, s, ad, cu, scale); break;
+    default: hipLaunchKernelGGL((attn_valu_kernel<T, 128, CAUSAL>), grid, block, 0, s, ad, cu, scale); break;
+  }
+}
+
+template <bool CAUSAL>
+void launch_mfma(const AttnAddr& ad, const int32_t* cu, int B, int max_len, int nh, int hd, hipStream_t s) {
+  const dim3 grid((unsigned)((max_len + kQB - 1) / kQB), (unsigned)B, (unsigned)nh), block(256);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);  // log2(e) / sqrt(hd)
+  switch (hd) {
+    case 32: hipLaunchKernelGGL((attn_mfma_kernel<32, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2); break;
+    case 64: hipLaunchKernelGGL((attn_mfma_kernel<64, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2); break;
+    default: hipLaunchKernelGGL((attn_mfma_kernel<128, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2); break;
+  }
+}
+
+hipError_t launch_attn(ee_dtype dt, const AttnAddr& ad, const int32_t* cu, int B, int max_len, int nh, int hd,
+                       bool causal, hipStream_t s) {
+  if (B <= 0 || max_len <= 0) return hipSuccess;
+  if (dt == EE_F16 && (hd == 32 || hd == 64 || hd == 128)) {
+    if (causal) launch_mfma<true>(ad, cu, B, max_len, nh, hd, s);
+    else launch_mfma<false>(ad, cu, B, max_len, nh, hd, s);
+  } else if (dt == EE_F16) {
+    if (causal) launch_valu<f16, true>(ad, cu, B, max_len, nh, hd, s);
+    else launch_valu<f16, false>(ad, cu, B, max_len, nh, hd, s);
+  } else {
+    if (causal) launch_valu<float, true>(ad, cu, B, max_len, nh, hd, s);
+    else launch_valu<float, false>(ad, cu, B, max_len, nh, hd, s);
   }
   return hipGetLastError();
 }
@@ -228,22 +281,18 @@ hipError_t launch_valu(const void* qkv, const int32_t* cu, int B, int max_len, i
 bool attention_mfma_ok(ee_dtype dt, int hd) { return dt == EE_F16 && (hd == 32 || hd == 64 || hd == 128); }
 
 hipError_t launch_attention(ee_dtype dt, const void* qkv, const int32_t* cu, int B, int max_len, int nh, int hd,
-                            void* o, hipStream_t s) {
-  if (B <= 0 || max_len <= 0) return hipSuccess;
-  if (attention_mfma_ok(dt, hd)) {
-    const dim3 grid((unsigned)((max_len + kQB - 1) / kQB), (unsigned)B, (unsigned)nh), block(256);
-    const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);  // log2(e) / sqrt(hd)
-    const f16* q = static_cast<const f16*>(qkv);
-    f16* out = static_cast<f16*>(o);
-    switch (hd) {
-      case 32: hipLaunchKernelGGL((attn_mfma_kernel<32>), grid, block, 0, s, q, cu, nh, scale_log2, out); break;
-      case 64: hipLaunchKernelGGL((attn_mfma_kernel<64>), grid, block, 0, s, q, cu, nh, scale_log2, out); break;
-      default: hipLaunchKernelGGL((attn_mfma_kernel<128>), grid, block, 0, s, q, cu, nh, scale_log2, out); break;
-    }
-    return hipGetLastError();
-  }
-  return dt == EE_F16 ? launch_valu<f16>(qkv, cu, B, max_len, nh, hd, o, s)
-                      : launch_valu<float>(qkv, cu, B, max_len, nh, hd, o, s);
+                            bool causal, void* o, hipStream_t s) {
+  const int64_t Hp = (int64_t)nh * hd, es = dt == EE_F16 ? 2 : 4;
+  const char* base = static_cast<const char*>(qkv);
+  const AttnAddr ad{base, base + Hp * es, base + 2 * Hp * es, o, 0, hd, 3 * Hp, 0, hd, Hp, 1};
+  return launch_attn(dt, ad, cu, B, max_len, nh, hd, causal, s);
+}
+
+hipError_t launch_attention_padded(ee_dtype dt, const void* q, const void* k, const void* v, const int32_t* cu,
+                                   int B, int P, int nh, int hd, bool causal, void* o, hipStream_t s) {
+  const int64_t hs = (int64_t)P * hd, bs = (int64_t)nh * hs;
+  const AttnAddr ad{q, k, v, o, bs, hs, hd, bs, hs, hd, 0};
+  return launch_attn(dt, ad, cu, B, P, nh, hd, causal, s);
 }
 
 }  // namespace ee

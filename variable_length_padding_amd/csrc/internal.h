@@ -27,11 +27,20 @@ hipError_t launch_remove(const void* padded, const int32_t* token_src, int64_t T
                          void* packed, hipStream_t s);
 hipError_t launch_rebuild(const void* packed, const int32_t* pad2pack, int64_t rows, int64_t row_bytes,
                           void* padded, hipStream_t s);
+// transposing forms: packed [T, n*nh*hd] <-> head-major padded [n, B, nh, P, hd]
+// (head_bytes = hd * element size, a multiple of 16)
+hipError_t launch_rebuild_heads(const void* packed, const int32_t* cu, int B, int nh, int P, int head_bytes,
+                                int n_mats, void* out, hipStream_t s);
+hipError_t launch_remove_heads(const void* heads, const int32_t* cu, int B, int nh, int P, int head_bytes,
+                               void* packed, hipStream_t s);
 
 // ---- layernorm.hip ----
 int layernorm_max_hidden(ee_dtype dt);
 hipError_t launch_layernorm(ee_dtype dt, const void* x, const void* g, const void* b, int64_t rows, int H,
                             float eps, void* y, hipStream_t s);
+hipError_t launch_add_bias_residual_layernorm(ee_dtype dt, const void* u, const void* bias, const void* res,
+                                              const void* g, const void* b, int64_t rows, int H, float eps, void* y,
+                                              hipStream_t s);
 
 // ---- bias_gelu.hip ----
 hipError_t launch_bias_gelu(ee_dtype dt, const void* u, const void* bias, int64_t rows, int cols,
@@ -47,6 +56,8 @@ hipError_t launch_gemm_valu(ee_dtype dt, const void* A, const void* W, const voi
 // ---- attention.hip ----
 bool attention_mfma_ok(ee_dtype dt, int head_dim);
 hipError_t launch_attention(ee_dtype dt, const void* qkv, const int32_t* cu, int B, int max_len, int nh,
-                            int hd, void* o, hipStream_t s);
+                            int hd, bool causal, void* o, hipStream_t s);
+hipError_t launch_attention_padded(ee_dtype dt, const void* q, const void* k, const void* v, const int32_t* cu,
+                                   int B, int P, int nh, int hd, bool causal, void* o, hipStream_t s);
 
 }  // namespace ee

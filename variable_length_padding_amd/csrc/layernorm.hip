@@ -162,6 +162,86 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_wave_kernel(const T* __r
   }
 }
 
+// Post-LN residual step (the add bias + input + LayerNorm launcher of the
+// announcement article's "Ease of use" listing): y = LN(u + bias + residual),
+// the sum formed in fp32 and never stored.  One workgroup per row.
+template <typename T, int VPT>
+__global__ __launch_bounds__(kLnThreads) void add_bias_residual_ln_kernel(
+    const T* __restrict__ u, const T* __restrict__ bias, const T* __restrict__ res, const T* __restrict__ gamma,
+    const T* __restrict__ beta, int64_t rows, int H, float eps, T* __restrict__ y) {
+  typedef typename Vec16<T>::type V;
+  constexpr int E = Vec16<T>::n;
+  __shared__ float s_red[kLnThreads / kWave];
+  const int nvec = H / E;
+  const float inv_h = 1.0f / (float)H;
+  const V* bv = reinterpret_cast<const V*>(bias);
+  for (int64_t row = blockIdx.x; row < rows; row += gridDim.x) {
+    const V* ur = reinterpret_cast<const V*>(u + row * H);
+    const V* rr = reinterpret_cast<const V*>(res + row * H);
+    float v[VPT][E];
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * kLnThreads;
+      if (c < nvec) {
+        const V a = ur[c], r = rr[c], bb = bv[c];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          v[i][e] = to_f32(a[e]) + to_f32(bb[e]) + to_f32(r[e]);
+          s += v[i][e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[i][e] = 0.f;
+      }
+    }
+    const float mean = block_sum(s, s_red) * inv_h;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < VPT; ++i)
+      if (threadIdx.x + i * kLnThreads < nvec)
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = v[i][e] - mean;
+          q += d * d;
+        }
+    const float rstd = 1.0f / sqrtf(block_sum(q, s_red) * inv_h + eps);
+    V* yr = reinterpret_cast<V*>(y + row * H);
+    const V* gv = reinterpret_cast<const V*>(gamma);
+    const V* btv = reinterpret_cast<const V*>(beta);
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * kLnThreads;
+      if (c < nvec) {
+        const V g = gv[c], bt = btv[c];
+        V o;
+#pragma unroll
+        for (int e = 0; e < E; ++e) o[e] = from_f32<T>((v[i][e] - mean) * rstd * to_f32(g[e]) + to_f32(bt[e]));
+        yr[c] = o;
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_abrln_t(const void* u, const void* bias, const void* res, const void* g, const void* b,
+                          int64_t rows, int H, float eps, void* y, hipStream_t s) {
+  const int nvec = H / Vec16<T>::n;
+  const unsigned grid = (unsigned)(rows > (1 << 20) ? (1 << 20) : rows);
+  const T *up = static_cast<const T*>(u), *bp = static_cast<const T*>(bias), *rp = static_cast<const T*>(res);
+  const T *gp = static_cast<const T*>(g), *btp = static_cast<const T*>(b);
+  T* yp = static_cast<T*>(y);
+  if (nvec <= 256)
+    hipLaunchKernelGGL((add_bias_residual_ln_kernel<T, 1>), dim3(grid), dim3(kLnThreads), 0, s, up, bp, rp, gp, btp, rows, H, eps, yp);
+  else if (nvec <= 1024)
+    hipLaunchKernelGGL((add_bias_residual_ln_kernel<T, 4>), dim3(grid), dim3(kLnThreads), 0, s, up, bp, rp, gp, btp, rows, H, eps, yp);
+  else if (nvec <= 2048)
+    hipLaunchKernelGGL((add_bias_residual_ln_kernel<T, 8>), dim3(grid), dim3(kLnThreads), 0, s, up, bp, rp, gp, btp, rows, H, eps, yp);
+  else
+    hipLaunchKernelGGL((add_bias_residual_ln_kernel<T, 16>), dim3(grid), dim3(kLnThreads), 0, s, up, bp, rp, gp, btp, rows, H, eps, yp);
+  return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_ln_t(const void* x, const void* g, const void* b, int64_t rows, int H, float eps, void* y,
                        hipStream_t s) {
@@ -207,6 +287,14 @@ hipError_t launch_layernorm(ee_dtype dt, const void* x, const void* g, const voi
                             void* y, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   return dt == EE_F16 ? launch_ln_t<f16>(x, g, b, rows, H, eps, y, s) : launch_ln_t<float>(x, g, b, rows, H, eps, y, s);
+}
+
+hipError_t launch_add_bias_residual_layernorm(ee_dtype dt, const void* u, const void* bias, const void* res,
+                                              const void* g, const void* b, int64_t rows, int H, float eps, void* y,
+                                              hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return dt == EE_F16 ? launch_abrln_t<f16>(u, bias, res, g, b, rows, H, eps, y, s)
+                      : launch_abrln_t<float>(u, bias, res, g, b, rows, H, eps, y, s);
 }
 
 }  // namespace ee
