@@ -46,6 +46,14 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-seqs", type=int, default=4)
     ap.add_argument("--no-fuse-gelu", action="store_true", help="unfused bias+GeLU (ablation)")
+    ap.add_argument("--attention", choices=("varlen", "padded"), default="varlen",
+                    help="padded: transposing rebuild -> fixed-shape masked attention -> transposing remove "
+                         "(the pages' form of padding removal, as an ablation)")
+    ap.add_argument("--block", choices=("gpt", "bert"), default="gpt",
+                    help="bert: post-LN encoder block (bidirectional attention, erf GeLU), as an ablation")
+    ap.add_argument("--no-pack", action="store_true",
+                    help="padding kept: every one of the B*P rows runs through the layers (the redundant "
+                         "computation the method removes); value still counts valid tokens only")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -56,7 +64,8 @@ def _log(msg):
 
 
 def _site_work(w, T, B, P, site):
-    """(algorithmic flops, algorithmic HBM bytes) of one launch at a site."""
+    """(algorithmic flops, algorithmic HBM bytes) of one launch at a site, for
+    T rows run through the layer."""
     s = w.elem_bytes
     H, Hp, F = w.hidden, w.inner, w.ffn
     gemm = {"gemm_qkv": (H, 3 * Hp), "gemm_out": (Hp, H), "gemm_fc1": (H, F), "gemm_fc2": (F, H)}
@@ -72,14 +81,23 @@ def _site_work(w, T, B, P, site):
         return 0.0, float((T + B * P) * H * s)
     if site == "attention":
         return 0.0, 4.0 * T * Hp * s
+    if site == "rebuild_heads":          # q|k|v valid rows read, [3, B, nh, P, hd] written (pads as zeros)
+        return 0.0, float(3 * (T + B * P) * Hp * s)
+    if site == "remove_heads":
+        return 0.0, 2.0 * T * Hp * s
+    if site in ("add_ln1", "add_ln2"):   # u and residual read, y written
+        return 0.0, 3.0 * T * H * s
     if site == "bias_gelu":
         return 0.0, 2.0 * T * F * s
     return 0.0, 0.0
 
 
-def _attention_flops(w, lens):
-    # QK^T and PV over the causal triangle: 2 * 2 * hd * nh * len(len+1)/2 per sequence
-    return sum(2.0 * w.inner * n * (n + 1) for n in lens)
+def _attention_flops(w, lens, causal=True):
+    # QK^T and PV: 2 * 2 * hd * nh flops per (query, key) pair; len(len+1)/2
+    # pairs per sequence under the causal mask, len^2 without it
+    if causal:
+        return sum(2.0 * w.inner * n * (n + 1) for n in lens)
+    return sum(4.0 * w.inner * n * n for n in lens)
 
 
 def _traffic():
@@ -154,22 +172,30 @@ def main():
     lens = workloads.lengths(w, args.seed)
     B, P, L = w.batch, w.pad_len, w.layers
     T = sum(lens)
-    _log(f"workload {w.name}: B={B} P={P} T={T} H={w.hidden} nh={w.n_heads} hd={w.head_dim} F={w.ffn} L={L}")
+    # rows actually run through the layers: the valid ones, or all B*P with --no-pack
+    run_lens = [P] * B if args.no_pack else lens
+    T_run = sum(run_lens)
+    _log(f"workload {w.name}: B={B} P={P} T={T} (rows run {T_run}) H={w.hidden} nh={w.n_heads} "
+         f"hd={w.head_dim} F={w.ffn} L={L} block={args.block} attention={args.attention}")
 
     x = workloads.activations(w, args.seed, B, P, lens, device=dev)
     params = [workloads.layer_params(w, args.seed, l, device=dev) for l in range(L)]
     torch.cuda.synchronize()
     dt = ee.F16 if w.dtype == "f16" else ee.F32
-    layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=dt, fuse_gelu=not args.no_fuse_gelu)
+    bert = args.block == "bert"
+    layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=dt, fuse_gelu=not args.no_fuse_gelu,
+                       gelu=ee.GELU_ERF if bert else ee.GELU_TANH,
+                       block=ee.BLOCK_BERT_POSTLN if bert else ee.BLOCK_GPT_PRELN,
+                       attention=ee.ATTN_PADDED if args.attention == "padded" else ee.ATTN_VARLEN)
               for p in params]
-    ws = torch.empty(layers[0].workspace_size(B, P, T), dtype=torch.uint8, device=dev)
+    ws = torch.empty(layers[0].workspace_size(B, P, T_run), dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
     stream = torch.cuda.current_stream()
     _log(f"weights {sum(t.numel() * t.element_size() for p in params for t in p.values()) / 1e9:.1f} GB resident; "
          f"workspace {ws.numel() / 1e6:.0f} MB")
 
     for _ in range(args.warmup):
-        ee.ee_stack_forward(layers, x, lens, y, ws, stream)
+        ee.ee_stack_forward(layers, x, run_lens, y, ws, stream)
     torch.cuda.synchronize()
     _log(f"warmup done ({args.warmup} steps)")
 
@@ -180,7 +206,7 @@ def main():
     t_host = time.perf_counter()
     e0.record(stream)
     for _ in range(args.steps):
-        ee.ee_stack_forward(layers, x, lens, y, ws, stream)
+        ee.ee_stack_forward(layers, x, run_lens, y, ws, stream)
     e1.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
@@ -194,9 +220,9 @@ def main():
     for site, st in stats.items():
         n = st["launches"]
         avg_ms = st["total_ms"] / n
-        fl, by = _site_work(w, T, B, P, site)
+        fl, by = _site_work(w, T_run, B, P, site)
         if site == "attention":
-            fl = _attention_flops(w, lens)
+            fl = _attention_flops(w, run_lens, causal=not bert)
         k = {"launches_per_step": n / args.steps, "avg_ms": round(avg_ms, 5),
              "share": round(st["total_ms"] / (ms_step * args.steps), 4)}
         if fl:
@@ -209,15 +235,15 @@ def main():
 
     fc1 = stats[ROOFLINE_KERNEL]
     fc1_ms = fc1["total_ms"] / fc1["launches"]
-    fc1_flops = _site_work(w, T, B, P, ROOFLINE_KERNEL)[0]
+    fc1_flops = _site_work(w, T_run, B, P, ROOFLINE_KERNEL)[0]
     achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": ROOFLINE_SYMBOL, "achieved": round(achieved, 1),
                 "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                "traffic": _traffic(), "avg_launch_ms": round(fc1_ms, 4),
+                "traffic": _traffic() if not (args.no_pack or bert) else None, "avg_launch_ms": round(fc1_ms, 4),
                 "flops_per_launch": fc1_flops}
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not (bert or args.no_pack or args.attention != "varlen"):
         _log("timing the CPU oracle on a bounded sample")
         cpu = _cpu_baseline(w, lens, x.cpu(), params[0], args.cpu_sample_seqs)
 
@@ -228,7 +254,8 @@ def main():
         "data": "synthetic (seeded lengths, N(0,1) activations, N(0,0.02) random-init weights)",
         "config": {"workload": w.name, "batch": B, "pad_len": P, "valid_tokens": T, "layers": L,
                    "hidden": w.hidden, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": w.ffn,
-                   "fuse_gelu": not args.no_fuse_gelu},
+                   "fuse_gelu": not args.no_fuse_gelu, "block": "bert-postln" if bert else "gpt-preln",
+                   "attention": args.attention, "rows_run": T_run, "padding_removed": not args.no_pack},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

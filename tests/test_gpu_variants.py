@@ -162,3 +162,20 @@ def test_encoder_stack_and_nan_pads():
     assert not torch.isnan(y_n).any()
     y_vp = _run(w, lens, x, ps, ee.BLOCK_BERT_POSTLN, ee.ATTN_PADDED, gelu=ee.GELU_ERF)
     assert torch.equal(y_n, y_vp)
+
+
+@pytest.mark.parametrize("name", ["gpt2-small", "tiny-fp32"])
+def test_padding_kept_gives_the_same_valid_rows(name):
+    """The result the method preserves: with right padding and the causal mask,
+    running all B*P rows through the layers (padding kept) leaves the valid
+    rows exactly as the packed run computes them; only the work differs."""
+    w = workloads.get(name)
+    lens = workloads.lengths(w, 77)
+    x = workloads.activations(w, 77, w.batch, w.pad_len, lens, pad_fill="random")
+    ps = [workloads.layer_params(w, 77, l, variant="affine") for l in range(2)]
+    y_rce = _run(w, lens, x, ps, ee.BLOCK_GPT_PRELN, ee.ATTN_VARLEN)
+    y_full = _run(w, [w.pad_len] * w.batch, x, ps, ee.BLOCK_GPT_PRELN, ee.ATTN_VARLEN)
+    m = torch.from_numpy(valid_mask(lens, w.pad_len)).to(DEV)
+    diff = (y_rce[m].float() - y_full[m].float()).abs().max().item()
+    say(f"{name}: padding kept vs removed, max |diff| on valid rows {diff:.3e}")
+    assert torch.equal(y_rce[m], y_full[m])
