@@ -26,6 +26,8 @@
 //     the 8 XCDs, so ids are remapped to give each XCD a contiguous range, and
 //     that range walks tiles in groups of 4 M-tiles, so the workgroups that
 //     share an XCD's L2 share A and W panels.
+//   * Epilogues go through LDS so C and the residual move in 16-byte vectors
+//     (store_tile_staged); a direct per-element store covers N % 8 != 0.
 //   * Ragged M (and N): the buffer descriptors end at the last valid row, so
 //     out-of-range rows load zeros; their results are never stored.  K must be
 //     a multiple of 64, and 256 rows x K x 2 bytes must fit 32-bit offsets.
@@ -80,6 +82,75 @@ __device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int& m0, i
   const int ig = bid - group * per_group;
   m0 = (first_m + ig % gm) * BM;
   n0 = (ig / gm) * BN;
+}
+
+// Row-major epilogue through LDS: the MFMA result layout gives a lane one
+// column of 16 rows, so storing from it writes 2 bytes per lane and 64-byte
+// row pieces.  Instead each wave writes one 32-row band of its block (with
+// bias and GeLU applied, still fp32) to its own slice of the LDS ring, then
+// reads it back as 8 consecutive columns per lane, so C (and the residual R)
+// move in 16-byte vectors and whole 128-byte row segments.  The rounding is
+// the same as the direct store: (acc + bias) + R in fp32, one fp16 rounding.
+// Needs N % 8 == 0 and 16-byte aligned C and R; `stage` holds 32 x kStageLd floats.
+template <int FN>
+struct StagedEpilogue {
+  static constexpr int WTN = FN * 32;
+  static constexpr int kLd = WTN + 8;          // rows r and r+4 land on opposite bank halves
+  static constexpr int kFloats = 32 * kLd;     // per wave
+  static constexpr int kLanesPerRow = WTN / 8;
+  static constexpr int kRowsPerPass = 64 / kLanesPerRow;
+};
+
+template <int FM, int FN, int EPI>
+__device__ __forceinline__ void store_tile_staged(const floatx16 (&acc)[FM][FN], float* __restrict__ stage, int row0,
+                                                  int col0, int lane, const f16* __restrict__ bias,
+                                                  const f16* __restrict__ R, f16* __restrict__ C, int M, int N,
+                                                  int gelu_form) {
+  using SE = StagedEpilogue<FN>;
+  const int hk = lane >> 5;
+  const int c8 = lane % SE::kLanesPerRow, rsub = lane / SE::kLanesPerRow;
+  const int col = col0 + c8 * 8;
+  float bcol[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int cj = col0 + j * 32 + (lane & 31);
+    bcol[j] = (EPI != EE_EPI_NONE && cj < N) ? (float)bias[cj] : 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    // the residual of this band is requested before the band goes through LDS
+    half8 rv[32 / SE::kRowsPerPass];
+#pragma unroll
+    for (int it = 0; it < 32 / SE::kRowsPerPass; ++it) {
+      const int row = row0 + i * 32 + it * SE::kRowsPerPass + rsub;
+      if (EPI == EE_EPI_BIAS_RESIDUAL && row < M && col < N)
+        rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * N + col);
+    }
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float v = acc[i][j][e] + bcol[j];
+        if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
+        stage[((e >> 2) * 8 + hk * 4 + (e & 3)) * SE::kLd + j * 32 + (lane & 31)] = v;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 32 / SE::kRowsPerPass; ++it) {
+      const int r = it * SE::kRowsPerPass + rsub;
+      const int row = row0 + i * 32 + r;
+      const float4 lo = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8);
+      const float4 hi = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8 + 4);
+      if (row < M && col < N) {
+        const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        half8 out;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) out[k] = (f16)(EPI == EE_EPI_BIAS_RESIDUAL ? v[k] + (float)rv[it][k] : v[k]);
+        *reinterpret_cast<half8*>(C + (int64_t)row * N + col) = out;
+      }
+    }
+    __syncthreads();  // the next band overwrites this wave's slice
+  }
 }
 
 // Epilogue of a wave's FM x FN block of 32 x 32 fragments whose top-left
@@ -266,7 +337,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   mfmas(fa1, fb1);
   wait_dma();  // no load may still be writing LDS when the workgroup retires
 
-  store_tile<FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
+  static_assert(NW * StagedEpilogue<FN>::kFloats * 4 <= 2 * STAGE * 2, "epilogue staging exceeds the LDS ring");
+  const bool vec_ok = (N & 7) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(R)) & 15) == 0;
+  if (vec_ok) {
+    __syncthreads();  // every wave is done reading the ring
+    float* stage = reinterpret_cast<float*>(smem) + wave * StagedEpilogue<FN>::kFloats;
+    store_tile_staged<FM, FN, EPI>(acc, stage, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
+  } else {
+    store_tile<FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
+  }
 }
 
 template <int BM, int BN, int WGM, int WGN>
