@@ -31,7 +31,7 @@ METRIC = "valid tokens/s per GPT layer fwd (packed) + % HBM/MFMA roofline, 1 GPU
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROOFLINE_KERNEL = "gemm_fc1"
-ROOFLINE_SYMBOL = "gemm_f16_mfma_kernel<256, 256, 2, 4, EE_EPI_BIAS_GELU>"
+ROOFLINE_SYMBOL = "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, EE_EPI_BIAS_GELU>"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fc1_gpt3-12l_pmc.json")
 GEMM_SOURCE = os.path.join(ROOT, "variable_length_padding_amd", "csrc", "gemm_f16.hip")
 

@@ -127,7 +127,8 @@ def _small_ints(shape, lo=-2, hi=2):
 
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (37, 96, 128), (300, 256, 192), (516, 2304, 768),
                                    (1000, 1000, 640), (4112, 768, 3072), (2048, 4096, 12288),
-                                   (4100, 4200, 320), (4096, 4096, 1024)])
+                                   (4100, 4200, 320), (4096, 4096, 1024), (4096, 4096, 64), (4300, 4096, 192),
+                                   (4096, 4104, 128), (4096, 4099, 64)])
 @pytest.mark.parametrize("epi", [ee.EPI_NONE, ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL])
 def test_gemm_integer_exact(M, N, K, epi):
     """Small-integer fp16 operands: every product and partial sum is an integer

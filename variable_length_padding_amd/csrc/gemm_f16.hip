@@ -8,16 +8,21 @@
 // Design (gfx950, wave64):
 //   * Both operands are K-contiguous, which is the layout the MFMA operand
 //     registers want: every lane reads 8 consecutive K values (16 bytes).
-//   * Workgroup tile BM x BN x 64 with a grid of waves (256 x 256: 2 x 4 waves,
-//     two per SIMD; 128 x 128: 2 x 2); a wave owns a block of 32 x 32
-//     v_mfma_f32_32x32x16_f16 fragments with fp32 accumulators in registers.
-//   * Two LDS stages (BM=BN=256: 2 x 64 KiB of the 160 KiB per CU) filled by
-//     16-byte direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no
-//     register staging and no LDS store instructions.  Tile kt+2 is requested
-//     right after the barrier that retires tile kt's stage, so a load has a
-//     whole K tile of MFMA work to land; one barrier per K tile.
+//   * Large problems: workgroup tile 256 x 256 x 64, 2 x 2 waves (one per
+//     SIMD), each wave a 128 x 128 block of v_mfma_f32_16x16x32_f16 fragments
+//     (256 fp32 accumulators per lane, in AGPRs).  Small problems: 128 x 128
+//     tiles, 2 x 2 waves of 32 x 32 x 16 fragments.  The 128 x 128 wave block
+//     reads 2/3 of the LDS bytes per flop that a 128 x 64 block (two waves per
+//     SIMD) does; the chip is power-limited under this load and ran ~15% higher
+//     clocks with it (1.8 vs 1.5 GHz on the FC1 shape).
+//   * Two LDS stages (2 x 64 KiB of the 160 KiB per CU) filled by 16-byte
+//     direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no register
+//     staging and no LDS store instructions.  Tile kt+2 is requested right
+//     after the barrier that retires tile kt's stage, one load per four MFMAs
+//     (bunching them stalls MFMA issue), so a load has about a K tile of MFMA
+//     work to land; one barrier per K tile.
 //   * MFMA fragments are double-buffered in registers: the LDS reads of K step
-//     kk+1 are in flight while the 16 MFMAs of step kk issue.
+//     kk+1 are in flight while the MFMAs of step kk issue.
 //   * LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row r is stored at
 //     chunk c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), so the 16 rows
 //     read by a quarter-wave land on distinct banks whether the LDS serves
@@ -39,12 +44,15 @@
 namespace ee {
 namespace {
 
-// Wave grid of the 256 x 256 tile: 2 x 4 waves of 128 x 64 (two waves per SIMD,
-// which measured faster than 2 x 2 waves of 128 x 128 at one wave per SIMD).
+// Large-problem configuration: MFMA shape and wave grid of the 256 x 256 tile.
 #ifndef EE_GEMM_WGM
 #define EE_GEMM_WGM 2
-#define EE_GEMM_WGN 4
+#define EE_GEMM_WGN 2
 #endif
+#ifndef EE_GEMM_MF
+#define EE_GEMM_MF 16
+#endif
+
 constexpr int kBK = 64;
 
 __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
@@ -84,61 +92,88 @@ __device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int& m0, i
   n0 = (ig / gm) * BN;
 }
 
+// Fragment geometry of the two MFMA shapes used here.  Element e of lane l
+// of a fragment sits at (row(l, e), col(l)) of its MF x MF block:
+//   32x32x16: row (e/4)*8 + (l/32)*4 + e%4, column l%32 (16 fp32 per lane);
+//   16x16x32: row (l/16)*4 + e,             column l%16 (4 fp32 per lane).
+// A lane feeds the row l%MF of an operand fragment with 8 consecutive K values
+// from K group l/MF.
+template <int MF>
+struct Frag;
+template <>
+struct Frag<32> {
+  using acc_t = floatx16;
+  static constexpr int kElems = 16, kK = 16, kPad = 8;
+  __device__ static int row(int lane, int e) { return (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3); }
+  __device__ static acc_t mfma(half8 a, half8 b, acc_t c) { return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0); }
+};
+template <>
+struct Frag<16> {
+  using acc_t = floatx4;
+  static constexpr int kElems = 4, kK = 32, kPad = 4;
+  __device__ static int row(int lane, int e) { return (lane >> 4) * 4 + e; }
+  __device__ static acc_t mfma(half8 a, half8 b, acc_t c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+};
+
 // Row-major epilogue through LDS: the MFMA result layout gives a lane one
-// column of 16 rows, so storing from it writes 2 bytes per lane and 64-byte
-// row pieces.  Instead each wave writes one 32-row band of its block (with
-// bias and GeLU applied, still fp32) to its own slice of the LDS ring, then
-// reads it back as 8 consecutive columns per lane, so C (and the residual R)
-// move in 16-byte vectors and whole 128-byte row segments.  The rounding is
-// the same as the direct store: (acc + bias) + R in fp32, one fp16 rounding.
-// Needs N % 8 == 0 and 16-byte aligned C and R; `stage` holds 32 x kStageLd floats.
-template <int FN>
+// column of several rows, so storing from it writes 2 bytes per lane and
+// short row pieces.  Instead each wave writes one 32-row band of its block
+// (with bias and GeLU applied, still fp32) to its own slice of the LDS ring,
+// then reads it back as 8 consecutive columns per lane, so C (and the residual
+// R) move in 16-byte vectors and whole row segments.  The rounding is the
+// same as a direct store: (acc + bias) + R in fp32, one fp16 rounding.
+// Needs N % 8 == 0 and 16-byte aligned C and R.  The row pitch WTN + kPad
+// puts the rows one lane group writes at once on disjoint banks.
+template <int MF, int FN>
 struct StagedEpilogue {
-  static constexpr int WTN = FN * 32;
-  static constexpr int kLd = WTN + 8;          // rows r and r+4 land on opposite bank halves
-  static constexpr int kFloats = 32 * kLd;     // per wave
+  static constexpr int WTN = FN * MF;
+  static constexpr int kLd = WTN + Frag<MF>::kPad;
+  static constexpr int kFloats = 32 * kLd;  // per wave
   static constexpr int kLanesPerRow = WTN / 8;
   static constexpr int kRowsPerPass = 64 / kLanesPerRow;
 };
 
-template <int FM, int FN, int EPI>
-__device__ __forceinline__ void store_tile_staged(const floatx16 (&acc)[FM][FN], float* __restrict__ stage, int row0,
-                                                  int col0, int lane, const f16* __restrict__ bias,
+template <int MF, int FM, int FN, int EPI>
+__device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t (&acc)[FM][FN], float* __restrict__ stage,
+                                                  int row0, int col0, int lane, const f16* __restrict__ bias,
                                                   const f16* __restrict__ R, f16* __restrict__ C, int M, int N,
                                                   int gelu_form) {
-  using SE = StagedEpilogue<FN>;
-  const int hk = lane >> 5;
+  using SE = StagedEpilogue<MF, FN>;
+  constexpr int FPB = 32 / MF;  // fragment rows per 32-row band
+  constexpr int PASSES = 32 / SE::kRowsPerPass;
   const int c8 = lane % SE::kLanesPerRow, rsub = lane / SE::kLanesPerRow;
   const int col = col0 + c8 * 8;
   float bcol[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int cj = col0 + j * 32 + (lane & 31);
+    const int cj = col0 + j * MF + lane % MF;
     bcol[j] = (EPI != EE_EPI_NONE && cj < N) ? (float)bias[cj] : 0.f;
   }
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+  for (int band = 0; band < FM / FPB; ++band) {
     // the residual of this band is requested before the band goes through LDS
-    half8 rv[32 / SE::kRowsPerPass];
+    half8 rv[PASSES];
 #pragma unroll
-    for (int it = 0; it < 32 / SE::kRowsPerPass; ++it) {
-      const int row = row0 + i * 32 + it * SE::kRowsPerPass + rsub;
+    for (int it = 0; it < PASSES; ++it) {
+      const int row = row0 + band * 32 + it * SE::kRowsPerPass + rsub;
       if (EPI == EE_EPI_BIAS_RESIDUAL && row < M && col < N)
         rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * N + col);
     }
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int ii = 0; ii < FPB; ++ii)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float v = acc[i][j][e] + bcol[j];
-        if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
-        stage[((e >> 2) * 8 + hk * 4 + (e & 3)) * SE::kLd + j * 32 + (lane & 31)] = v;
-      }
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < Frag<MF>::kElems; ++e) {
+          float v = acc[band * FPB + ii][j][e] + bcol[j];
+          if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
+          stage[(ii * MF + Frag<MF>::row(lane, e)) * SE::kLd + j * MF + lane % MF] = v;
+        }
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < 32 / SE::kRowsPerPass; ++it) {
+    for (int it = 0; it < PASSES; ++it) {
       const int r = it * SE::kRowsPerPass + rsub;
-      const int row = row0 + i * 32 + r;
+      const int row = row0 + band * 32 + r;
       const float4 lo = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8);
       const float4 hi = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8 + 4);
       if (row < M && col < N) {
@@ -153,25 +188,22 @@ __device__ __forceinline__ void store_tile_staged(const floatx16 (&acc)[FM][FN],
   }
 }
 
-// Epilogue of a wave's FM x FN block of 32 x 32 fragments whose top-left
-// output element is (row0, col0).  Fragment element e of lane l is row
-// (e/4)*8 + (l/32)*4 + e%4, column l%32 of its block.
-template <int FM, int FN, int EPI>
-__device__ __forceinline__ void store_tile(const floatx16 (&acc)[FM][FN], int row0, int col0, int lane,
+// Direct per-element epilogue of a wave's FM x FN block of fragments whose
+// top-left output element is (row0, col0); used when N % 8 != 0.
+template <int MF, int FM, int FN, int EPI>
+__device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)[FM][FN], int row0, int col0, int lane,
                                            const f16* __restrict__ bias, const f16* __restrict__ R,
                                            f16* __restrict__ C, int M, int N, int gelu_form) {
-  const int hk = lane >> 5;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int col = col0 + j * 32 + (lane & 31);
+    const int col = col0 + j * MF + lane % MF;
     if (col >= N) continue;
     const float bcol = (EPI != EE_EPI_NONE) ? (float)bias[col] : 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int rbase = row0 + i * 32 + hk * 4;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = rbase + (e >> 2) * 8 + (e & 3);
+      for (int e = 0; e < Frag<MF>::kElems; ++e) {
+        const int row = row0 + i * MF + Frag<MF>::row(lane, e);
         if (row < M) {
           float v = acc[i][j][e] + bcol;
           if (EPI == EE_EPI_BIAS_RESIDUAL) v += (float)R[(int64_t)row * N + col];
@@ -183,17 +215,21 @@ __device__ __forceinline__ void store_tile(const floatx16 (&acc)[FM][FN], int ro
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int EPI>
+template <int MF, int BM, int BN, int WGM, int WGN, int EPI>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16* __restrict__ A, const f16* __restrict__ W,
                                                                  const f16* __restrict__ bias,
                                                                  const f16* __restrict__ R, f16* __restrict__ C,
                                                                  int M, int N, int K, int gelu_form, int tiles_m,
                                                                  int tiles_n) {
+  using FR = Frag<MF>;
+  using acc_t = typename FR::acc_t;
   constexpr int NW = WGM * WGN;                // waves: WGM x WGN grid over the tile
   constexpr int WTM = BM / WGM, WTN = BN / WGN;  // wave tile
-  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int FM = WTM / MF, FN = WTN / MF;
+  constexpr int NSTEP = kBK / FR::kK;          // MFMA K steps per K tile (4 or 2)
   constexpr int AJ = BM / (8 * NW), BJ = BN / (8 * NW);  // direct-to-LDS loads per wave per K tile (8 rows each)
   constexpr int STAGE = (BM + BN) * kBK;     // halves per LDS stage
+  static_assert(NSTEP == 2 || NSTEP == 4, "two or four K steps per K tile");
   __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
 
   int m0, n0;
@@ -240,57 +276,57 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     for (int q = 0; q < AJ + BJ; ++q) dma_one(stage, k0, q);
   };
 
-  // ---- wave / lane roles for the MFMA fragments
+  // ---- wave / lane roles for the MFMA fragments.  Fragment rows are
+  // lane % MF (+ MF per fragment), so f(row) = f(lane % 16) for both shapes.
   const int wm = wave / WGN, wn = wave % WGN;
-  const int hk = lane >> 5;  // which 8-wide K half of a 16-wide MFMA step this lane feeds
+  const int kg = lane / MF;  // which 8-wide K group of an MFMA step this lane feeds
   const int rsw = lds_swizzle(lane & 15);
-  const int abase = (wm * WTM + (lane & 31)) * kBK;
-  const int bbase = BM * kBK + (wn * WTN + (lane & 31)) * kBK;
+  const int abase = (wm * WTM + lane % MF) * kBK;
+  const int bbase = BM * kBK + (wn * WTN + lane % MF) * kBK;
   // Reads are issued in the order the MFMAs below consume them (a0, b0..bN, a1..aM),
   // so each MFMA waits only for its own operands.
   auto frag_one = [&](int stage, int kk, int r, half8 (&af)[FM], half8 (&bf)[FN]) {
     const f16* s = smem + stage * STAGE;
-    const int ch = ((kk * 2 + hk) ^ rsw) * 8;
+    const int ch = ((kk * (FR::kK / 8) + kg) ^ rsw) * 8;
     if (r == 0)
       af[0] = *reinterpret_cast<const half8*>(s + abase + ch);
     else if (r <= FN)
-      bf[r - 1] = *reinterpret_cast<const half8*>(s + bbase + (r - 1) * 32 * kBK + ch);
+      bf[r - 1] = *reinterpret_cast<const half8*>(s + bbase + (r - 1) * MF * kBK + ch);
     else
-      af[r - FN] = *reinterpret_cast<const half8*>(s + abase + (r - FN) * 32 * kBK + ch);
+      af[r - FN] = *reinterpret_cast<const half8*>(s + abase + (r - FN) * MF * kBK + ch);
   };
   auto frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
 #pragma unroll
     for (int r = 0; r < FM + FN; ++r) frag_one(stage, kk, r, af, bf);
   };
 
-  floatx16 acc[FM][FN];
+  acc_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+      for (int e = 0; e < FR::kElems; ++e) acc[i][j][e] = 0.f;
   auto mfmas = [&](const half8 (&af)[FM], const half8 (&bf)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[i], bf[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < FN; ++j) acc[i][j] = FR::mfma(af[i], bf[j], acc[i][j]);
   };
 
   // ---- main loop.  Stage kt&1 holds K tile kt.  The barrier at the end of
   // tile kt both publishes tile kt+1 (each wave waited for its own loads) and
   // retires every read of stage kt&1, which then receives tile kt+2 (clamped
   // to the last tile: a redundant load into a stage nobody reads again keeps
-  // the loop body free of branches).  The 16 MFMAs of the tile's last K step
+  // the loop body free of branches).  The MFMAs of the tile's last K step
   // issue after the barrier, from fragments already in registers, while the
   // next tile's first fragments and the new loads are in flight.
   //
   // Within a K step the order is written out and fenced with sched_barrier:
-  // every other MFMA is preceded by one LDS read of the next step (reads in
-  // consumption order: a0, b0..b3, a1..a3) and, after the barrier, every MFMA
-  // by its share of the tile's direct-to-LDS loads.  LDS demand stays even
-  // (no bursts) and each operand is requested 10+ MFMAs (320+ cycles) before
-  // its first use.
+  // the LDS reads of the next step are spread evenly over the MFMAs (reads in
+  // consumption order: a0, b0.., a1..) and, after the barrier, so are the
+  // tile's direct-to-LDS loads.  LDS demand stays even (no bursts) and each
+  // operand is requested well before its first use.
   constexpr int NF = FM + FN;  // LDS reads per K step
   constexpr int NM = FM * FN;  // MFMAs per K step
   constexpr int NL = AJ + BJ;  // direct-to-LDS loads per K tile
@@ -308,7 +344,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
 #pragma unroll
       for (int r = m * NF / NM; r < (m + 1) * NF / NM; ++r) frag_one(rstage, rkk, r, ya, yb);
       const int i = m / FN, j = m % FN;
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(xa[i], xb[j], acc[i][j], 0, 0, 0);
+      acc[i][j] = FR::mfma(xa[i], xb[j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -321,34 +357,39 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   frags(0, 0, fa0, fb0);
   const std::integral_constant<bool, false> no_dma;
   const std::integral_constant<bool, true> with_dma;
+  // the K steps of a tile before its barrier (all but the last); NSTEP is even,
+  // so the last step's fragments are always in fa1/fb1
+  auto steps_before_barrier = [&](int stage) {
+    step(no_dma, fa0, fb0, stage, 1, fa1, fb1, 0, 0);
+    if constexpr (NSTEP == 4) {
+      step(no_dma, fa1, fb1, stage, 2, fa0, fb0, 0, 0);
+      step(no_dma, fa0, fb0, stage, 3, fa1, fb1, 0, 0);
+    }
+  };
   int cur = 0;
   for (int kt = 0; kt + 1 < nk; ++kt) {
-    step(no_dma, fa0, fb0, cur, 1, fa1, fb1, 0, 0);
-    step(no_dma, fa1, fb1, cur, 2, fa0, fb0, 0, 0);
-    step(no_dma, fa0, fb0, cur, 3, fa1, fb1, 0, 0);
+    steps_before_barrier(cur);
     wait_dma();
     __syncthreads();
     step(with_dma, fa1, fb1, cur ^ 1, 0, fa0, fb0, cur, min(kt + 2, nk - 1) * kBK);
     cur ^= 1;
   }
-  step(no_dma, fa0, fb0, cur, 1, fa1, fb1, 0, 0);
-  step(no_dma, fa1, fb1, cur, 2, fa0, fb0, 0, 0);
-  step(no_dma, fa0, fb0, cur, 3, fa1, fb1, 0, 0);
+  steps_before_barrier(cur);
   mfmas(fa1, fb1);
   wait_dma();  // no load may still be writing LDS when the workgroup retires
 
-  static_assert(NW * StagedEpilogue<FN>::kFloats * 4 <= 2 * STAGE * 2, "epilogue staging exceeds the LDS ring");
+  static_assert(NW * StagedEpilogue<MF, FN>::kFloats * 4 <= 2 * STAGE * 2, "epilogue staging exceeds the LDS ring");
   const bool vec_ok = (N & 7) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(R)) & 15) == 0;
   if (vec_ok) {
     __syncthreads();  // every wave is done reading the ring
-    float* stage = reinterpret_cast<float*>(smem) + wave * StagedEpilogue<FN>::kFloats;
-    store_tile_staged<FM, FN, EPI>(acc, stage, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
+    float* stage = reinterpret_cast<float*>(smem) + wave * StagedEpilogue<MF, FN>::kFloats;
+    store_tile_staged<MF, FM, FN, EPI>(acc, stage, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
   } else {
-    store_tile<FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
+    store_tile<MF, FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
   }
 }
 
-template <int BM, int BN, int WGM, int WGN>
+template <int MF, int BM, int BN, int WGM, int WGN>
 hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K,
                       ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
@@ -360,19 +401,19 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
   f16* c = static_cast<f16*>(C);
   switch (epi) {
     case EE_EPI_NONE:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_NONE>), grid, block, 0, s, a, w, b, r, c, M, N, K,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_NONE>), grid, block, 0, s, a, w, b, r, c, M, N, K,
                          (int)form, tm, tn);
       break;
     case EE_EPI_BIAS:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_BIAS>), grid, block, 0, s, a, w, b, r, c, M, N, K,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_BIAS>), grid, block, 0, s, a, w, b, r, c, M, N, K,
                          (int)form, tm, tn);
       break;
     case EE_EPI_BIAS_RESIDUAL:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_BIAS_RESIDUAL>), grid, block, 0, s, a, w, b, r, c, M,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_BIAS_RESIDUAL>), grid, block, 0, s, a, w, b, r, c, M,
                          N, K, (int)form, tm, tn);
       break;
     case EE_EPI_BIAS_GELU:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<BM, BN, WGM, WGN, EE_EPI_BIAS_GELU>), grid, block, 0, s, a, w, b, r, c, M, N,
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_BIAS_GELU>), grid, block, 0, s, a, w, b, r, c, M, N,
                          K, (int)form, tm, tn);
       break;
   }
@@ -389,8 +430,9 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
                                 int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles_big >= 256) return launch_cfg<256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
-  return launch_cfg<128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
+  if (tiles_big >= 256)
+    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
+  return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
 }
 
 }  // namespace ee
