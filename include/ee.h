@@ -265,6 +265,58 @@ EE_API ee_status ee_profile_enable(int32_t on);
  * `out` (host), sets *count, and clears the record. */
 EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* count);
 
+/* ---- Batch planning over a request queue (host only; no device work) ----
+ *
+ * The announcement article's "Serving" section and the README's "Batching"
+ * section: queued variable-length requests are packed into batches according
+ * to how fast the machine runs them, then the batch with the highest priority
+ * is run first (waiting time, batch size, how much the batch could still grow
+ * at its padded length); the packing follows TurboTransformers' dynamic
+ * programming scheduler.  The baseline is FIFO packing, each batch padded to
+ * its longest request (the "Performance tests" section).
+ *
+ * Cost of running one batch of B requests with lengths len_1..len_B, padded
+ * to P = max len_i:
+ *   t_batch + t_token * tokens + t_row * B * P + t_pair * pairs
+ * tokens = sum len_i rounded up to a multiple of token_quantum (1 = no
+ * rounding), pairs = sum len_i (len_i + 1) / 2 (causal attention);
+ * padded_compute != 0 models a forward that keeps the padding: tokens = B * P
+ * and pairs = B * P (P + 1) / 2.  The coefficients are fitted to measured
+ * batch times on the machine. */
+typedef struct {
+  double t_batch;
+  double t_token;
+  double t_row;
+  double t_pair;
+  int32_t token_quantum;
+  int32_t padded_compute;
+} ee_batch_cost;
+
+/* Cost of one batch under `cost` (as above).  lens: host, n >= 1 values >= 1. */
+EE_API ee_status ee_batch_cost_eval(const int32_t* lens, int32_t n, const ee_batch_cost* cost, double* out);
+
+/* FIFO: request i (arrival order) goes to batch i / max_batch.
+ * batch_of: host [n] output; *n_batches set.  lens only checked (>= 1). */
+EE_API ee_status ee_plan_fifo(const int32_t* lens, int32_t n, int32_t max_batch, int32_t* batch_of,
+                              int32_t* n_batches);
+
+/* Dynamic batching.  The requests are ordered by length (arrival order breaks
+ * ties) and split into contiguous runs of that order by dynamic programming
+ * over prefixes, minimising the summed batch cost subject to at most
+ * max_batch requests and at most max_tokens rows per batch (rows = sum len,
+ * or B * P with padded_compute; max_tokens <= 0: no limit).  Ties between
+ * equal-cost splits go to the longer last batch.  The batches are then
+ * numbered in priority order: longest waiting request first (wait: host [n]
+ * seconds each request has waited, or NULL for all zero), then more
+ * requests, then earliest arrival.
+ * batch_of: host [n] output, the run position of each request's batch;
+ * *n_batches set; *total_cost (may be NULL) the summed cost.
+ * Errors: EE_ERR_INVALID_ARG for n < 0, max_batch < 1, a length < 1, a
+ * request longer than max_tokens, or NULL outputs.  Allocates host memory. */
+EE_API ee_status ee_plan_dynamic(const int32_t* lens, const double* wait, int32_t n, int32_t max_batch,
+                                 int64_t max_tokens, const ee_batch_cost* cost, int32_t* batch_of,
+                                 int32_t* n_batches, double* total_cost);
+
 #ifdef __cplusplus
 }
 #endif

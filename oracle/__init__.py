@@ -41,3 +41,6 @@ from .layer import (  # noqa: F401
     add_bias_residual_layernorm, attention_packed_bidirectional, attention_via_padded_heads,
     encoder_layer_forward_packed, encoder_layer_forward_padded,
 )
+from .batching import (  # noqa: F401
+    Cost, batch_cost, fifo_batches, length_order, dp_runs, dynamic_batches, padded_rows,
+)

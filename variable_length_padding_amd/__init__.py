@@ -20,6 +20,7 @@ __all__ = [
     "ee_transpose_padding_remove_heads", "ee_add_bias_residual_layernorm",
     "BLOCK_GPT_PRELN", "BLOCK_BERT_POSTLN", "ATTN_VARLEN", "ATTN_PADDED",
     "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_collect",
+    "BatchCost", "ee_batch_cost_eval", "ee_plan_fifo", "ee_plan_dynamic", "batches_of",
     "EXPORTED_SYMBOLS", "lib_path",
 ]
 
@@ -65,6 +66,12 @@ class KernelStat(C.Structure):
     _fields_ = [("name", C.c_char * 32), ("launches", C.c_int64), ("total_ms", C.c_double)]
 
 
+class BatchCost(C.Structure):
+    """Per-batch cost model of the batch planners (seconds)."""
+    _fields_ = [("t_batch", C.c_double), ("t_token", C.c_double), ("t_row", C.c_double), ("t_pair", C.c_double),
+                ("token_quantum", C.c_int32), ("padded_compute", C.c_int32)]
+
+
 _VP, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t
 _PI32 = C.POINTER(C.c_int32)
 
@@ -96,6 +103,10 @@ _SIGS = {
                                                  _VP]),
     "ee_profile_enable": (C.c_int, [_I32]),
     "ee_profile_collect": (C.c_int, [C.POINTER(KernelStat), _I32, _PI32]),
+    "ee_batch_cost_eval": (C.c_int, [_PI32, _I32, C.POINTER(BatchCost), C.POINTER(C.c_double)]),
+    "ee_plan_fifo": (C.c_int, [_PI32, _I32, _I32, _PI32, _PI32]),
+    "ee_plan_dynamic": (C.c_int, [_PI32, C.POINTER(C.c_double), _I32, _I32, _I64, C.POINTER(BatchCost), _PI32,
+                                  _PI32, C.POINTER(C.c_double)]),
 }
 EXPORTED_SYMBOLS = tuple(_SIGS)
 
@@ -302,3 +313,46 @@ def ee_profile_collect() -> Dict[str, Dict[str, float]]:
     _check(lib().ee_profile_collect(arr, cap, C.byref(n)), "ee_profile_collect")
     return {arr[i].name.decode(): {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms)}
             for i in range(n.value)}
+
+
+# ---------------------------------------------------------------- batch planning (host only)
+def _cost(t_batch=0.0, t_token=0.0, t_row=0.0, t_pair=0.0, token_quantum=1, padded_compute=False) -> BatchCost:
+    return BatchCost(float(t_batch), float(t_token), float(t_row), float(t_pair), int(token_quantum),
+                     1 if padded_compute else 0)
+
+
+def ee_batch_cost_eval(lens: Sequence[int], cost: BatchCost) -> float:
+    out = C.c_double(0.0)
+    _check(lib().ee_batch_cost_eval(_lens(lens), len(lens), C.byref(cost), C.byref(out)), "ee_batch_cost_eval")
+    return out.value
+
+
+def ee_plan_fifo(lens: Sequence[int], max_batch: int) -> List[int]:
+    """Batch index of each request (arrival order), FIFO groups of max_batch."""
+    n = len(lens)
+    out = (C.c_int32 * max(1, n))()
+    nb = C.c_int32(0)
+    _check(lib().ee_plan_fifo(_lens(lens), n, max_batch, out, C.byref(nb)), "ee_plan_fifo")
+    return list(out)[:n]
+
+
+def ee_plan_dynamic(lens: Sequence[int], max_batch: int, cost: BatchCost, max_tokens: int = 0,
+                    wait: Optional[Sequence[float]] = None):
+    """(batch index of each request in run order, summed cost) of the dynamic plan."""
+    n = len(lens)
+    out = (C.c_int32 * max(1, n))()
+    nb = C.c_int32(0)
+    total = C.c_double(0.0)
+    w = None if wait is None else (C.c_double * max(1, n))(*[float(x) for x in wait])
+    _check(lib().ee_plan_dynamic(_lens(lens), w, n, max_batch, int(max_tokens), C.byref(cost), out, C.byref(nb),
+                                 C.byref(total)), "ee_plan_dynamic")
+    return list(out)[:n], total.value
+
+
+def batches_of(plan: Sequence[int]) -> List[List[int]]:
+    """Request indices of each batch, in run order, from a batch-index plan."""
+    nb = (max(plan) + 1) if plan else 0
+    groups: List[List[int]] = [[] for _ in range(nb)]
+    for i, b in enumerate(plan):
+        groups[b].append(i)
+    return groups

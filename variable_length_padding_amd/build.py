@@ -21,7 +21,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libee.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "offsets.hip", "padding.hip", "layernorm.hip", "bias_gelu.hip",
+SOURCES = ["api.cpp", "batching.cpp", "offsets.hip", "padding.hip", "layernorm.hip", "bias_gelu.hip",
            "gemm_f16.hip", "gemm_valu.hip", "attention.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_*_f32 instructions.

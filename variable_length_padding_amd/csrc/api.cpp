@@ -40,6 +40,15 @@ ee_status fail(ee_status s, const char* fmt, ...) {
   return s;
 }
 
+}  // namespace
+
+ee_status ee::set_error(ee_status s, const char* msg) {
+  g_err = msg;
+  return s;
+}
+
+namespace {
+
 ee_status hip_fail(hipError_t e, const char* what) {
   return fail(EE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }

@@ -16,6 +16,9 @@ struct LensArg {
   int32_t v[EE_MAX_BATCH];
 };
 
+// Records `msg` as the calling thread's last error (ee_last_error) and returns s.
+ee_status set_error(ee_status s, const char* msg);
+
 // ---- offsets.hip ----
 hipError_t launch_offsets(const LensArg& lens, int B, int P, int32_t* cu, int32_t* token_src,
                           int32_t* pad2pack, hipStream_t s);
