@@ -14,6 +14,14 @@ roofline: the FC1 GEMM kernel (gelu epilogue, the largest single contraction;
 the GEMMs together take ~95% of a step), algorithmic flops 2*T*H*F per launch
 over its hipEvent-measured average duration on the launch stream.
 cpu_baseline: the CPU oracle's packed layer forward on a bounded sample.
+
+    python bench.py --workload gpt3-48l-stream [--no-pack] [--max-batch N]
+
+The request stream (1024 requests, lengths U[1,256], 48 layers): FIFO batches
+and dynamically planned batches (ee_plan_dynamic, on a table of batch times
+measured at the start of the run) each run once over the whole stream; the
+line's value is the dynamic plan's valid tokens/s per layer, and "batching"
+holds both plans' times, batch counts and padded-row ratios.
 """
 from __future__ import annotations
 
@@ -54,6 +62,8 @@ def _parse():
     ap.add_argument("--no-pack", action="store_true",
                     help="padding kept: every one of the B*P rows runs through the layers (the redundant "
                          "computation the method removes); value still counts valid tokens only")
+    ap.add_argument("--max-batch", type=int, default=0,
+                    help="request-stream workload: batch size cap of both planners (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scale reference for HBM byte counters)")
     return ap.parse_args()
@@ -149,6 +159,142 @@ def _copy_calibration():
     print(json.dumps({"copy_calibration_bytes_read": n, "bytes_written": n, "launches": 5}), flush=True)
 
 
+def _stream_bench(args):
+    """The request stream: both planners (FIFO and dynamic) over all requests
+    through all layers, one timed pass each, in one process."""
+    import numpy as np
+    import torch
+
+    import variable_length_padding_amd as ee
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload)
+    lens = [n for g in workloads.request_stream(w, args.seed) for n in g]
+    n_req, L, P_max = len(lens), w.layers, w.pad_len
+    cap = args.max_batch or w.batch
+    T = sum(lens)
+    stream = torch.cuda.current_stream()
+    _log(f"request stream {w.name}: {n_req} requests, T={T}, {L} layers, batch cap {cap}, "
+         f"padding {'kept' if args.no_pack else 'removed'}")
+    params = []
+    for l in range(L):
+        params.append(workloads.layer_params(w, args.seed, l, device=dev))
+        if l % 12 == 11:
+            torch.cuda.synchronize()
+            _log(f"weights: {l + 1}/{L} layers")
+    dt = ee.F16 if w.dtype == "f16" else ee.F32
+    layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=dt) for p in params]
+    reqs = workloads.request_activations(w, args.seed, lens, device=dev)
+    ws = torch.empty(layers[0].workspace_size(cap, P_max, cap * P_max), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def run(x, batch_lens, y):
+        B, P, _ = x.shape
+        ee.ee_stack_forward(layers, x, [P] * B if args.no_pack else batch_lens, y, ws, stream)
+
+    # cost model "by machine performance" (TurboTransformers' scheduler works
+    # from a table of measured batch times): the whole stack timed on batches
+    # of `cap` equal-length requests, tokens = (k + 1) * 8 * cap, no padding
+    # (random activations: the chip draws more power, and clocks lower, on random data than on zeros)
+    x_cal = workloads.activations(w, args.seed + 9, cap, P_max, device=dev)
+
+    def timed(bl, P=None):
+        P = P or max(bl)
+        x = x_cal[:len(bl), :P].contiguous()
+        y = torch.empty_like(x)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run(x, bl, y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+    quantum = 8 * cap
+    timed([8] * cap)                                   # warm-up
+    table = [timed([8 * (k + 1)] * cap) for k in range(P_max // 8)]
+    _log(f"cost table: {len(table)} batch sizes timed, {table[0]:.3f} s at {quantum} tokens .. "
+         f"{table[-1]:.3f} s at {quantum * len(table)}")
+    t_row = 0.0
+    if not args.no_pack:
+        # with the padding removed, a padded row costs only its share of the
+        # rebuild (written as zeros); time that on its own: one-token sequences
+        x = torch.zeros((cap, P_max, w.hidden), dtype=w.torch_dtype, device=dev)
+        packed = torch.zeros((cap, w.hidden), dtype=w.torch_dtype, device=dev)
+        pws = torch.empty(ee.ee_padding_workspace_size(cap, P_max), dtype=torch.uint8, device=dev)
+        ee.ee_rebuild_padding(packed, [1] * cap, x, pws, stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            ee.ee_rebuild_padding(packed, [1] * cap, x, pws, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        t_row = e0.elapsed_time(e1) / 1e3 / 10 / (cap * P_max)
+        del x, packed, pws
+    cost = ee.BatchCost(0.0, 0.0, t_row, 0.0, quantum, 1 if args.no_pack else 0).set_table(table)
+    g = torch.Generator().manual_seed(args.seed + 7)
+    checks = []
+    for B, P in ((cap, P_max), (max(1, cap // 2), P_max // 2)):
+        bl = torch.randint(1, P + 1, (B,), generator=g).tolist()
+        checks.append((B, sum(bl), timed(bl), ee.ee_batch_cost_eval(bl, cost)))
+    _log("cost model check: " + ", ".join(f"B={B} T={T}: measured {t:.3f} s, model {m:.3f} s"
+                                           for B, T, t, m in checks))
+    del x_cal
+    plans = {"fifo": ee.batches_of(ee.ee_plan_fifo(lens, cap)),
+             "dynamic": ee.batches_of(ee.ee_plan_dynamic(lens, cap, cost)[0])}
+    results = {}
+    fc1 = {}
+    for name, plan in plans.items():
+        xs = [workloads.pad_batch([reqs[i] for i in b]) for b in plan]
+        ys = [torch.empty_like(x) for x in xs]
+        bls = [[lens[i] for i in b] for b in plan]
+        run(xs[0], bls[0], ys[0])                     # warm-up: one batch
+        torch.cuda.synchronize()
+        ee.ee_profile_enable(True)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for x, bl, y in zip(xs, bls, ys):
+            run(x, bl, y)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ee.ee_profile_enable(False)
+        st = ee.ee_profile_collect()
+        sec = e0.elapsed_time(e1) / 1e3
+        rows = sum(x.shape[0] * x.shape[1] for x in xs)
+        rows_run = rows if args.no_pack else T
+        fc1[name] = (st["gemm_fc1"]["total_ms"], 2.0 * rows_run * w.hidden * w.ffn * L)
+        results[name] = {
+            "batches": len(plan), "padded_rows": rows, "padded_ratio": round(rows / T, 4), "rows_run": rows_run,
+            "seconds": round(sec, 3), "value": round(T * L / sec, 1),
+            "predicted_seconds": round(sum(ee.ee_batch_cost_eval(bl, cost) for bl in bls), 3)}
+        _log(f"{name}: {len(plan)} batches, padded/valid rows {rows / T:.3f}, {sec:.2f} s, "
+             f"{T * L / sec:.0f} valid tokens/s per layer (model {results[name]['predicted_seconds']:.2f} s)")
+        del xs, ys
+        torch.cuda.synchronize()
+
+    ms, flops = fc1["dynamic"]
+    achieved = flops / (ms * 1e-3) / 1e12
+    d = results["dynamic"]
+    out = {
+        "metric": METRIC, "value": d["value"], "unit": "valid tokens/s per layer", "n_gpus": 1, "steps": 1,
+        "warmup": 1, "ms_per_step": round(1e3 * d["seconds"], 1), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f16" if w.dtype == "f16" else "f32",
+        "data": "synthetic (seeded request lengths U[1,%d], N(0,1) activations, N(0,0.02) random-init weights)" % P_max,
+        "config": {"workload": w.name, "requests": n_req, "valid_tokens": T, "layers": L, "max_batch": cap,
+                   "hidden": w.hidden, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": w.ffn,
+                   "batching": "dynamic", "padding_removed": not args.no_pack},
+        "roofline": {"bound": "mfma", "kernel": ROOFLINE_SYMBOL, "achieved": round(achieved, 1),
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "traffic": None, "note": "FC1 launches of the dynamic plan: summed flops over summed time"},
+        "cpu_baseline": None,
+        "batching": {"fifo": results["fifo"], "dynamic": d,
+                     "dynamic_over_fifo": round(d["value"] / results["fifo"]["value"], 4),
+                     "cost_model": {"t_row": cost.t_row, "token_quantum": quantum,
+                                    "token_table_s": [round(v, 4) for v in table],
+                                    "check": [[B, T, round(t, 4), round(m, 4)] for B, T, t, m in checks]}},
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -168,7 +314,8 @@ def main():
     dev = torch.device("cuda:0")
     w = workloads.get(args.workload)
     if w.requests:
-        raise SystemExit("the request-stream workload is not a bench line")
+        _stream_bench(args)
+        return
     lens = workloads.lengths(w, args.seed)
     B, P, L = w.batch, w.pad_len, w.layers
     T = sum(lens)

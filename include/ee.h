@@ -277,12 +277,17 @@ EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32
  *
  * Cost of running one batch of B requests with lengths len_1..len_B, padded
  * to P = max len_i:
- *   t_batch + t_token * tokens + t_row * B * P + t_pair * pairs
+ *   t_batch + S(tokens) + t_row * B * P + t_pair * pairs
  * tokens = sum len_i rounded up to a multiple of token_quantum (1 = no
  * rounding), pairs = sum len_i (len_i + 1) / 2 (causal attention);
  * padded_compute != 0 models a forward that keeps the padding: tokens = B * P
- * and pairs = B * P (P + 1) / 2.  The coefficients are fitted to measured
- * batch times on the machine. */
+ * and pairs = B * P (P + 1) / 2.
+ * S(tokens) = t_token * tokens, or, when token_table is given (host,
+ * token_table_len >= 1 entries), the measured seconds of a batch of
+ * tokens = (k + 1) * token_quantum at entry k, extended past the last entry
+ * along the line through the last two (or through the origin and the only
+ * one).  The coefficients and the table come from batch times measured on
+ * the machine. */
 typedef struct {
   double t_batch;
   double t_token;
@@ -290,6 +295,8 @@ typedef struct {
   double t_pair;
   int32_t token_quantum;
   int32_t padded_compute;
+  const double* token_table;
+  int32_t token_table_len;
 } ee_batch_cost;
 
 /* Cost of one batch under `cost` (as above).  lens: host, n >= 1 values >= 1. */

@@ -42,5 +42,5 @@ from .layer import (  # noqa: F401
     encoder_layer_forward_packed, encoder_layer_forward_padded,
 )
 from .batching import (  # noqa: F401
-    Cost, batch_cost, fifo_batches, length_order, dp_runs, dynamic_batches, padded_rows,
+    Cost, batch_cost, token_seconds, fifo_batches, length_order, dp_runs, dynamic_batches, padded_rows,
 )

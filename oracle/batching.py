@@ -9,10 +9,12 @@ scheduler); FIFO packing padded to each batch's longest request is the
 baseline of the article's "Performance tests" section.
 
 Readings (the pages give no formula):
-  * cost of a batch = t_batch + t_token * tokens + t_row * B * P + t_pair * pairs
+  * cost of a batch = t_batch + S(tokens) + t_row * B * P + t_pair * pairs
     with P the longest length in the batch, tokens the summed lengths (rounded
     up to token_quantum), pairs the summed len(len+1)/2; when the forward keeps
-    the padding, tokens = B * P and pairs = B * P(P+1)/2;
+    the padding, tokens = B * P and pairs = B * P(P+1)/2; S is linear
+    (t_token * tokens) or a table of measured batch times over token counts
+    (TurboTransformers' scheduler works from such a table);
   * the plan splits the length-sorted queue (ties by arrival) into runs, the
     least summed cost over all such splits, ties to the longer last batch;
   * run order: longest waiting request first, then more requests, then the
@@ -34,6 +36,25 @@ class Cost:
     t_pair: float = 0.0
     token_quantum: int = 1
     padded_compute: bool = False
+    token_table: Tuple[float, ...] = ()
+
+
+def token_seconds(tokens: float, c: Cost) -> float:
+    """The token term: t_token * tokens, or the measured table -- entry k holds
+    a batch of (k + 1) * token_quantum tokens; past the end, the line through
+    the last two entries (or through the origin and the only entry)."""
+    if not c.token_table:
+        return c.t_token * tokens
+    q = max(1, c.token_quantum)
+    k = int(tokens // q) - 1
+    table = c.token_table
+    if k < 0:
+        return 0.0
+    if k < len(table):
+        return table[k]
+    if len(table) >= 2:
+        return table[-1] + (k - (len(table) - 1)) * (table[-1] - table[-2])
+    return table[0] * (k + 1)
 
 
 def batch_cost(batch_lens: Sequence[int], c: Cost) -> float:
@@ -48,7 +69,7 @@ def batch_cost(batch_lens: Sequence[int], c: Cost) -> float:
         pairs = float(sum(n * (n + 1) // 2 for n in batch_lens))
     if c.token_quantum > 1:
         tokens = float(math.ceil(tokens / c.token_quantum) * c.token_quantum)
-    return c.t_batch + c.t_token * tokens + c.t_row * float(B * P) + c.t_pair * pairs
+    return c.t_batch + token_seconds(tokens, c) + c.t_row * float(B * P) + c.t_pair * pairs
 
 
 def fifo_batches(lens: Sequence[int], max_batch: int) -> List[List[int]]:

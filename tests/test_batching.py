@@ -13,7 +13,14 @@ from oracle import Cost
 
 
 def _native_cost(c: Cost) -> ee.BatchCost:
-    return ee.BatchCost(c.t_batch, c.t_token, c.t_row, c.t_pair, c.token_quantum, 1 if c.padded_compute else 0)
+    n = ee.BatchCost(c.t_batch, c.t_token, c.t_row, c.t_pair, c.token_quantum, 1 if c.padded_compute else 0)
+    if c.token_table:
+        n.set_table(c.token_table)
+    return n
+
+
+# a concave measured-looking table: seconds for 1..16 K tokens
+_TABLE = tuple(0.03 + 0.00012 * 1024 * (k + 1) * (1.0 + 0.3 / (k + 1)) for k in range(16))
 
 
 COSTS = [
@@ -21,6 +28,9 @@ COSTS = [
     Cost(t_batch=0.05, t_token=1.3e-4, t_row=1.2e-8, t_pair=2.0e-10, padded_compute=True),
     Cost(t_batch=1.0, t_token=0.01, t_row=0.001),
     Cost(t_batch=0.0, t_token=1.0, t_row=0.25, t_pair=1e-3, token_quantum=7),
+    Cost(t_row=5e-9, token_quantum=1024, token_table=_TABLE),
+    Cost(token_quantum=1024, padded_compute=True, token_table=_TABLE[:3]),
+    Cost(t_batch=0.01, token_quantum=64, token_table=(0.5,)),
 ]
 
 
@@ -74,5 +84,7 @@ def test_planner_errors():
         ee.ee_plan_dynamic([300, 2], 4, c, max_tokens=256)    # longer than the token limit
     with pytest.raises(ee.EEError):
         ee.ee_plan_dynamic([3, 2], 4, ee.BatchCost(-1.0, 0, 0, 0, 1, 0))
+    with pytest.raises(ee.EEError):
+        ee.ee_plan_dynamic([3, 2], 4, ee.BatchCost(0, 0, 0, 0, 1, 0).set_table([0.1, -0.2]))
     assert ee.ee_plan_dynamic([], 4, c) == ([], 0.0)
     assert ee.ee_plan_fifo([], 4) == []

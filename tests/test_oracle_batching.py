@@ -107,6 +107,35 @@ def test_equal_lengths_closed_form():
     assert oracle.padded_rows(batches, [L] * (cap * k)) == cap * k * L
 
 
+def test_token_table_closed_forms():
+    # entry k: (k+1) * 100 tokens; inside the table the entry itself, past it the
+    # line through the last two entries, below one quantum nothing
+    c = Cost(token_quantum=100, token_table=(1.0, 1.5, 1.8))
+    assert oracle.token_seconds(100, c) == 1.0 and oracle.token_seconds(300, c) == 1.8
+    assert oracle.token_seconds(500, c) == pytest.approx(1.8 + 2 * 0.3)
+    assert oracle.batch_cost([150, 40], c) == 1.5                 # 190 tokens round up to 200
+    one = Cost(token_quantum=10, token_table=(2.0,))
+    assert oracle.token_seconds(30, one) == 6.0
+    # a table that is exactly linear reproduces the linear model
+    lin = Cost(t_row=0.01, token_quantum=64, token_table=tuple(0.002 * 64 * (k + 1) for k in range(8)))
+    ref = Cost(t_row=0.01, t_token=0.002, token_quantum=64)
+    for lens in ([5, 60, 200], [64] * 8, [1]):
+        assert oracle.batch_cost(lens, lin) == pytest.approx(oracle.batch_cost(lens, ref), rel=1e-12)
+
+
+def test_dp_with_a_table_is_the_least_cost_split():
+    rng = random.Random(3)
+    c = Cost(t_row=0.001, token_quantum=16, token_table=(1.0, 1.2, 1.3, 1.35, 1.4))
+    for _ in range(30):
+        n = rng.randint(1, 8)
+        lens = [rng.randint(1, 40) for _ in range(n)]
+        cap = rng.randint(1, 4)
+        order = oracle.length_order(lens)
+        best = min(sum(oracle.batch_cost([lens[k] for k in order[lo:hi]], c) for lo, hi in runs)
+                   for runs in _compositions(n, cap))
+        assert oracle.dp_runs(lens, cap, c)[1] == pytest.approx(best, rel=1e-12)
+
+
 def test_fifo_and_padded_rows():
     lens = [3, 10, 2, 2, 7]
     b = oracle.fifo_batches(lens, 2)

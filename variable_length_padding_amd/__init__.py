@@ -67,9 +67,17 @@ class KernelStat(C.Structure):
 
 
 class BatchCost(C.Structure):
-    """Per-batch cost model of the batch planners (seconds)."""
+    """Per-batch cost model of the batch planners (seconds).  A token table is
+    kept alive by the structure (`_table`)."""
     _fields_ = [("t_batch", C.c_double), ("t_token", C.c_double), ("t_row", C.c_double), ("t_pair", C.c_double),
-                ("token_quantum", C.c_int32), ("padded_compute", C.c_int32)]
+                ("token_quantum", C.c_int32), ("padded_compute", C.c_int32),
+                ("token_table", C.POINTER(C.c_double)), ("token_table_len", C.c_int32)]
+
+    def set_table(self, seconds: Sequence[float]):
+        self._table = (C.c_double * max(1, len(seconds)))(*[float(v) for v in seconds])
+        self.token_table = self._table
+        self.token_table_len = len(seconds)
+        return self
 
 
 _VP, _I32, _I64, _SZ = C.c_void_p, C.c_int32, C.c_int64, C.c_size_t

@@ -39,8 +39,24 @@ double run_cost(const ee_batch_cost& c, const Run& r) {
     tok = (double)r.tokens;
     pairs = r.pairs;
   }
-  if (c.token_quantum > 1) tok = std::ceil(tok / (double)c.token_quantum) * (double)c.token_quantum;
-  return c.t_batch + c.t_token * tok + c.t_row * (double)(r.B * r.P) + c.t_pair * pairs;
+  const double q = c.token_quantum > 1 ? (double)c.token_quantum : 1.0;
+  if (c.token_quantum > 1) tok = std::ceil(tok / q) * q;
+  double s;
+  if (c.token_table && c.token_table_len >= 1) {
+    const int64_t k = (int64_t)(tok / q) - 1;  // entry of this token count
+    const int64_t last = c.token_table_len - 1;
+    if (k < 0)
+      s = 0.0;
+    else if (k <= last)
+      s = c.token_table[k];
+    else if (last >= 1)
+      s = c.token_table[last] + (double)(k - last) * (c.token_table[last] - c.token_table[last - 1]);
+    else
+      s = c.token_table[0] * (double)(k + 1);
+  } else {
+    s = c.t_token * tok;
+  }
+  return c.t_batch + s + c.t_row * (double)(r.B * r.P) + c.t_pair * pairs;
 }
 
 ee_status check_lens(const int32_t* lens, int32_t n) {
@@ -53,8 +69,11 @@ ee_status check_lens(const int32_t* lens, int32_t n) {
 
 ee_status check_cost(const ee_batch_cost* c) {
   if (!c) return ee::set_error(EE_ERR_INVALID_ARG, "cost is NULL");
-  if (!(c->t_batch >= 0 && c->t_token >= 0 && c->t_row >= 0 && c->t_pair >= 0) || c->token_quantum < 0)
+  if (!(c->t_batch >= 0 && c->t_token >= 0 && c->t_row >= 0 && c->t_pair >= 0) || c->token_quantum < 0 ||
+      c->token_table_len < 0)
     return ee::set_error(EE_ERR_INVALID_ARG, "cost coefficients must be finite and >= 0");
+  for (int32_t k = 0; c->token_table && k < c->token_table_len; ++k)
+    if (!(c->token_table[k] >= 0)) return ee::set_error(EE_ERR_INVALID_ARG, "token_table entries must be >= 0");
   return EE_OK;
 }
 

@@ -128,6 +128,30 @@ def request_stream(w: Workload, seed: int) -> List[List[int]]:
     return [lens[i:i + w.batch] for i in range(0, len(lens), w.batch)]
 
 
+REQUEST_STREAM_BASE = 1 << 20
+
+
+def request_activations(w: Workload, seed: int, lens: List[int], device="cpu") -> List[torch.Tensor]:
+    """Activations of each request of a stream, [len_i, hidden] ~ N(0, x_std^2)
+    in the workload dtype, request i from stream REQUEST_STREAM_BASE + i, so a
+    request carries the same values whichever batch it lands in."""
+    out = []
+    for i, n in enumerate(lens):
+        g = stream_generator(seed, REQUEST_STREAM_BASE + i, device)
+        x = torch.randn((n, w.hidden), generator=g, device=device, dtype=torch.float32)
+        out.append(x.mul_(w.x_std).to(w.torch_dtype))
+    return out
+
+
+def pad_batch(rows: List[torch.Tensor], pad_len: Optional[int] = None) -> torch.Tensor:
+    """Right-pads per-request [len_i, hidden] rows into [B, P, hidden] (pads zero)."""
+    P = pad_len if pad_len is not None else max(r.shape[0] for r in rows)
+    x = torch.zeros((len(rows), P, rows[0].shape[1]), dtype=rows[0].dtype, device=rows[0].device)
+    for b, r in enumerate(rows):
+        x[b, :r.shape[0]] = r
+    return x
+
+
 def activations(w: Workload, seed: int, batch: int, pad_len: int, lens: Optional[List[int]] = None,
                 device="cpu", pad_fill: str = "random", stream: int = 1) -> torch.Tensor:
     """Padded activations [batch, pad_len, hidden] ~ N(0, x_std^2), stored in the
