@@ -55,6 +55,7 @@ extern "C" {
 #endif
 
 #define EE_MAX_BATCH 512
+#define EE_MAX_EXTEND_BATCH 256
 
 typedef enum {
   EE_OK = 0,
@@ -264,6 +265,46 @@ EE_API ee_status ee_profile_enable(int32_t on);
 /* Waits for the recorded events, writes up to `capacity` per-site totals into
  * `out` (host), sets *count, and clears the record. */
 EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* count);
+
+/* ---- Incremental decoding with a packed KV cache ----
+ *
+ * Generation (the README's "Latency" section times a GPT-3 generation
+ * service; the EET page reports decoder-layer speedups): each new token of a
+ * sequence attends to all earlier tokens of that sequence through their
+ * cached keys and values.  One call runs an "extend" step of a layer stack:
+ * sequence b brings new_len[b] >= 0 new tokens at positions
+ * ctx_len[b] .. ctx_len[b] + new_len[b] - 1, after ctx_len[b] tokens whose
+ * keys and values are already cached.  A prefill is an extend from
+ * ctx_len = 0; a decode step brings one token per sequence.  Only the new
+ * tokens are computed (the padding-free layout of the forward above).
+ *
+ * KV cache (caller-owned device memory, ee_kv_cache_bytes): for each layer
+ * l, [2 (k | v)][n_heads][capacity][head_dim] elements of the layer dtype,
+ * layers one after another.  Sequence b owns the slots
+ * slot_base[b] .. slot_base[b] + ctx_len[b] + new_len[b] - 1, so sequences
+ * take only the slots they use.  The call writes the new tokens' keys and
+ * values of every layer into their slots and reads the cached ones; the
+ * caller advances ctx_len by new_len afterwards.
+ *
+ * Arguments: layers as for ee_stack_forward (all GPT pre-LN, same
+ * descriptor; the descriptor's attention form does not apply here).
+ * d_x: device [T_new, hidden], the new tokens packed sequence by sequence
+ * (T_new = sum new_len); d_y: device [T_new, hidden] output; new_len,
+ * ctx_len, slot_base: host [batch], batch <= EE_MAX_EXTEND_BATCH, not kept
+ * after the call.  Errors: EE_ERR_INVALID_ARG for negative counts, a slot
+ * range outside [0, capacity), overlapping slot ranges of sequences with
+ * tokens, overlapping buffers, or a post-LN descriptor; EE_ERR_UNSUPPORTED
+ * for head_dim outside {16, 32, 64, 128} or more than
+ * ee_extend_max_positions() positions in one sequence; EE_ERR_WORKSPACE
+ * when ws_bytes < ee_extend_workspace_size(layer, batch, T_new). */
+EE_API ee_status ee_kv_cache_bytes(const ee_layer* layer, int32_t n_layers, int64_t capacity, size_t* bytes);
+EE_API ee_status ee_extend_workspace_size(const ee_layer* layer, int32_t batch, int64_t max_new_tokens,
+                                          size_t* bytes);
+EE_API int32_t ee_extend_max_positions(void);
+EE_API ee_status ee_stack_extend(ee_layer* const* layers, int32_t n_layers, const void* d_x,
+                                 const int32_t* new_len, const int32_t* ctx_len, const int32_t* slot_base,
+                                 int32_t batch, void* d_cache, int64_t capacity, void* d_y, void* ws,
+                                 size_t ws_bytes, void* stream);
 
 /* ---- Batch planning over a request queue (host only; no device work) ----
  *

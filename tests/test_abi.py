@@ -148,3 +148,43 @@ def test_op_entry_points_validate():
     assert lib.ee_compute_offsets((C.c_int32 * 2)(1, 9), 2, 8, 1 << 30, 1 << 31, 1 << 32, C.byref(total), None) == 1
     assert lib.ee_compute_offsets(lens, 2, 8, None, 1 << 31, 1 << 32, C.byref(total), None) == 1
     assert lib.ee_bias_gelu(1 << 30, None, 4, 64, ee.F16, 0, 1 << 31, None) == 1
+
+
+def test_extend_validation_happens_before_device_work():
+    lib = ee.lib()
+    st, h = _create(_desc(), _weights())
+    assert st == 0
+    try:
+        arr = (C.c_void_p * 1)(h.value)
+
+        def I(*v):
+            return (C.c_int32 * len(v))(*v)
+        n = C.c_size_t(0)
+        assert lib.ee_extend_workspace_size(h, 2, 8, C.byref(n)) == 0 and n.value > 0
+        cb = C.c_size_t(0)
+        assert lib.ee_kv_cache_bytes(h, 3, 10, C.byref(cb)) == 0
+        assert cb.value == 3 * 2 * 4 * 10 * 16 * 4          # layers x (k|v) x heads x slots x head_dim x fp32
+        assert lib.ee_extend_max_positions() >= 4096
+        x, y, ws, cache = 1 << 30, 1 << 31, 1 << 32, 1 << 33
+        # a sequence's slots past the capacity (base 4 + ctx 5 + new 1 > 8)
+        assert lib.ee_stack_extend(arr, 1, x, I(3, 1), I(0, 5), I(0, 4), 2, cache, 8, y, ws, n.value, None) == 1
+        # overlapping slot ranges ([0, 3) and [2, 3))
+        assert lib.ee_stack_extend(arr, 1, x, I(3, 1), I(0, 0), I(0, 2), 2, cache, 64, y, ws, n.value, None) == 1
+        # an idle sequence's cached range still counts
+        assert lib.ee_stack_extend(arr, 1, x, I(1, 0), I(0, 6), I(0, 0), 2, cache, 64, y, ws, n.value, None) == 1
+        # negative counts, batch above the limit, workspace too small
+        assert lib.ee_stack_extend(arr, 1, x, I(-1, 1), I(0, 0), I(0, 8), 2, cache, 64, y, ws, n.value, None) == 1
+        big = (C.c_int32 * 257)(*([0] * 257))
+        assert lib.ee_stack_extend(arr, 1, x, big, big, big, 257, cache, 64, y, ws, n.value, None) == 1
+        assert lib.ee_stack_extend(arr, 1, x, I(3, 1), I(0, 0), I(0, 8), 2, cache, 64, y, ws, 64, None) == 3
+        # the cache overlapping the output
+        assert lib.ee_stack_extend(arr, 1, x, I(3, 1), I(0, 0), I(0, 8), 2, y + 64, 64, y, ws, n.value, None) == 1
+        # nothing new: a no-op
+        assert lib.ee_stack_extend(arr, 1, x, I(0, 0), I(2, 3), I(0, 8), 2, cache, 64, y, ws, n.value, None) == 0
+        # post-LN encoder layers are not causal
+        st2, h2 = _create(_desc(block=ee.BLOCK_BERT_POSTLN), _weights())
+        arr2 = (C.c_void_p * 1)(h2.value)
+        assert lib.ee_stack_extend(arr2, 1, x, I(3, 1), I(0, 0), I(0, 8), 2, cache, 64, y, ws, n.value, None) == 1
+        lib.ee_layer_destroy(h2)
+    finally:
+        lib.ee_layer_destroy(h)

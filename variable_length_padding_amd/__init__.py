@@ -20,6 +20,8 @@ __all__ = [
     "ee_transpose_padding_remove_heads", "ee_add_bias_residual_layernorm",
     "BLOCK_GPT_PRELN", "BLOCK_BERT_POSTLN", "ATTN_VARLEN", "ATTN_PADDED",
     "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_collect",
+    "ee_kv_cache_bytes", "ee_extend_workspace_size", "ee_extend_max_positions", "ee_stack_extend",
+    "MAX_EXTEND_BATCH",
     "BatchCost", "ee_batch_cost_eval", "ee_plan_fifo", "ee_plan_dynamic", "batches_of",
     "EXPORTED_SYMBOLS", "lib_path",
 ]
@@ -30,6 +32,7 @@ EPI_NONE, EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3
 BLOCK_GPT_PRELN, BLOCK_BERT_POSTLN = 0, 1
 ATTN_VARLEN, ATTN_PADDED = 0, 1
 MAX_BATCH = 512
+MAX_EXTEND_BATCH = 256
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -111,6 +114,11 @@ _SIGS = {
                                                  _VP]),
     "ee_profile_enable": (C.c_int, [_I32]),
     "ee_profile_collect": (C.c_int, [C.POINTER(KernelStat), _I32, _PI32]),
+    "ee_kv_cache_bytes": (C.c_int, [_VP, _I32, _I64, C.POINTER(_SZ)]),
+    "ee_extend_workspace_size": (C.c_int, [_VP, _I32, _I64, C.POINTER(_SZ)]),
+    "ee_extend_max_positions": (C.c_int32, []),
+    "ee_stack_extend": (C.c_int, [C.POINTER(_VP), _I32, _VP, _PI32, _PI32, _PI32, _I32, _VP, _I64, _VP, _VP, _SZ,
+                                  _VP]),
     "ee_batch_cost_eval": (C.c_int, [_PI32, _I32, C.POINTER(BatchCost), C.POINTER(C.c_double)]),
     "ee_plan_fifo": (C.c_int, [_PI32, _I32, _I32, _PI32, _PI32]),
     "ee_plan_dynamic": (C.c_int, [_PI32, C.POINTER(C.c_double), _I32, _I32, _I64, C.POINTER(BatchCost), _PI32,
@@ -300,6 +308,37 @@ class Layer:
             self.close()
         except Exception:
             pass
+
+
+def ee_kv_cache_bytes(layer: Layer, n_layers: int, capacity: int) -> int:
+    """Bytes of a KV cache of `capacity` slots per layer for n_layers layers."""
+    n = C.c_size_t(0)
+    _check(lib().ee_kv_cache_bytes(layer.handle, n_layers, capacity, C.byref(n)), "ee_kv_cache_bytes")
+    return n.value
+
+
+def ee_extend_workspace_size(layer: Layer, batch: int, max_new_tokens: int) -> int:
+    n = C.c_size_t(0)
+    _check(lib().ee_extend_workspace_size(layer.handle, batch, max_new_tokens, C.byref(n)),
+           "ee_extend_workspace_size")
+    return n.value
+
+
+def ee_extend_max_positions() -> int:
+    return int(lib().ee_extend_max_positions())
+
+
+def ee_stack_extend(layers: List[Layer], x, new_len: Sequence[int], ctx_len: Sequence[int],
+                    slot_base: Sequence[int], cache, capacity: int, y, workspace, stream=None):
+    """One extend step: x/y device [sum(new_len), hidden]; cache device buffer of
+    ee_kv_cache_bytes(layers[0], len(layers), capacity) bytes."""
+    B = len(new_len)
+    if len(ctx_len) != B or len(slot_base) != B:
+        raise ValueError("new_len, ctx_len and slot_base must have one entry per sequence")
+    arr = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
+    _check(lib().ee_stack_extend(arr, len(layers), _ptr(x), _lens(new_len), _lens(ctx_len), _lens(slot_base), B,
+                                 _ptr(cache), int(capacity), _ptr(y), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)), "ee_stack_extend")
 
 
 def ee_stack_forward(layers: List[Layer], x, lens: Sequence[int], y, workspace, stream=None):

@@ -254,8 +254,9 @@ ee_status attend(const ee_layer_desc& d, void* ws, const Plan& p, const void* qk
 }
 
 // The packed layer on T rows held in ws.x; the output replaces ws.x.
-ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, int32_t B, int32_t P, int32_t max_len,
-                       hipStream_t s) {
+// attn(qkv, o, causal) runs the attention step from the packed qkv rows.
+template <class Attn>
+ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, hipStream_t s, Attn&& attn) {
   const ee_layer_desc& d = L->desc;
   const ee_layer_weights& w = L->w;
   const int H = d.hidden, Hp = d.n_heads * d.head_dim, F = d.ffn;
@@ -276,7 +277,7 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, in
   if (d.block == EE_BLOCK_GPT_PRELN) {
     EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
     EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
-    EE_TRY(attend(d, ws, p, big, o, B, P, max_len, true, s));
+    EE_TRY(attn(big, o, true));
     EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s));
     EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
     EE_TRY(fc1(ln));
@@ -285,7 +286,7 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, in
   }
   // post-LN encoder: GEMM, then bias + residual + LayerNorm in one pass
   EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
-  EE_TRY(attend(d, ws, p, big, o, B, P, max_len, false, s));
+  EE_TRY(attn(big, o, false));
   EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, EE_EPI_NONE, d.gelu, ln, s));
   EE_LAUNCH("add_ln1", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_out, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, h, s));
@@ -327,9 +328,132 @@ ee_status stack_impl(ee_layer* const* layers, int32_t n_layers, const void* x_pa
   EE_TRY(offsets_from_host(seq_lens, B, P, cu, tsrc, p2p, s));
   if (T > 0) {
     EE_LAUNCH("remove", s, launch_remove(x_padded, tsrc, T, row_bytes, at(ws, p.x), s));
-    for (int32_t i = 0; i < n_layers; ++i) EE_TRY(packed_layer(layers[i], ws, p, T, B, P, max_len, s));
+    for (int32_t i = 0; i < n_layers; ++i)
+      EE_TRY(packed_layer(layers[i], ws, p, T, s, [&](const void* qkv, void* o, bool causal) {
+        return attend(d, ws, p, qkv, o, B, P, max_len, causal, s);
+      }));
   }
   EE_LAUNCH("rebuild", s, launch_rebuild(at(ws, p.x), p2p, (int64_t)B * P, row_bytes, y_padded, s));
+  return EE_OK;
+}
+
+// ---------------------------------------------------------------- extend (incremental decoding)
+Plan plan_extend(const ee_layer_desc& d, int32_t B, int64_t T) {
+  Plan p{};
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off += align256(n);
+    return o;
+  };
+  const size_t s = dtype_size(d.dtype), t = (size_t)T;
+  const size_t H = d.hidden, Hp = (size_t)d.n_heads * d.head_dim, F = d.ffn;
+  p.cu = take(4 * (size_t)(B + 1));
+  p.x = take(t * H * s);
+  p.ln = take(t * H * s);
+  p.big = take(t * std::max(3 * Hp, F) * s);
+  p.o = take(t * Hp * s);
+  p.h = take(t * H * s);
+  p.total = off;
+  return p;
+}
+
+size_t cache_layer_bytes(const ee_layer_desc& d, int64_t capacity) {
+  return 2 * (size_t)d.n_heads * (size_t)capacity * (size_t)d.head_dim * dtype_size(d.dtype);
+}
+
+ee_status extend_impl(ee_layer* const* layers, int32_t n_layers, const void* d_x, const int32_t* new_len,
+                      const int32_t* ctx_len, const int32_t* slot_base, int32_t B, void* d_cache, int64_t capacity,
+                      void* d_y, void* ws, size_t ws_bytes, void* stream) {
+  if (!layers || n_layers < 1) return fail(EE_ERR_INVALID_ARG, "need at least one layer");
+  for (int32_t i = 0; i < n_layers; ++i) {
+    if (!layers[i]) return fail(EE_ERR_INVALID_ARG, "layers[%d] is NULL", i);
+    if (!desc_equal(layers[i]->desc, layers[0]->desc))
+      return fail(EE_ERR_INVALID_ARG, "layers[%d] has a different descriptor from layers[0]", i);
+  }
+  const ee_layer_desc& d = layers[0]->desc;
+  if (d.block != EE_BLOCK_GPT_PRELN)
+    return fail(EE_ERR_INVALID_ARG, "incremental decoding needs the causal (GPT pre-LN) block");
+  if (!cache_attention_ok(d.head_dim)) return fail(EE_ERR_UNSUPPORTED, "head_dim %d unsupported", d.head_dim);
+  if (B < 1 || B > EE_MAX_EXTEND_BATCH) return fail(EE_ERR_INVALID_ARG, "batch %d not in [1, %d]", B, EE_MAX_EXTEND_BATCH);
+  if (!new_len || !ctx_len || !slot_base) return fail(EE_ERR_INVALID_ARG, "new_len, ctx_len, slot_base are required");
+  if (capacity < 1 || capacity > INT32_MAX) return fail(EE_ERR_INVALID_ARG, "capacity must be in [1, 2^31)");
+  // every slot written or read lies in [0, capacity), and sequences with
+  // tokens own disjoint slot ranges
+  int64_t T = 0;
+  int32_t max_pos = 0;
+  std::vector<std::pair<int64_t, int64_t>> ranges;
+  for (int32_t b = 0; b < B; ++b) {
+    if (new_len[b] < 0 || ctx_len[b] < 0 || slot_base[b] < 0)
+      return fail(EE_ERR_INVALID_ARG, "negative new_len, ctx_len or slot_base at %d", b);
+    const int64_t used = (int64_t)ctx_len[b] + new_len[b];
+    if ((int64_t)slot_base[b] + used > capacity)
+      return fail(EE_ERR_INVALID_ARG, "sequence %d needs slots up to %lld, capacity %lld", b,
+                  (long long)(slot_base[b] + used), (long long)capacity);
+    if (new_len[b] > 0) {
+      if (used > ee_extend_max_positions())
+        return fail(EE_ERR_UNSUPPORTED, "sequence %d reaches %lld positions, above %d", b, (long long)used,
+                    ee_extend_max_positions());
+      max_pos = std::max<int32_t>(max_pos, (int32_t)used);
+    }
+    if (used > 0) ranges.emplace_back(slot_base[b], slot_base[b] + used);
+    T += new_len[b];
+  }
+  std::sort(ranges.begin(), ranges.end());
+  for (size_t i = 1; i < ranges.size(); ++i)
+    if (ranges[i].first < ranges[i - 1].second) return fail(EE_ERR_INVALID_ARG, "sequences share cache slots");
+  if (T == 0) return EE_OK;
+  EE_TRY(check_ptr(d_x, "d_x"));
+  EE_TRY(check_ptr(d_y, "d_y"));
+  EE_TRY(check_ptr(d_cache, "d_cache"));
+  EE_TRY(check_ptr(ws, "workspace"));
+  const Plan p = plan_extend(d, B, T);
+  if (ws_bytes < p.total)
+    return fail(EE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu for %lld new tokens", ws_bytes, p.total,
+                (long long)T);
+  const size_t s_el = dtype_size(d.dtype);
+  const size_t io = (size_t)T * d.hidden * s_el, cl = cache_layer_bytes(d, capacity);
+  const size_t cache_bytes = cl * (size_t)n_layers;
+  if (overlap(d_x, io, d_y, io)) return fail(EE_ERR_INVALID_ARG, "d_x and d_y overlap");
+  if (overlap(ws, p.total, d_x, io) || overlap(ws, p.total, d_y, io) || overlap(ws, p.total, d_cache, cache_bytes))
+    return fail(EE_ERR_INVALID_ARG, "workspace overlaps d_x, d_y or the cache");
+  if (overlap(d_cache, cache_bytes, d_x, io) || overlap(d_cache, cache_bytes, d_y, io))
+    return fail(EE_ERR_INVALID_ARG, "the cache overlaps d_x or d_y");
+
+  ExtendArg arg;
+  std::memset(&arg, 0, sizeof arg);
+  bool prefill = true;  // no sequence with new tokens has cached ones
+  int32_t max_new = 0;
+  for (int32_t b = 0; b < B; ++b) {
+    arg.new_len[b] = new_len[b];
+    arg.ctx_len[b] = ctx_len[b];
+    arg.slot_base[b] = slot_base[b];
+    if (new_len[b] > 0 && ctx_len[b] > 0) prefill = false;
+    max_new = std::max(max_new, new_len[b]);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t* cu = reinterpret_cast<int32_t*>(at(ws, p.cu));
+  EE_LAUNCH("extend_cu", s, launch_extend_cu(arg, B, cu, s));
+  const hipError_t e_in = hipMemcpyAsync(at(ws, p.x), d_x, io, hipMemcpyDeviceToDevice, s);
+  if (e_in != hipSuccess) return hip_fail(e_in, "copy in");
+  const int nh = d.n_heads, hd = d.head_dim;
+  const size_t kv_half = (size_t)nh * (size_t)capacity * hd * s_el;  // the k part of a layer's cache
+  for (int32_t l = 0; l < n_layers; ++l) {
+    char* layer_cache = static_cast<char*>(d_cache) + cl * (size_t)l;
+    EE_TRY(packed_layer(layers[l], ws, p, T, s, [&](const void* qkv, void* o, bool) -> ee_status {
+      EE_LAUNCH("append_kv", s,
+                launch_append_kv(qkv, arg, cu, B, T, nh, hd * (int)s_el, capacity, layer_cache, s));
+      if (prefill) {  // attention among the new tokens only: the packed varlen kernel
+        EE_LAUNCH("attention", s, launch_attention(d.dtype, qkv, cu, B, max_new, nh, hd, true, o, s));
+      } else {
+        EE_LAUNCH("cache_attention", s, launch_cache_attention(d.dtype, qkv, arg, cu, B, nh, hd, max_pos, capacity,
+                                                               layer_cache, layer_cache + kv_half, o, s));
+      }
+      return EE_OK;
+    }));
+  }
+  const hipError_t e_out = hipMemcpyAsync(d_y, at(ws, p.x), io, hipMemcpyDeviceToDevice, s);
+  if (e_out != hipSuccess) return hip_fail(e_out, "copy out");
   return EE_OK;
 }
 
@@ -400,6 +524,30 @@ ee_status ee_stack_forward(ee_layer* const* layers, int32_t n_layers, const void
                            int32_t batch, int32_t pad_len, void* y_padded, void* workspace, size_t ws_bytes,
                            void* stream) {
   return stack_impl(layers, n_layers, x_padded, seq_lens, batch, pad_len, y_padded, workspace, ws_bytes, stream);
+}
+
+ee_status ee_kv_cache_bytes(const ee_layer* layer, int32_t n_layers, int64_t capacity, size_t* bytes) {
+  if (!layer || !bytes || n_layers < 1 || capacity < 1 || capacity > INT32_MAX)
+    return fail(EE_ERR_INVALID_ARG, "need a layer, n_layers >= 1, capacity in [1, 2^31) and an output");
+  *bytes = cache_layer_bytes(layer->desc, capacity) * (size_t)n_layers;
+  return EE_OK;
+}
+
+ee_status ee_extend_workspace_size(const ee_layer* layer, int32_t batch, int64_t max_new_tokens, size_t* bytes) {
+  if (!layer || !bytes || batch < 1 || batch > EE_MAX_EXTEND_BATCH || max_new_tokens < 0)
+    return fail(EE_ERR_INVALID_ARG, "need a layer, batch in [1, %d], max_new_tokens >= 0 and an output",
+                EE_MAX_EXTEND_BATCH);
+  *bytes = plan_extend(layer->desc, batch, max_new_tokens).total;
+  return EE_OK;
+}
+
+int32_t ee_extend_max_positions(void) { return cache_attention_max_positions(); }
+
+ee_status ee_stack_extend(ee_layer* const* layers, int32_t n_layers, const void* d_x, const int32_t* new_len,
+                          const int32_t* ctx_len, const int32_t* slot_base, int32_t batch, void* d_cache,
+                          int64_t capacity, void* d_y, void* ws, size_t ws_bytes, void* stream) {
+  return extend_impl(layers, n_layers, d_x, new_len, ctx_len, slot_base, batch, d_cache, capacity, d_y, ws, ws_bytes,
+                     stream);
 }
 
 ee_status ee_compute_offsets(const int32_t* seq_lens, int32_t batch, int32_t pad_len, int32_t* d_cu,

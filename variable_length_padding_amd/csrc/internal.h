@@ -37,6 +37,21 @@ hipError_t launch_rebuild_heads(const void* packed, const int32_t* cu, int B, in
 hipError_t launch_remove_heads(const void* heads, const int32_t* cu, int B, int nh, int P, int head_bytes,
                                void* packed, hipStream_t s);
 
+// ---- decode.hip ----  (extend step: new tokens after cached ones; B <= EE_MAX_EXTEND_BATCH)
+struct ExtendArg {
+  int32_t new_len[EE_MAX_EXTEND_BATCH];
+  int32_t ctx_len[EE_MAX_EXTEND_BATCH];
+  int32_t slot_base[EE_MAX_EXTEND_BATCH];
+};
+bool cache_attention_ok(int head_dim);
+int cache_attention_max_positions();
+hipError_t launch_extend_cu(const ExtendArg& arg, int B, int32_t* cu, hipStream_t s);
+hipError_t launch_append_kv(const void* qkv, const ExtendArg& arg, const int32_t* cu, int B, int64_t T, int nh,
+                            int head_bytes, int64_t capacity, void* cache, hipStream_t s);
+hipError_t launch_cache_attention(ee_dtype dt, const void* qkv, const ExtendArg& arg, const int32_t* cu, int B,
+                                  int nh, int hd, int max_pos, int64_t capacity, const void* kc, const void* vc,
+                                  void* o, hipStream_t s);
+
 // ---- layernorm.hip ----
 int layernorm_max_hidden(ee_dtype dt);
 hipError_t launch_layernorm(ee_dtype dt, const void* x, const void* g, const void* b, int64_t rows, int H,

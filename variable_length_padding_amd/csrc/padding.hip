@@ -12,7 +12,6 @@ namespace ee {
 namespace {
 
 constexpr int kCopyThreads = 256;
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));  // 16 bytes
 
 __device__ __forceinline__ void copy_row(const u32x4* __restrict__ s, u32x4* __restrict__ d, int vpr) {
   int c = threadIdx.x;
