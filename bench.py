@@ -62,6 +62,9 @@ def _parse():
     ap.add_argument("--no-pack", action="store_true",
                     help="padding kept: every one of the B*P rows runs through the layers (the redundant "
                          "computation the method removes); value still counts valid tokens only")
+    ap.add_argument("--decode-steps", type=int, default=0,
+                    help="incremental decoding: prefill the batch's prompts, then time this many decode steps "
+                         "(one new token per sequence each) through ee_stack_extend")
     ap.add_argument("--max-batch", type=int, default=0,
                     help="request-stream workload: batch size cap of both planners (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -295,6 +298,91 @@ def _stream_bench(args):
     print(json.dumps(out), flush=True)
 
 
+def _decode_bench(args):
+    """Incremental decoding: the workload's batch as prompts (prefill, untimed),
+    then --decode-steps steps of one new token per sequence, timed."""
+    import torch
+
+    import variable_length_padding_amd as ee
+    import workloads
+
+    dev = torch.device("cuda:0")
+    w = workloads.get(args.workload)
+    prompts = workloads.lengths(w, args.seed)
+    B, L, N = len(prompts), w.layers, args.decode_steps
+    s_el = w.elem_bytes
+    H, Hp, F = w.hidden, w.inner, w.ffn
+    params = [workloads.layer_params(w, args.seed, l, device=dev) for l in range(L)]
+    dt = ee.F16 if w.dtype == "f16" else ee.F32
+    layers = [ee.Layer(H, w.n_heads, w.head_dim, F, p, dtype=dt) for p in params]
+    slot_base, cap = [], 0
+    for n in prompts:
+        slot_base.append(cap)
+        cap += n + N + args.warmup
+    cache = torch.empty(ee.ee_kv_cache_bytes(layers[0], L, cap), dtype=torch.uint8, device=dev)
+    T0 = sum(prompts)
+    ws = torch.empty(ee.ee_extend_workspace_size(layers[0], B, max(T0, B)), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    g = workloads.stream_generator(args.seed, workloads.REQUEST_STREAM_BASE - 1, dev)
+    x0 = (w.x_std * torch.randn(T0, H, generator=g, device=dev)).to(w.torch_dtype)
+    y0 = torch.empty_like(x0)
+    xs = (w.x_std * torch.randn(N + args.warmup, B, H, generator=g, device=dev)).to(w.torch_dtype)
+    ys = torch.empty_like(xs)
+    _log(f"decode {w.name}: {B} sequences, prompts T={T0}, {L} layers, {N} timed steps; cache "
+         f"{cache.numel() / 1e9:.2f} GB for {cap} slots per layer")
+    ee.ee_stack_extend(layers, x0, prompts, [0] * B, slot_base, cache, cap, y0, ws, stream)
+    ctx = list(prompts)
+    for i in range(args.warmup):
+        ee.ee_stack_extend(layers, xs[i], [1] * B, ctx, slot_base, cache, cap, ys[i], ws, stream)
+        ctx = [c + 1 for c in ctx]
+    torch.cuda.synchronize()
+    ctx_start = list(ctx)
+    ee.ee_profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.warmup, args.warmup + N):
+        ee.ee_stack_extend(layers, xs[i], [1] * B, ctx, slot_base, cache, cap, ys[i], ws, stream)
+        ctx = [c + 1 for c in ctx]
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ee.ee_profile_enable(False)
+    st = ee.ee_profile_collect()
+    ms_step = e0.elapsed_time(e1) / N
+    value = B * L / (ms_step / 1e3)
+    # bytes a decode step must move: every layer's weights, the cached keys and
+    # values it attends over, and the new tokens' rows (small)
+    w_bytes = (H * 3 * Hp + Hp * H + 2 * H * F + 3 * Hp + 2 * H + F + 4 * H) * s_el
+    mid_ctx = [c + N // 2 for c in ctx_start]          # context length half-way through the timed steps
+    kv_bytes = sum(2 * (c + 1) * Hp * s_el for c in mid_ctx)
+    step_bytes = L * (w_bytes + kv_bytes)
+    kernels = {}
+    for site, v in st.items():
+        kernels[site] = {"launches_per_step": v["launches"] / N, "avg_ms": round(v["total_ms"] / v["launches"], 5),
+                         "share": round(v["total_ms"] / (ms_step * N), 4)}
+    fc1_ms = st["gemm_fc1"]["total_ms"] / st["gemm_fc1"]["launches"]
+    fc1_bytes = (H * F + B * H + B * F) * s_el
+    achieved = fc1_bytes / (fc1_ms * 1e-3) / 1e9
+    _log(f"decode: {ms_step:.3f} ms per step, {value:.0f} tokens/s per layer, "
+         f"{step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s of weights + cache")
+    out = {
+        "metric": "decode tokens/s per GPT layer (incremental, packed KV cache), 1 GPU", "value": round(value, 1),
+        "unit": "decode tokens/s per layer", "n_gpus": 1, "steps": N, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f16" if w.dtype == "f16" else "f32",
+        "data": "synthetic (seeded prompts and token rows, N(0,0.02) random-init weights)",
+        "config": {"workload": w.name, "mode": "decode", "sequences": B, "prompt_tokens": T0, "layers": L,
+                   "hidden": H, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": F},
+        "roofline": {"bound": "hbm", "kernel": "gemm_fc1 at M = %d (weights streamed once)" % B,
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(fc1_ms, 4), "bytes_per_launch": fc1_bytes,
+                     "step_gbs": round(step_bytes / (ms_step * 1e-3) / 1e9, 1)},
+        "cpu_baseline": None,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = _parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -315,6 +403,9 @@ def main():
     w = workloads.get(args.workload)
     if w.requests:
         _stream_bench(args)
+        return
+    if args.decode_steps > 0:
+        _decode_bench(args)
         return
     lens = workloads.lengths(w, args.seed)
     B, P, L = w.batch, w.pad_len, w.layers

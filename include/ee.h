@@ -207,6 +207,19 @@ EE_API ee_status ee_linear(const void* A, const void* W, const void* bias, const
                     int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
                     ee_gelu gelu, void* C, void* stream);
 
+/* ee_linear for fp16 with the K dimension split: `splits` workgroup rows each
+ * sum an equal K range (K % (64 * splits) == 0) into fp32 partials in the
+ * workspace (ee_linear_splitk_workspace_size bytes), and a second kernel adds
+ * the partials in split order and applies the epilogue.  For small M (e.g. a
+ * decode step, M = batch), where the unsplit grid has too few workgroups to
+ * stream W at full bandwidth; the layer calls choose the split themselves.
+ * Errors: EE_ERR_UNSUPPORTED for fp32 or shapes the fp16 kernels do not take;
+ * EE_ERR_WORKSPACE for a small workspace. */
+EE_API ee_status ee_linear_splitk_workspace_size(int64_t M, int32_t N, int32_t splits, size_t* bytes);
+EE_API ee_status ee_linear_splitk(const void* A, const void* W, const void* bias, const void* residual,
+                                  int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu,
+                                  int32_t splits, void* C, void* ws, size_t ws_bytes, void* stream);
+
 /* g[r, c] = gelu(u[r, c] + bias[c]): the standalone form of the FC1 epilogue
  * (announcement article, "Ease of use" listing: add bias + activation). */
 EE_API ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t cols, ee_dtype dtype,
@@ -296,7 +309,9 @@ EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32
  * tokens, overlapping buffers, or a post-LN descriptor; EE_ERR_UNSUPPORTED
  * for head_dim outside {16, 32, 64, 128} or more than
  * ee_extend_max_positions() positions in one sequence; EE_ERR_WORKSPACE
- * when ws_bytes < ee_extend_workspace_size(layer, batch, T_new). */
+ * when ws_bytes < ee_extend_workspace_size(layer, batch, T_new).  A size
+ * taken for some T_new covers every step with fewer new tokens; fp16 sizes
+ * include 64 MiB for the split-K partial sums of small steps. */
 EE_API ee_status ee_kv_cache_bytes(const ee_layer* layer, int32_t n_layers, int64_t capacity, size_t* bytes);
 EE_API ee_status ee_extend_workspace_size(const ee_layer* layer, int32_t batch, int64_t max_new_tokens,
                                           size_t* bytes);

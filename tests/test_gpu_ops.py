@@ -154,6 +154,50 @@ def test_gemm_integer_exact(M, N, K, epi):
         f"{np.count_nonzero(got != ref16)} of {got.size} differ"
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(1, 1024, 1024, 2), (32, 12288, 4096, 8), (100, 4104, 1024, 4),
+                                          (128, 4099, 512, 2), (32, 640, 2048, 16), (77, 256, 128, 2)])
+@pytest.mark.parametrize("epi", [ee.EPI_NONE, ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL])
+def test_gemm_splitk_integer_exact(M, N, K, splits, epi):
+    """Split-K on small-integer operands: each K range's partial sum and the
+    sum of the partials are integers below 2^24, exact in fp32, so the result
+    is the fp16 rounding of the exact sum, bit for bit, as unsplit."""
+    A, W = _small_ints((M, K)), _small_ints((N, K))
+    bias = _small_ints((N,)) if epi != ee.EPI_NONE else None
+    R = _small_ints((M, N), -8, 8) if epi == ee.EPI_BIAS_RESIDUAL else None
+    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    ws = torch.empty(ee.ee_linear_splitk_workspace_size(M, N, splits), dtype=torch.uint8, device=DEV)
+    ee.ee_linear_splitk(A.to(DEV), W.to(DEV), None if bias is None else bias.to(DEV),
+                        None if R is None else R.to(DEV), epi, C, splits, ws)
+    torch.cuda.synchronize()
+    exact = A.double().numpy() @ W.double().numpy().T
+    if bias is not None:
+        exact = exact + bias.double().numpy()
+    if R is not None:
+        exact = exact + R.double().numpy()
+    assert np.abs(exact).max() < 2 ** 24
+    ref16 = exact.astype(np.float16)
+    got = C.cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), ref16.view(np.uint16)), \
+        f"{np.count_nonzero(got != ref16)} of {got.size} differ"
+
+
+@pytest.mark.parametrize("gelu", [ee.GELU_TANH, ee.GELU_ERF])
+def test_gemm_splitk_random_matches_unsplit(gelu):
+    M, N, K = 32, 4096, 12288
+    A = torch.randn(M, K, generator=GEN).to(torch.float16).to(DEV)
+    W = (0.02 * torch.randn(N, K, generator=GEN)).to(torch.float16).to(DEV)
+    bias = (0.1 * torch.randn(N, generator=GEN)).to(torch.float16).to(DEV)
+    C1 = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    C8 = torch.empty_like(C1)
+    ee.ee_linear(A, W, bias, None, ee.EPI_BIAS_GELU, C1, gelu=gelu)
+    ws = torch.empty(ee.ee_linear_splitk_workspace_size(M, N, 8), dtype=torch.uint8, device=DEV)
+    ee.ee_linear_splitk(A, W, bias, None, ee.EPI_BIAS_GELU, C8, 8, ws, gelu=gelu)
+    torch.cuda.synchronize()
+    u = oracle.linear(A.double().cpu().numpy(), W.double().cpu().numpy(), bias.double().cpu().numpy())
+    ref = oracle.gelu(u, "tanh" if gelu == ee.GELU_TANH else "erf")
+    assert normwise_rel(to_host64(C8), ref) <= 2e-3 and normwise_rel(to_host64(C1), ref) <= 2e-3
+
+
 @pytest.mark.parametrize("M,N,K,epi,gelu", [
     (129, 768, 768, ee.EPI_BIAS_GELU, ee.GELU_TANH), (516, 3072, 768, ee.EPI_BIAS_GELU, ee.GELU_ERF),
     (4100, 1024, 1024, ee.EPI_BIAS_GELU, ee.GELU_TANH), (77, 2304, 768, ee.EPI_BIAS, ee.GELU_TANH),

@@ -16,6 +16,7 @@ __all__ = [
     "EPI_NONE", "EPI_BIAS", "EPI_BIAS_RESIDUAL", "EPI_BIAS_GELU",
     "ee_compute_offsets", "ee_compute_offsets_mask", "ee_padding_workspace_size",
     "ee_remove_padding", "ee_rebuild_padding", "ee_layernorm", "ee_linear", "ee_bias_gelu",
+    "ee_linear_splitk", "ee_linear_splitk_workspace_size",
     "ee_attention_varlen", "ee_attention_padded", "ee_transpose_padding_rebuild_heads",
     "ee_transpose_padding_remove_heads", "ee_add_bias_residual_layernorm",
     "BLOCK_GPT_PRELN", "BLOCK_BERT_POSTLN", "ATTN_VARLEN", "ATTN_PADDED",
@@ -104,6 +105,9 @@ _SIGS = {
     "ee_layernorm": (C.c_int, [_VP, _VP, _VP, _I64, _I32, C.c_float, C.c_int, _VP, _VP]),
     "ee_linear": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP, _VP]),
     "ee_bias_gelu": (C.c_int, [_VP, _VP, _I64, _I32, C.c_int, C.c_int, _VP, _VP]),
+    "ee_linear_splitk_workspace_size": (C.c_int, [_I64, _I32, _I32, C.POINTER(_SZ)]),
+    "ee_linear_splitk": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _I32, _VP, _VP,
+                                   _SZ, _VP]),
     "ee_attention_varlen": (C.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I64, _I32, C.c_int, _VP, _VP]),
     "ee_attention_padded": (C.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_int, _VP, _VP]),
     "ee_transpose_padding_rebuild_heads": (C.c_int, [_VP, _PI32, _I32, _I32, _I32, _I32, _I32, C.c_int, _VP, _VP,
@@ -224,6 +228,21 @@ def ee_linear(A, W, bias, residual, epi: int, C_out, gelu: int = GELU_TANH, stre
     N = W.shape[0]
     _check(lib().ee_linear(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
                            _ptr(C_out), _stream(stream)), "ee_linear")
+
+
+def ee_linear_splitk_workspace_size(M: int, N: int, splits: int) -> int:
+    n = C.c_size_t(0)
+    _check(lib().ee_linear_splitk_workspace_size(M, N, splits, C.byref(n)), "ee_linear_splitk_workspace_size")
+    return n.value
+
+
+def ee_linear_splitk(A, W, bias, residual, epi: int, C_out, splits: int, workspace, gelu: int = GELU_TANH,
+                     stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().ee_linear_splitk(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
+                                  splits, _ptr(C_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream)), "ee_linear_splitk")
 
 
 def ee_bias_gelu(u, bias, g, gelu: int = GELU_TANH, stream=None):

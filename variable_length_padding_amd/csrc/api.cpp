@@ -175,8 +175,12 @@ bool desc_equal(const ee_layer_desc& a, const ee_layer_desc& b) {
 
 // ---------------------------------------------------------------- workspace
 struct Plan {
-  size_t cu, token_src, pad2pack, x, ln, big, o, h, heads, o_heads, total;
+  size_t cu, token_src, pad2pack, x, ln, big, o, h, heads, o_heads, splitk, splitk_bytes, total;
 };
+
+// split-K partial sums of the small-M GEMMs of an extend step
+constexpr size_t kSplitkScratch = size_t(64) << 20;
+constexpr int64_t kSplitkMaxRows = 128;
 
 Plan plan_offsets_only(int32_t B, int32_t P) {
   Plan p{};
@@ -221,8 +225,13 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // ---------------------------------------------------------------- launch helpers
 hipError_t gemm(ee_dtype dt, const void* A, const void* W, const void* bias, const void* R, int64_t M, int N, int K,
-                ee_epilogue epi, ee_gelu g, void* C, hipStream_t s) {
-  if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K)) return launch_gemm_f16_mfma(A, W, bias, R, M, N, K, epi, g, C, s);
+                ee_epilogue epi, ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr,
+                size_t scratch_bytes = 0) {
+  if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K)) {
+    const int splits = scratch && M <= kSplitkMaxRows ? gemm_f16_splitk_choice(M, N, K, scratch_bytes) : 1;
+    if (splits > 1) return launch_gemm_f16_splitk(A, W, bias, R, M, N, K, epi, g, C, splits, scratch, s);
+    return launch_gemm_f16_mfma(A, W, bias, R, M, N, K, epi, g, C, s);
+  }
   return launch_gemm_valu(dt, A, W, bias, R, M, N, K, epi, g, C, s);
 }
 
@@ -265,33 +274,35 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, hi
   void* big = at(ws, p.big);
   void* o = at(ws, p.o);
   void* h = at(ws, p.h);
+  void* sk = p.splitk_bytes ? at(ws, p.splitk) : nullptr;
+  const size_t skb = p.splitk_bytes;
   auto fc1 = [&](const void* in) -> ee_status {
     if (d.fuse_gelu) {
-      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, EE_EPI_BIAS_GELU, d.gelu, big, s));
+      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, EE_EPI_BIAS_GELU, d.gelu, big, s, sk, skb));
     } else {
-      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, EE_EPI_NONE, d.gelu, big, s));
+      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, EE_EPI_NONE, d.gelu, big, s, sk, skb));
       EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, d.gelu, big, s));
     }
     return EE_OK;
   };
   if (d.block == EE_BLOCK_GPT_PRELN) {
     EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
-    EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
+    EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
     EE_TRY(attn(big, o, true));
-    EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s));
+    EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb));
     EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
     EE_TRY(fc1(ln));
-    EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s));
+    EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s, sk, skb));
     return EE_OK;
   }
   // post-LN encoder: GEMM, then bias + residual + LayerNorm in one pass
-  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s));
+  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
   EE_TRY(attn(big, o, false));
-  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, EE_EPI_NONE, d.gelu, ln, s));
+  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
   EE_LAUNCH("add_ln1", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_out, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, h, s));
   EE_TRY(fc1(h));
-  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, EE_EPI_NONE, d.gelu, ln, s));
+  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
   EE_LAUNCH("add_ln2", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_fc2, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, x, s));
   return EE_OK;
@@ -354,6 +365,10 @@ Plan plan_extend(const ee_layer_desc& d, int32_t B, int64_t T) {
   p.big = take(t * std::max(3 * Hp, F) * s);
   p.o = take(t * Hp * s);
   p.h = take(t * H * s);
+  if (d.dtype == EE_F16) {  // reserved at every T, so a size taken for T covers any smaller step
+    p.splitk = take(kSplitkScratch);
+    p.splitk_bytes = kSplitkScratch;
+  }
   p.total = off;
   return p;
 }
@@ -683,6 +698,43 @@ ee_status ee_linear(const void* A, const void* W, const void* bias, const void* 
     return fail(EE_ERR_INVALID_ARG, "C overlaps an input");
   hipStream_t st = static_cast<hipStream_t>(stream);
   EE_LAUNCH("linear", st, gemm(dtype, A, W, bias, residual, M, N, K, epi, gelu, C, st));
+  return EE_OK;
+}
+
+ee_status ee_linear_splitk_workspace_size(int64_t M, int32_t N, int32_t splits, size_t* bytes) {
+  if (M < 0 || N < 1 || splits < 1 || splits > 64 || !bytes)
+    return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, 1 <= splits <= 64 and an output");
+  *bytes = gemm_f16_splitk_bytes(M, N, splits);
+  return EE_OK;
+}
+
+ee_status ee_linear_splitk(const void* A, const void* W, const void* bias, const void* residual, int64_t M,
+                           int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, int32_t splits,
+                           void* C, void* ws, size_t ws_bytes, void* stream) {
+  if (dtype != EE_F16) return fail(EE_ERR_UNSUPPORTED, "split-K is fp16 only");
+  if (epi < EE_EPI_NONE || epi > EE_EPI_BIAS_GELU) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi);
+  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+  if (M < 0 || N < 1 || K < 1 || splits < 1 || splits > 64)
+    return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1, 1 <= splits <= 64");
+  if (M == 0) return EE_OK;
+  if (!gemm_f16_mfma_ok(M, N, K) || K % (64 * splits) != 0)
+    return fail(EE_ERR_UNSUPPORTED, "shape M=%lld N=%d K=%d splits=%d not supported", (long long)M, N, K, splits);
+  EE_TRY(check_ptr(A, "A"));
+  EE_TRY(check_ptr(W, "W"));
+  EE_TRY(check_ptr(C, "C"));
+  EE_TRY(check_ptr(ws, "workspace"));
+  if (epi != EE_EPI_NONE) EE_TRY(check_ptr(bias, "bias"));
+  if (epi == EE_EPI_BIAS_RESIDUAL) EE_TRY(check_ptr(residual, "residual"));
+  const size_t need = gemm_f16_splitk_bytes(M, N, splits);
+  if (ws_bytes < need) return fail(EE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, need);
+  const size_t nc = (size_t)M * N * 2;
+  if (overlap(C, nc, A, (size_t)M * K * 2) || overlap(C, nc, W, (size_t)N * K * 2) ||
+      (epi != EE_EPI_NONE && overlap(C, nc, bias, (size_t)N * 2)) ||
+      (epi == EE_EPI_BIAS_RESIDUAL && overlap(C, nc, residual, nc)) || overlap(ws, need, C, nc) ||
+      overlap(ws, need, A, (size_t)M * K * 2) || overlap(ws, need, W, (size_t)N * K * 2))
+    return fail(EE_ERR_INVALID_ARG, "C or the workspace overlaps an input");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("linear", st, launch_gemm_f16_splitk(A, W, bias, residual, M, N, K, epi, gelu, C, splits, ws, st));
   return EE_OK;
 }
 

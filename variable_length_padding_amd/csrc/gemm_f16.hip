@@ -36,6 +36,7 @@
 //   * Ragged M (and N): the buffer descriptors end at the last valid row, so
 //     out-of-range rows load zeros; their results are never stored.  K must be
 //     a multiple of 64, and 256 rows x K x 2 bytes must fit 32-bit offsets.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -54,6 +55,10 @@ namespace {
 #endif
 
 constexpr int kBK = 64;
+// Split-K partial store (internal): fp32 sums of one K range, no epilogue.
+constexpr int kEpiPartial = 4;
+template <int EPI>
+constexpr bool kHasBias = EPI == EE_EPI_BIAS || EPI == EE_EPI_BIAS_RESIDUAL || EPI == EE_EPI_BIAS_GELU;
 
 __device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
@@ -137,7 +142,7 @@ template <int MF, int FM, int FN, int EPI>
 __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t (&acc)[FM][FN], float* __restrict__ stage,
                                                   int row0, int col0, int lane, const f16* __restrict__ bias,
                                                   const f16* __restrict__ R, f16* __restrict__ C, int M, int N,
-                                                  int gelu_form) {
+                                                  int gelu_form, float* __restrict__ Pp) {
   using SE = StagedEpilogue<MF, FN>;
   constexpr int FPB = 32 / MF;  // fragment rows per 32-row band
   constexpr int PASSES = 32 / SE::kRowsPerPass;
@@ -147,7 +152,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int cj = col0 + j * MF + lane % MF;
-    bcol[j] = (EPI != EE_EPI_NONE && cj < N) ? (float)bias[cj] : 0.f;
+    bcol[j] = (kHasBias<EPI> && cj < N) ? (float)bias[cj] : 0.f;
   }
 #pragma unroll
   for (int band = 0; band < FM / FPB; ++band) {
@@ -176,7 +181,12 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
       const int row = row0 + band * 32 + r;
       const float4 lo = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8);
       const float4 hi = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8 + 4);
-      if (row < M && col < N) {
+      if (EPI == kEpiPartial) {
+        if (row < M && col < N) {
+          *reinterpret_cast<float4*>(Pp + (int64_t)row * N + col) = lo;
+          *reinterpret_cast<float4*>(Pp + (int64_t)row * N + col + 4) = hi;
+        }
+      } else if (row < M && col < N) {
         const float v[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         half8 out;
 #pragma unroll
@@ -193,18 +203,20 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
 template <int MF, int FM, int FN, int EPI>
 __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)[FM][FN], int row0, int col0, int lane,
                                            const f16* __restrict__ bias, const f16* __restrict__ R,
-                                           f16* __restrict__ C, int M, int N, int gelu_form) {
+                                           f16* __restrict__ C, int M, int N, int gelu_form, float* __restrict__ Pp) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int col = col0 + j * MF + lane % MF;
     if (col >= N) continue;
-    const float bcol = (EPI != EE_EPI_NONE) ? (float)bias[col] : 0.f;
+    const float bcol = kHasBias<EPI> ? (float)bias[col] : 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int e = 0; e < Frag<MF>::kElems; ++e) {
         const int row = row0 + i * MF + Frag<MF>::row(lane, e);
-        if (row < M) {
+        if (row < M && EPI == kEpiPartial) {
+          Pp[(int64_t)row * N + col] = acc[i][j][e];
+        } else if (row < M) {
           float v = acc[i][j][e] + bcol;
           if (EPI == EE_EPI_BIAS_RESIDUAL) v += (float)R[(int64_t)row * N + col];
           if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
@@ -220,7 +232,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
                                                                  const f16* __restrict__ bias,
                                                                  const f16* __restrict__ R, f16* __restrict__ C,
                                                                  int M, int N, int K, int gelu_form, int tiles_m,
-                                                                 int tiles_n) {
+                                                                 int tiles_n, float* __restrict__ P) {
   using FR = Frag<MF>;
   using acc_t = typename FR::acc_t;
   constexpr int NW = WGM * WGN;                // waves: WGM x WGN grid over the tile
@@ -234,6 +246,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
 
   int m0, n0;
   tile_origin<BM, BN>(tiles_m, tiles_n, m0, n0);
+  // split-K: workgroup row y of the grid sums the y-th of gridDim.y equal K ranges
+  const int k_len = K / (int)gridDim.y, kbeg = (int)blockIdx.y * k_len;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -265,10 +279,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   auto dma_one = [&](int stage, int k0, int q) {
     if (q < AJ) {
       f16* sa = smem + stage * STAGE + (wave * (BM / NW) + 8 * q) * kBK;
-      buffer_load_lds16(arsrc, sa, aoff[q], k0 * 2);
+      buffer_load_lds16(arsrc, sa, aoff[q], (kbeg + k0) * 2);
     } else {
       f16* sb = smem + stage * STAGE + BM * kBK + (wave * (BN / NW) + 8 * (q - AJ)) * kBK;
-      buffer_load_lds16(wrsrc, sb, boff[q - AJ], k0 * 2);
+      buffer_load_lds16(wrsrc, sb, boff[q - AJ], (kbeg + k0) * 2);
     }
   };
   auto dma = [&](int stage, int k0) {
@@ -348,7 +362,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  const int nk = K / kBK;
+  const int nk = k_len / kBK;
   half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   dma(0, 0);
   if (nk > 1) dma(1, kBK);
@@ -383,40 +397,79 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   if (vec_ok) {
     __syncthreads();  // every wave is done reading the ring
     float* stage = reinterpret_cast<float*>(smem) + wave * StagedEpilogue<MF, FN>::kFloats;
-    store_tile_staged<MF, FM, FN, EPI>(acc, stage, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
+    store_tile_staged<MF, FM, FN, EPI>(acc, stage, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form,
+                                       P + (int64_t)blockIdx.y * M * N);
   } else {
-    store_tile<MF, FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form);
+    store_tile<MF, FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form,
+                                P + (int64_t)blockIdx.y * M * N);
   }
 }
 
 template <int MF, int BM, int BN, int WGM, int WGN>
-hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K,
-                      ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
+hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K, int epi,
+                      ee_gelu form, void* C, int splits, float* P, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  const dim3 grid((unsigned)(tm * tn)), block(64 * WGM * WGN);
+  const dim3 grid((unsigned)(tm * tn), (unsigned)splits), block(64 * WGM * WGN);
   const f16* a = static_cast<const f16*>(A);
   const f16* w = static_cast<const f16*>(W);
   const f16* b = static_cast<const f16*>(bias);
   const f16* r = static_cast<const f16*>(R);
   f16* c = static_cast<f16*>(C);
+#define EE_GEMM_LAUNCH(E)                                                                                        \
+  hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E>), grid, block, 0, s, a, w, b, r, c, M, N, K, \
+                     (int)form, tm, tn, P)
   switch (epi) {
-    case EE_EPI_NONE:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_NONE>), grid, block, 0, s, a, w, b, r, c, M, N, K,
-                         (int)form, tm, tn);
-      break;
-    case EE_EPI_BIAS:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_BIAS>), grid, block, 0, s, a, w, b, r, c, M, N, K,
-                         (int)form, tm, tn);
-      break;
-    case EE_EPI_BIAS_RESIDUAL:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_BIAS_RESIDUAL>), grid, block, 0, s, a, w, b, r, c, M,
-                         N, K, (int)form, tm, tn);
-      break;
-    case EE_EPI_BIAS_GELU:
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EE_EPI_BIAS_GELU>), grid, block, 0, s, a, w, b, r, c, M, N,
-                         K, (int)form, tm, tn);
-      break;
+    case EE_EPI_NONE: EE_GEMM_LAUNCH(EE_EPI_NONE); break;
+    case EE_EPI_BIAS: EE_GEMM_LAUNCH(EE_EPI_BIAS); break;
+    case EE_EPI_BIAS_RESIDUAL: EE_GEMM_LAUNCH(EE_EPI_BIAS_RESIDUAL); break;
+    case EE_EPI_BIAS_GELU: EE_GEMM_LAUNCH(EE_EPI_BIAS_GELU); break;
+    case kEpiPartial: EE_GEMM_LAUNCH(kEpiPartial); break;
   }
+#undef EE_GEMM_LAUNCH
+  return hipGetLastError();
+}
+
+// C = epilogue(sum over the splits of P[split]): the partial sums added in
+// split order in fp32, then bias, GeLU or residual and one fp16 rounding, as
+// the unsplit store does.  8 columns per thread (N % 8 == 0) or 1.
+template <int EPI, int V>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int splits, int64_t M, int N,
+                                                          const f16* __restrict__ bias, const f16* __restrict__ R,
+                                                          f16* __restrict__ C, int gelu_form) {
+  const int64_t per_row = N / V, total = M * per_row;
+  for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i / per_row;
+    const int col = (int)(i - row * per_row) * V;
+    float v[V];
+#pragma unroll
+    for (int k = 0; k < V; ++k) v[k] = 0.f;
+    for (int sp = 0; sp < splits; ++sp) {
+      const float* src = P + ((int64_t)sp * M + row) * N + col;
+#pragma unroll
+      for (int k = 0; k < V; ++k) v[k] += src[k];
+    }
+#pragma unroll
+    for (int k = 0; k < V; ++k) {
+      float x = v[k] + (kHasBias<EPI> ? (float)bias[col + k] : 0.f);
+      if (EPI == EE_EPI_BIAS_RESIDUAL) x += (float)R[row * N + col + k];
+      if (EPI == EE_EPI_BIAS_GELU) x = gelu_f(x, gelu_form);
+      C[row * N + col + k] = (f16)x;
+    }
+  }
+}
+
+template <int EPI>
+hipError_t launch_reduce(const float* P, int splits, int64_t M, int N, const void* bias, const void* R, void* C,
+                         ee_gelu form, hipStream_t s) {
+  const bool vec = N % 8 == 0;
+  const int64_t items = M * (vec ? N / 8 : N);
+  const unsigned grid = (unsigned)std::min<int64_t>((items + 255) / 256, 4096);
+  if (vec)
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, 8>), dim3(grid), dim3(256), 0, s, P, splits, M, N,
+                       static_cast<const f16*>(bias), static_cast<const f16*>(R), static_cast<f16*>(C), (int)form);
+  else
+    hipLaunchKernelGGL((splitk_reduce_kernel<EPI, 1>), dim3(grid), dim3(256), 0, s, P, splits, M, N,
+                       static_cast<const f16*>(bias), static_cast<const f16*>(R), static_cast<f16*>(C), (int)form);
   return hipGetLastError();
 }
 
@@ -431,8 +484,39 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
   if (M <= 0) return hipSuccess;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_big >= 256)
-    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
-  return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, s);
+    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, epi, form, C, 1,
+                                                                      nullptr, s);
+  return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, 1, nullptr, s);
+}
+
+int gemm_f16_splitk_choice(int64_t M, int N, int K, size_t scratch_bytes) {
+  if (M > 128 || !gemm_f16_mfma_ok(M, N, K)) return 1;
+  const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
+  if (tiles >= 256) return 1;  // one workgroup per CU or more already: splitting measured slower
+  int splits = 1;
+  while (splits < 8 && tiles * splits < 512 && K % (kBK * 2 * splits) == 0 && K / (2 * splits) >= 4 * kBK &&
+         (size_t)(2 * splits) * (size_t)M * (size_t)N * 4 <= scratch_bytes)
+    splits *= 2;
+  return splits;
+}
+
+size_t gemm_f16_splitk_bytes(int64_t M, int N, int splits) { return (size_t)splits * (size_t)M * (size_t)N * 4; }
+
+hipError_t launch_gemm_f16_splitk(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
+                                  int K, ee_epilogue epi, ee_gelu form, void* C, int splits, void* scratch,
+                                  hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  float* P = static_cast<float*>(scratch);
+  hipError_t e = launch_cfg<32, 128, 128, 2, 2>(A, W, nullptr, nullptr, (int)M, N, K, kEpiPartial, form, nullptr,
+                                                splits, P, s);
+  if (e != hipSuccess) return e;
+  switch (epi) {
+    case EE_EPI_NONE: return launch_reduce<EE_EPI_NONE>(P, splits, M, N, bias, R, C, form, s);
+    case EE_EPI_BIAS: return launch_reduce<EE_EPI_BIAS>(P, splits, M, N, bias, R, C, form, s);
+    case EE_EPI_BIAS_RESIDUAL: return launch_reduce<EE_EPI_BIAS_RESIDUAL>(P, splits, M, N, bias, R, C, form, s);
+    case EE_EPI_BIAS_GELU: return launch_reduce<EE_EPI_BIAS_GELU>(P, splits, M, N, bias, R, C, form, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace ee

@@ -68,6 +68,14 @@ hipError_t launch_bias_gelu(ee_dtype dt, const void* u, const void* bias, int64_
 bool gemm_f16_mfma_ok(int64_t M, int N, int K);
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M,
                                 int N, int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s);
+// Split-K for small M: `splits` equal K ranges (K % (64 * splits) == 0) summed
+// into fp32 partials in scratch (gemm_f16_splitk_bytes), then reduced with the
+// epilogue.  gemm_f16_splitk_choice picks the split count (1 = do not split).
+int gemm_f16_splitk_choice(int64_t M, int N, int K, size_t scratch_bytes);
+size_t gemm_f16_splitk_bytes(int64_t M, int N, int splits);
+hipError_t launch_gemm_f16_splitk(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
+                                  int K, ee_epilogue epi, ee_gelu form, void* C, int splits, void* scratch,
+                                  hipStream_t s);
 hipError_t launch_gemm_valu(ee_dtype dt, const void* A, const void* W, const void* bias, const void* R,
                             int64_t M, int N, int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s);
 
