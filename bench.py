@@ -40,6 +40,7 @@ PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROOFLINE_KERNEL = "gemm_fc1"
 ROOFLINE_SYMBOL = "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, EE_EPI_BIAS_GELU>"
+ROOFLINE_MANGLED = "_ZN2ee12_GLOBAL__N_120gemm_f16_mfma_kernelILi16ELi256ELi256ELi2ELi2ELi3EEEvPKDF16_S3_S3_S3_PDF16_iiiiiiPf"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fc1_gpt3-12l_pmc.json")
 GEMM_SOURCE = os.path.join(ROOT, "variable_length_padding_amd", "csrc", "gemm_f16.hip")
 
@@ -475,7 +476,7 @@ def main():
     fc1_ms = fc1["total_ms"] / fc1["launches"]
     fc1_flops = _site_work(w, T_run, B, P, ROOFLINE_KERNEL)[0]
     achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
-    roofline = {"bound": "mfma", "kernel": ROOFLINE_SYMBOL, "achieved": round(achieved, 1),
+    roofline = {"bound": "mfma", "kernel": ROOFLINE_SYMBOL, "symbol": ROOFLINE_MANGLED, "achieved": round(achieved, 1),
                 "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
                 "traffic": _traffic() if not (args.no_pack or bert) else None, "avg_launch_ms": round(fc1_ms, 4),
                 "flops_per_launch": fc1_flops}
