@@ -53,6 +53,10 @@ namespace {
 #ifndef EE_GEMM_MF
 #define EE_GEMM_MF 16
 #endif
+// Large problems: one workgroup per CU looping over tiles (1), or one per tile (0).
+#ifndef EE_GEMM_PERSIST
+#define EE_GEMM_PERSIST 1
+#endif
 
 constexpr int kBK = 64;
 // Split-K partial store (internal): fp32 sums of one K range, no epilogue.
@@ -83,9 +87,9 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // Tile origin of this workgroup: XCD-contiguous ranges of workgroup ids,
 // walked in groups of 4 M-tiles (see the file comment).
 template <int BM, int BN>
-__device__ __forceinline__ void tile_origin(int tiles_m, int tiles_n, int& m0, int& n0) {
-  int bid = blockIdx.x;
-  const int nblk = gridDim.x;
+__device__ __forceinline__ void tile_origin(int tile, int n_tiles, int tiles_m, int tiles_n, int& m0, int& n0) {
+  int bid = tile;
+  const int nblk = n_tiles;
   if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
   constexpr int GM = 4;
   const int per_group = GM * tiles_n;
@@ -122,8 +126,9 @@ struct Frag<16> {
 
 // Row-major epilogue through LDS: the MFMA result layout gives a lane one
 // column of several rows, so storing from it writes 2 bytes per lane and
-// short row pieces.  Instead each wave writes one 32-row band of its block
-// (with bias and GeLU applied, still fp32) to its own slice of the LDS ring,
+// short row pieces.  Instead each wave writes one band of its block (one
+// fragment row: 32 or 16 rows; bias and GeLU applied, still fp32) to its own
+// slice of the LDS,
 // then reads it back as 8 consecutive columns per lane, so C (and the residual
 // R) move in 16-byte vectors and whole row segments.  The rounding is the
 // same as a direct store: (acc + bias) + R in fp32, one fp16 rounding.
@@ -133,7 +138,8 @@ template <int MF, int FN>
 struct StagedEpilogue {
   static constexpr int WTN = FN * MF;
   static constexpr int kLd = WTN + Frag<MF>::kPad;
-  static constexpr int kFloats = 32 * kLd;  // per wave
+  static constexpr int kBandRows = MF;               // one fragment row per band
+  static constexpr int kFloats = kBandRows * kLd;    // per wave
   static constexpr int kLanesPerRow = WTN / 8;
   static constexpr int kRowsPerPass = 64 / kLanesPerRow;
 };
@@ -144,8 +150,8 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
                                                   const f16* __restrict__ R, f16* __restrict__ C, int M, int N,
                                                   int gelu_form, float* __restrict__ Pp) {
   using SE = StagedEpilogue<MF, FN>;
-  constexpr int FPB = 32 / MF;  // fragment rows per 32-row band
-  constexpr int PASSES = 32 / SE::kRowsPerPass;
+  constexpr int FPB = 1;  // fragment rows per band
+  constexpr int PASSES = SE::kBandRows / SE::kRowsPerPass;
   const int c8 = lane % SE::kLanesPerRow, rsub = lane / SE::kLanesPerRow;
   const int col = col0 + c8 * 8;
   float bcol[FN];
@@ -160,7 +166,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
     half8 rv[PASSES];
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
-      const int row = row0 + band * 32 + it * SE::kRowsPerPass + rsub;
+      const int row = row0 + band * SE::kBandRows + it * SE::kRowsPerPass + rsub;
       if (EPI == EE_EPI_BIAS_RESIDUAL && row < M && col < N)
         rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * N + col);
     }
@@ -178,7 +184,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
       const int r = it * SE::kRowsPerPass + rsub;
-      const int row = row0 + band * 32 + r;
+      const int row = row0 + band * SE::kBandRows + r;
       const float4 lo = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8);
       const float4 hi = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8 + 4);
       if (EPI == kEpiPartial) {
@@ -244,10 +250,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   static_assert(NSTEP == 2 || NSTEP == 4, "two or four K steps per K tile");
   __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
 
-  int m0, n0;
-  tile_origin<BM, BN>(tiles_m, tiles_n, m0, n0);
   // split-K: workgroup row y of the grid sums the y-th of gridDim.y equal K ranges
   const int k_len = K / (int)gridDim.y, kbeg = (int)blockIdx.y * k_len;
+  const int n_tiles = tiles_m * tiles_n;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -260,10 +265,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   // descriptors start at the tile's first row and end at the last valid row
   // (M or N), so rows past the end read as zeros and offsets stay 32-bit.
   const int lr = lane >> 3, lp = lane & 7;
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + (int64_t)m0 * K), (short)0, min(BM, M - m0) * K * 2, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(W + (int64_t)n0 * K), (short)0, min(BN, N - n0) * K * 2, kBufferFlags);
   int aoff[AJ], boff[BJ];  // byte offsets of this lane's 16-byte chunk, K tile 0
 #pragma unroll
   for (int j = 0; j < AJ; ++j) {
@@ -275,6 +276,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     const int r = wave * (BN / NW) + 8 * j + lr;
     boff[j] = (r * K + ((lp ^ lds_swizzle(r)) * 8)) * 2;
   }
+  __amdgpu_buffer_rsrc_t arsrc, wrsrc;
+  int m0 = 0, n0 = 0;
+  auto set_tile = [&](int tile) {
+    tile_origin<BM, BN>(tile, n_tiles, tiles_m, tiles_n, m0, n0);
+    arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * K), (short)0, min(BM, M - m0) * K * 2,
+                                              kBufferFlags);
+    wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K), (short)0, min(BN, N - n0) * K * 2,
+                                              kBufferFlags);
+  };
   // load q of a K tile: q < AJ -> rows of A, else rows of W
   auto dma_one = [&](int stage, int k0, int q) {
     if (q < AJ) {
@@ -315,12 +325,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   };
 
   acc_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < FR::kElems; ++e) acc[i][j][e] = 0.f;
   auto mfmas = [&](const half8 (&af)[FM], const half8 (&bf)[FN]) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -364,11 +368,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   };
   const int nk = k_len / kBK;
   half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
-  dma(0, 0);
-  if (nk > 1) dma(1, kBK);
-  wait_dma();
-  __syncthreads();
-  frags(0, 0, fa0, fb0);
   const std::integral_constant<bool, false> no_dma;
   const std::integral_constant<bool, true> with_dma;
   // the K steps of a tile before its barrier (all but the last); NSTEP is even,
@@ -380,36 +379,96 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
       step(no_dma, fa0, fb0, stage, 3, fa1, fb1, 0, 0);
     }
   };
-  int cur = 0;
-  for (int kt = 0; kt + 1 < nk; ++kt) {
-    steps_before_barrier(cur);
-    wait_dma();
-    __syncthreads();
-    step(with_dma, fa1, fb1, cur ^ 1, 0, fa0, fb0, cur, min(kt + 2, nk - 1) * kBK);
-    cur ^= 1;
-  }
-  steps_before_barrier(cur);
-  mfmas(fa1, fb1);
-  wait_dma();  // no load may still be writing LDS when the workgroup retires
 
-  static_assert(NW * StagedEpilogue<MF, FN>::kFloats * 4 <= 2 * STAGE * 2, "epilogue staging exceeds the LDS ring");
+  // ---- tiles: one per workgroup, or several (a persistent launch, fewer
+  // workgroups than tiles).  When the epilogue's staging fits in stage 1, the
+  // next tile's first K tile is loaded into stage 0 while this tile's results
+  // are stored.
+  using SE = StagedEpilogue<MF, FN>;
+  constexpr bool kOverlap = NW * SE::kFloats * 4 <= STAGE * 2;
+  static_assert(NW * SE::kFloats * 4 <= 2 * STAGE * 2, "epilogue staging exceeds the LDS ring");
   const bool vec_ok = (N & 7) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(R)) & 15) == 0;
-  if (vec_ok) {
+  float* const stage_base = reinterpret_cast<float*>(kOverlap ? smem + STAGE : smem);
+  int tile = blockIdx.x;
+  if (tile >= n_tiles) return;
+  set_tile(tile);
+  dma(0, 0);
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < FR::kElems; ++e) acc[i][j][e] = 0.f;
+    // K tile 0 is in flight (issued above, or during the previous epilogue)
+    if (nk > 1) {
+      dma(1, kBK);
+      if constexpr (NL == 16)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // K tile 0 landed; K tile 1 may still fly
+      else
+        wait_dma();
+    } else {
+      wait_dma();
+    }
+    __syncthreads();
+    frags(0, 0, fa0, fb0);
+    int cur = 0;
+    for (int kt = 0; kt + 1 < nk; ++kt) {
+      steps_before_barrier(cur);
+      wait_dma();
+      __syncthreads();
+      step(with_dma, fa1, fb1, cur ^ 1, 0, fa0, fb0, cur, min(kt + 2, nk - 1) * kBK);
+      cur ^= 1;
+    }
+    steps_before_barrier(cur);
+    mfmas(fa1, fb1);
+    wait_dma();  // no load may still be writing LDS when it is reused or the workgroup retires
+
+    const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
+    const int next = tile + (int)gridDim.x;
     __syncthreads();  // every wave is done reading the ring
-    float* stage = reinterpret_cast<float*>(smem) + wave * StagedEpilogue<MF, FN>::kFloats;
-    store_tile_staged<MF, FM, FN, EPI>(acc, stage, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form,
-                                       P + (int64_t)blockIdx.y * M * N);
-  } else {
-    store_tile<MF, FM, FN, EPI>(acc, m0 + wm * WTM, n0 + wn * WTN, lane, bias, R, C, M, N, gelu_form,
-                                P + (int64_t)blockIdx.y * M * N);
+    if (kOverlap && next < n_tiles) {
+      set_tile(next);
+      dma(0, 0);
+    }
+    float* const Pp = P + (int64_t)blockIdx.y * M * N;
+    if (vec_ok)
+      store_tile_staged<MF, FM, FN, EPI>(acc, stage_base + wave * SE::kFloats, row0, col0, lane, bias, R, C, M, N,
+                                         gelu_form, Pp);
+    else
+      store_tile<MF, FM, FN, EPI>(acc, row0, col0, lane, bias, R, C, M, N, gelu_form, Pp);
+    if (next >= n_tiles) break;
+    tile = next;
+    if (!kOverlap) {
+      __syncthreads();  // the staging is done with the ring
+      set_tile(tile);
+      dma(0, 0);
+    } else if (!vec_ok) {
+      __syncthreads();
+    }
   }
 }
 
+// Compute units of the current device (persistent launches use one workgroup per CU).
+int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
+// max_wgs > 0: at most that many workgroups, each looping over tiles
 template <int MF, int BM, int BN, int WGM, int WGN>
 hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K, int epi,
-                      ee_gelu form, void* C, int splits, float* P, hipStream_t s) {
+                      ee_gelu form, void* C, int splits, float* P, hipStream_t s, int max_wgs = 0) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
-  const dim3 grid((unsigned)(tm * tn), (unsigned)splits), block(64 * WGM * WGN);
+  const int wgs = max_wgs > 0 ? std::min(tm * tn, max_wgs) : tm * tn;
+  const dim3 grid((unsigned)wgs, (unsigned)splits), block(64 * WGM * WGN);
   const f16* a = static_cast<const f16*>(A);
   const f16* w = static_cast<const f16*>(W);
   const f16* b = static_cast<const f16*>(bias);
@@ -485,7 +544,7 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_big >= 256)
     return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, epi, form, C, 1,
-                                                                      nullptr, s);
+                                                                      nullptr, s, EE_GEMM_PERSIST ? device_cus() : 0);
   return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, 1, nullptr, s);
 }
 
