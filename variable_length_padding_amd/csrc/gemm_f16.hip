@@ -439,12 +439,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
       store_tile<MF, FM, FN, EPI>(acc, row0, col0, lane, bias, R, C, M, N, gelu_form, Pp);
     if (next >= n_tiles) break;
     tile = next;
+    __syncthreads();  // every wave's staging is done before the ring is loaded again
     if (!kOverlap) {
-      __syncthreads();  // the staging is done with the ring
       set_tile(tile);
       dma(0, 0);
-    } else if (!vec_ok) {
-      __syncthreads();
     }
   }
 }
