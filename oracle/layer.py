@@ -110,7 +110,7 @@ def rebuild_padding(packed: np.ndarray, lens: Sequence[int], pad_len: int) -> np
 def layer_norm(x: np.ndarray, gamma: np.ndarray, beta: np.ndarray, eps: float) -> np.ndarray:
     """Per row: (x - mean) / sqrt(var + eps) * gamma + beta, biased variance.
     LayerNorm appears in the announcement article's "Ease of use" listing
-    (add bias + input + LayerNorm); the pre-LN placement is this build's reading."""
+    (add bias + input + LayerNorm); the pre-LN placement is a reading of the pages (GPT-2/3 blocks)."""
     x = np.asarray(x, dtype=_F64)
     H = x.shape[-1]
     mu = x.sum(axis=-1, keepdims=True) / H
