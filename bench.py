@@ -439,20 +439,25 @@ def main():
     _log(f"warmup done ({args.warmup} steps)")
 
     ee.ee_profile_enable(True)
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    e0, e1 = marks[0], marks[-1]
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     e0.record(stream)
-    for _ in range(args.steps):
+    for i in range(args.steps):
         ee.ee_stack_forward(layers, x, run_lens, y, ws, stream)
-    e1.record(stream)
+        marks[i + 1].record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
     ee.ee_profile_enable(False)
     stats = ee.ee_profile_collect()
     ms_step = e0.elapsed_time(e1) / args.steps
-    _log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host clock {1e3 * t_host / args.steps:.3f})")
+    per_step = sorted(marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps))
+
+    def pct(q):
+        return per_step[min(len(per_step) - 1, int(round(q * (len(per_step) - 1))))]
+    _log(f"timed {args.steps} steps: {ms_step:.3f} ms/step (host clock {1e3 * t_host / args.steps:.3f}; "
+         f"p10 {pct(0.1):.3f}, median {pct(0.5):.3f}, p90 {pct(0.9):.3f})")
 
     value = T * L / (ms_step / 1e3)
     kernels = {}
@@ -488,7 +493,9 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "valid tokens/s per layer", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_step_p10_p50_p90": [round(pct(0.1), 4), round(pct(0.5), 4), round(pct(0.9), 4)],
+        "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f16" if w.dtype == "f16" else "f32",
         "data": "synthetic (seeded lengths, N(0,1) activations, N(0,0.02) random-init weights)",
         "config": {"workload": w.name, "batch": B, "pad_len": P, "valid_tokens": T, "layers": L,
