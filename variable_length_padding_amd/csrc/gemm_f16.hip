@@ -546,15 +546,19 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
   return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, 1, nullptr, s);
 }
 
+// Measured at M = 32 on the GPT-3 decode shapes (weights streamed once): four
+// K ranges were best on all four (QKV 201 vs 217 us unsplit, FC1 232 vs 238,
+// FC2 237 vs 632, out 67 vs 171); two were slower than none wherever the
+// unsplit grid already had a workgroup per CU.
 int gemm_f16_splitk_choice(int64_t M, int N, int K, size_t scratch_bytes) {
   if (M > 128 || !gemm_f16_mfma_ok(M, N, K)) return 1;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
-  if (tiles >= 256) return 1;  // one workgroup per CU or more already: splitting measured slower
-  int splits = 1;
-  while (splits < 8 && tiles * splits < 512 && K % (kBK * 2 * splits) == 0 && K / (2 * splits) >= 4 * kBK &&
-         (size_t)(2 * splits) * (size_t)M * (size_t)N * 4 <= scratch_bytes)
-    splits *= 2;
-  return splits;
+  for (int splits = 4; splits >= 2; splits /= 2) {
+    const bool fits = K % (kBK * splits) == 0 && K / splits >= 4 * kBK &&
+                      (size_t)splits * (size_t)M * (size_t)N * 4 <= scratch_bytes;
+    if (fits && (splits == 4 || tiles < 256)) return splits;
+  }
+  return 1;
 }
 
 size_t gemm_f16_splitk_bytes(int64_t M, int N, int splits) { return (size_t)splits * (size_t)M * (size_t)N * 4; }
