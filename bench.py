@@ -53,7 +53,7 @@ def _parse():
     ap.add_argument("--workload", default="gpt3-12l")
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-seqs", type=int, default=4)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=24)
     ap.add_argument("--no-fuse-gelu", action="store_true", help="unfused bias+GeLU (ablation)")
     ap.add_argument("--attention", choices=("varlen", "padded"), default="varlen",
                     help="padded: transposing rebuild -> fixed-shape masked attention -> transposing remove "

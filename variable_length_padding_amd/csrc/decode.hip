@@ -104,8 +104,9 @@ __device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) 
 //           lane group, coalesced), partial dot products summed by shuffles;
 //           scores go to LDS (dynamic, >= p + 1 floats);
 //   softmax: block max and sum; exp(s - max) in place;
-//   P.V:    each wave takes every 4th key, lanes own head_dim / 64 (or one)
-//           output dims; the four waves' partial sums meet in LDS.
+//   P.V:    the same key partition: a lane group reads a key's V row in
+//           16-byte chunks and accumulates its 8 dims; shuffles sum the key
+//           groups of a wave, LDS the four waves.
 template <typename T, int HD>
 __global__ __launch_bounds__(kExtendThreads) void cache_attention_kernel(const T* __restrict__ qkv, ExtendArg arg,
                                                                        const int32_t* __restrict__ cu, int nh,
@@ -114,7 +115,6 @@ __global__ __launch_bounds__(kExtendThreads) void cache_attention_kernel(const T
   constexpr int LPK = HD / 8;            // lanes per key row
   constexpr int KPW = 64 / LPK;          // keys per wave per pass
   constexpr int NW = kExtendThreads / 64;
-  constexpr int DPL = HD >= 64 ? HD / 64 : 1;
   static_assert(64 % LPK == 0, "a key row must be split over a power-of-two lane group");
   extern __shared__ float smem[];
   float* red = smem;                       // NW floats
@@ -163,19 +163,26 @@ __global__ __launch_bounds__(kExtendThreads) void cache_attention_kernel(const T
       l += e;
     }
     l = block_reduce(l, false, red);  // its barriers also publish the exponentials
-    float acc[DPL];
+    float acc[8];
 #pragma unroll
-    for (int d = 0; d < DPL; ++d) acc[d] = 0.f;
-    if (lane * DPL < HD) {
-      for (int j = wave; j < nk; j += NW) {
+    for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+    for (int j0 = wave * KPW; j0 < nk; j0 += NW * KPW) {
+      const int j = j0 + g;
+      if (j < nk) {
         const float pj = scores[j];
-        const T* vr = V + (int64_t)j * HD + lane * DPL;
+        float v[8];
+        Vec8<T>::load(V + (int64_t)j * HD + c * 8, v);
 #pragma unroll
-        for (int d = 0; d < DPL; ++d) acc[d] += pj * (float)vr[d];
+        for (int e = 0; e < 8; ++e) acc[e] += pj * v[e];
       }
-#pragma unroll
-      for (int d = 0; d < DPL; ++d) part[wave * HD + lane * DPL + d] = acc[d];
     }
+#pragma unroll
+    for (int d = LPK; d < 64; d <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], d, kWave);
+    if (g == 0)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[wave * HD + c * 8 + e] = acc[e];
     __syncthreads();
     for (int d = threadIdx.x; d < HD; d += kExtendThreads) {
       float s = 0.f;
