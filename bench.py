@@ -70,11 +70,20 @@ def _parse():
                     help="request-stream workload: batch size cap of both planners (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scale reference for HBM byte counters)")
+    ap.add_argument("--dense-weights", action="store_true",
+                    help="weight matrices stored dense instead of at ee_preferred_row_pitch (ablation)")
     return ap.parse_args()
 
 
 def _log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def _stored(args, params):
+    """A layer's parameters as the bench hands them to libee: weight rows at
+    the library's preferred pitch (dense with --dense-weights)."""
+    import variable_length_padding_amd as ee
+    return params if args.dense_weights else ee.pitched_weights(params)
 
 
 def _site_work(w, T, B, P, site):
@@ -183,7 +192,7 @@ def _stream_bench(args):
          f"padding {'kept' if args.no_pack else 'removed'}")
     params = []
     for l in range(L):
-        params.append(workloads.layer_params(w, args.seed, l, device=dev))
+        params.append(_stored(args, workloads.layer_params(w, args.seed, l, device=dev)))
         if l % 12 == 11:
             torch.cuda.synchronize()
             _log(f"weights: {l + 1}/{L} layers")
@@ -283,7 +292,7 @@ def _stream_bench(args):
         "warmup": 1, "ms_per_step": round(1e3 * d["seconds"], 1), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f16" if w.dtype == "f16" else "f32",
         "data": "synthetic (seeded request lengths U[1,%d], N(0,1) activations, N(0,0.02) random-init weights)" % P_max,
-        "config": {"workload": w.name, "requests": n_req, "valid_tokens": T, "layers": L, "max_batch": cap,
+        "config": {"weight_rows": "dense" if args.dense_weights else "preferred pitch", "workload": w.name, "requests": n_req, "valid_tokens": T, "layers": L, "max_batch": cap,
                    "hidden": w.hidden, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": w.ffn,
                    "batching": "dynamic", "padding_removed": not args.no_pack},
         "roofline": {"bound": "mfma", "kernel": ROOFLINE_SYMBOL, "achieved": round(achieved, 1),
@@ -313,7 +322,7 @@ def _decode_bench(args):
     B, L, N = len(prompts), w.layers, args.decode_steps
     s_el = w.elem_bytes
     H, Hp, F = w.hidden, w.inner, w.ffn
-    params = [workloads.layer_params(w, args.seed, l, device=dev) for l in range(L)]
+    params = [_stored(args, workloads.layer_params(w, args.seed, l, device=dev)) for l in range(L)]
     dt = ee.F16 if w.dtype == "f16" else ee.F32
     layers = [ee.Layer(H, w.n_heads, w.head_dim, F, p, dtype=dt) for p in params]
     slot_base, cap = [], 0
@@ -371,7 +380,7 @@ def _decode_bench(args):
         "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f16" if w.dtype == "f16" else "f32",
         "data": "synthetic (seeded prompts and token rows, N(0,0.02) random-init weights)",
-        "config": {"workload": w.name, "mode": "decode", "sequences": B, "prompt_tokens": T0, "layers": L,
+        "config": {"weight_rows": "dense" if args.dense_weights else "preferred pitch", "workload": w.name, "mode": "decode", "sequences": B, "prompt_tokens": T0, "layers": L,
                    "hidden": H, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": F},
         "roofline": {"bound": "hbm", "kernel": "gemm_fc1 at M = %d (weights streamed once)" % B,
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
@@ -418,7 +427,7 @@ def main():
          f"hd={w.head_dim} F={w.ffn} L={L} block={args.block} attention={args.attention}")
 
     x = workloads.activations(w, args.seed, B, P, lens, device=dev)
-    params = [workloads.layer_params(w, args.seed, l, device=dev) for l in range(L)]
+    params = [_stored(args, workloads.layer_params(w, args.seed, l, device=dev)) for l in range(L)]
     torch.cuda.synchronize()
     dt = ee.F16 if w.dtype == "f16" else ee.F32
     bert = args.block == "bert"
@@ -501,7 +510,8 @@ def main():
         "config": {"workload": w.name, "batch": B, "pad_len": P, "valid_tokens": T, "layers": L,
                    "hidden": w.hidden, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": w.ffn,
                    "fuse_gelu": not args.no_fuse_gelu, "block": "bert-postln" if bert else "gpt-preln",
-                   "attention": args.attention, "rows_run": T_run, "padding_removed": not args.no_pack},
+                   "attention": args.attention, "rows_run": T_run, "padding_removed": not args.no_pack,
+                   "weight_rows": "dense" if args.dense_weights else "preferred pitch"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

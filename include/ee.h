@@ -112,7 +112,11 @@ typedef struct {
 } ee_layer_desc;
 
 /* Device pointers, all of the descriptor's dtype, borrowed (not copied) by
- * ee_layer_create for the handle's lifetime. */
+ * ee_layer_create for the handle's lifetime.  Each weight matrix is
+ * [out, in], row-major.  Its rows may sit ld_* elements apart: 0 means dense
+ * (ld = in); a nonzero ld must be >= in and keep rows 16-byte aligned
+ * (ld * element size % 16 == 0).  ee_preferred_row_pitch gives a pitch that
+ * spreads the rows over the HBM channels. */
 typedef struct {
   const void *ln1_g, *ln1_b;   /* [H] */
   const void *w_qkv, *b_qkv;   /* [3H', H], [3H'] */
@@ -120,6 +124,7 @@ typedef struct {
   const void *ln2_g, *ln2_b;   /* [H] */
   const void *w_fc1, *b_fc1;   /* [F, H],   [F] */
   const void *w_fc2, *b_fc2;   /* [H, F],   [H] */
+  int64_t ld_qkv, ld_out, ld_fc1, ld_fc2;  /* row pitches of the four matrices (0: dense) */
 } ee_layer_weights;
 
 typedef struct ee_layer ee_layer;
@@ -202,10 +207,29 @@ EE_API ee_status ee_layernorm(const void* x, const void* gamma, const void* beta
 
 /* C[M, N] = epilogue(A[M, K] . W[N, K]^T): bias [N], residual [M, N] (may not
  * alias C).  fp16: MFMA kernels, fp32 accumulation, one rounding to fp16 at
- * the end.  fp32: fp32 FMA kernels.  M may be 0 (no work). */
+ * the end.  fp32: fp32 FMA kernels.  M may be 0 (no work).  All matrices
+ * dense; ee_linear_strided is the general form. */
 EE_API ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual,
                     int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
                     ee_gelu gelu, void* C, void* stream);
+
+/* ee_linear with row pitches, in elements: A [M, lda], W [N, ldw], C and the
+ * residual [M, ldc], with lda >= K, ldw >= K, ldc >= N (the columns past
+ * K or N are neither read nor written).  The fp16 MFMA kernels take K % 64
+ * == 0 with lda, ldw multiples of 8 and 16-byte aligned A and W; other fp16
+ * shapes run on the fp32 FMA kernels.  Errors as ee_linear, plus
+ * EE_ERR_INVALID_ARG for a pitch below its row length or above 2^31 - 1. */
+EE_API ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
+                                   const void* residual, int64_t M, int32_t N, int32_t K, ee_dtype dtype,
+                                   ee_epilogue epi, ee_gelu gelu, void* C, int64_t ldc, void* stream);
+
+/* The row pitch, in elements, that the library gives a matrix of `cols`
+ * columns it stores itself (the FC1 output in the layer workspace), and the
+ * one it suggests for weights: cols, plus 128 bytes when a row is a multiple
+ * of 32 KiB.  Such strides put every row of a GEMM panel on the same few HBM
+ * channels (K = 49152 fp16: 7% slower without the padding).  Returns 0 for
+ * cols < 1 or an unknown dtype. */
+EE_API int64_t ee_preferred_row_pitch(int64_t cols, ee_dtype dtype);
 
 /* ee_linear for fp16 with the K dimension split: `splits` workgroup rows each
  * sum an equal K range (K % (64 * splits) == 0) into fp32 partials in the

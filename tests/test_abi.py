@@ -188,3 +188,44 @@ def test_extend_validation_happens_before_device_work():
         lib.ee_layer_destroy(h2)
     finally:
         lib.ee_layer_destroy(h)
+
+
+def test_preferred_row_pitch():
+    lib = ee.lib()
+    # a row that is a multiple of 32 KiB gets 128 bytes more; others stay dense
+    assert lib.ee_preferred_row_pitch(49152, ee.F16) == 49216
+    assert lib.ee_preferred_row_pitch(16384, ee.F16) == 16448
+    assert lib.ee_preferred_row_pitch(8192, ee.F32) == 8224
+    assert lib.ee_preferred_row_pitch(12288, ee.F16) == 12288
+    assert lib.ee_preferred_row_pitch(3072, ee.F16) == 3072
+    assert lib.ee_preferred_row_pitch(24576, ee.F16) == 24576
+    assert lib.ee_preferred_row_pitch(0, ee.F16) == 0
+    assert lib.ee_preferred_row_pitch(64, 7) == 0
+
+
+def test_linear_strided_validates_pitches():
+    lib = ee.lib()
+    A, W, b, C_ = 1 << 30, 1 << 31, 1 << 32, 1 << 33
+    # pitches below the row lengths
+    assert lib.ee_linear_strided(A, 63, W, 64, b, None, 8, 32, 64, ee.F16, ee.EPI_BIAS, 0, C_, 32, None) == 1
+    assert lib.ee_linear_strided(A, 64, W, 60, b, None, 8, 32, 64, ee.F16, ee.EPI_BIAS, 0, C_, 32, None) == 1
+    assert lib.ee_linear_strided(A, 64, W, 64, b, None, 8, 32, 64, ee.F16, ee.EPI_BIAS, 0, C_, 31, None) == 1
+    assert lib.ee_linear_strided(A, 1 << 31, W, 64, b, None, 8, 32, 64, ee.F16, ee.EPI_BIAS, 0, C_, 32, None) == 1
+    # C's pitched extent (7 rows x 1000 + 32 elements) reaches the bias
+    assert lib.ee_linear_strided(A, 64, W, 64, C_ + 2 * 7000, None, 8, 32, 64, ee.F16, ee.EPI_BIAS, 0, C_, 1000,
+                                 None) == 1
+    # M = 0 is a valid no-op with any valid pitches
+    assert lib.ee_linear_strided(None, 72, W, 72, None, None, 0, 32, 64, ee.F16, ee.EPI_NONE, 0, None, 40, None) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("ld_fc2", 255, 1), ("ld_fc2", 257, 1), ("ld_qkv", 63, 1), ("ld_out", 1 << 31, 1),
+    ("ld_fc2", 260, 0), ("ld_fc1", 0, 0), ("ld_out", 68, 0),
+])
+def test_layer_create_validates_weight_pitches(field, value, status):
+    w = _weights()
+    setattr(w, field, value)      # fp32, H = 64, H' = 64, F = 256
+    st, h = _create(_desc(), w)
+    assert st == status
+    if h.value:
+        ee.lib().ee_layer_destroy(h)

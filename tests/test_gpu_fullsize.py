@@ -21,7 +21,7 @@ def _setup(w, seed, lens, layers, device_batch=None):
     B = len(lens)
     P = w.pad_len if device_batch is None else device_batch
     x = workloads.activations(w, seed, B, P, lens, device=DEV)
-    params = [workloads.layer_params(w, seed, l, device=DEV) for l in range(layers)]
+    params = [ee.pitched_weights(workloads.layer_params(w, seed, l, device=DEV)) for l in range(layers)]
     hs = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=ee.F16) for p in params]
     return x, params, hs
 
@@ -95,7 +95,7 @@ def test_gpt3_48l_stream_sequence_independence():
     torch.cuda.empty_cache()
     w = workloads.get("gpt3-48l-stream")
     groups = workloads.request_stream(w, SEED)
-    params = [workloads.layer_params(w, SEED, l, device=DEV) for l in range(w.layers)]
+    params = [ee.pitched_weights(workloads.layer_params(w, SEED, l, device=DEV)) for l in range(w.layers)]
     hs = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=ee.F16) for p in params]
     for gi in (0, len(groups) - 1):
         lens = groups[gi]
@@ -122,7 +122,7 @@ def test_gpt3_width_decode_sampled():
     w = workloads.get("gpt3-12l")
     prompts = [1, 57, 128, 200, 3, 96, 33, 150]
     B, L = len(prompts), 2
-    params = [workloads.layer_params(w, SEED, l, device=DEV) for l in range(L)]
+    params = [ee.pitched_weights(workloads.layer_params(w, SEED, l, device=DEV)) for l in range(L)]
     hs = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=ee.F16) for p in params]
     base = list(np.concatenate([[0], np.cumsum([n + 2 for n in prompts])[:-1]]).astype(int))
     cap = sum(n + 2 for n in prompts)

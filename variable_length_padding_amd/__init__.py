@@ -62,8 +62,12 @@ WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_out", "b_out",
                  "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2")
 
 
+# row pitch fields (elements; 0 = dense) of the four weight matrices, in order
+PITCH_FIELDS = (("w_qkv", "ld_qkv"), ("w_out", "ld_out"), ("w_fc1", "ld_fc1"), ("w_fc2", "ld_fc2"))
+
+
 class LayerWeights(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in WEIGHT_FIELDS]
+    _fields_ = [(n, C.c_void_p) for n in WEIGHT_FIELDS] + [(ld, C.c_int64) for _, ld in PITCH_FIELDS]
 
 
 class KernelStat(C.Structure):
@@ -104,6 +108,9 @@ _SIGS = {
     "ee_rebuild_padding": (C.c_int, [_VP, _PI32, _I32, _I32, _I32, C.c_int, _VP, _VP, _SZ, _VP]),
     "ee_layernorm": (C.c_int, [_VP, _VP, _VP, _I64, _I32, C.c_float, C.c_int, _VP, _VP]),
     "ee_linear": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP, _VP]),
+    "ee_linear_strided": (C.c_int, [_VP, _I64, _VP, _I64, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP,
+                                    _I64, _VP]),
+    "ee_preferred_row_pitch": (_I64, [_I64, C.c_int]),
     "ee_bias_gelu": (C.c_int, [_VP, _VP, _I64, _I32, C.c_int, C.c_int, _VP, _VP]),
     "ee_linear_splitk_workspace_size": (C.c_int, [_I64, _I32, _I32, C.POINTER(_SZ)]),
     "ee_linear_splitk": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _I32, _VP, _VP,
@@ -175,6 +182,18 @@ def _stream(stream) -> Optional[int]:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _row_pitch(t, dense: bool = False) -> int:
+    """Row pitch (elements) of a 2-D tensor with unit column stride; 0 for a
+    contiguous tensor unless `dense` asks for its row length."""
+    if t is None:
+        return 0
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("need a 2-D tensor with unit column stride")
+    if t.is_contiguous():
+        return t.shape[1] if dense else 0
+    return t.stride(0)
+
+
 def _lens(lens: Sequence[int]):
     arr = (C.c_int32 * max(1, len(lens)))(*[int(n) for n in lens])
     return arr
@@ -224,10 +243,45 @@ def ee_layernorm(x, gamma, beta, eps: float, y, stream=None):
 
 
 def ee_linear(A, W, bias, residual, epi: int, C_out, gelu: int = GELU_TANH, stream=None):
+    """C_out = epilogue(A . W^T); 2-D tensors whose rows may be strided
+    (unit column stride): their row strides are passed as the pitches."""
     M, K = A.shape
     N = W.shape[0]
-    _check(lib().ee_linear(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
-                           _ptr(C_out), _stream(stream)), "ee_linear")
+    if all(t is None or t.is_contiguous() for t in (A, W, residual, C_out)):
+        _check(lib().ee_linear(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
+                               _ptr(C_out), _stream(stream)), "ee_linear")
+        return
+    ldc = _row_pitch(C_out, dense=True)
+    if residual is not None and _row_pitch(residual, dense=True) != ldc:
+        raise ValueError("residual and C_out must share a row pitch")
+    _check(lib().ee_linear_strided(_ptr(A), _row_pitch(A, dense=True), _ptr(W), _row_pitch(W, dense=True), _ptr(bias),
+                                   _ptr(residual), M, N, K, _dtype_code(A), epi, gelu, _ptr(C_out), ldc,
+                                   _stream(stream)), "ee_linear_strided")
+
+
+def ee_preferred_row_pitch(cols: int, dtype: int = F16) -> int:
+    """Row pitch (elements) the library suggests for a matrix of `cols` columns."""
+    return int(lib().ee_preferred_row_pitch(cols, dtype))
+
+
+def pitched(t):
+    """A copy of the 2-D tensor t stored at ee_preferred_row_pitch (a view of
+    the first t.shape[1] columns of a wider tensor), or t itself when the
+    dense pitch is already the preferred one."""
+    import torch
+    rows, cols = t.shape
+    ld = ee_preferred_row_pitch(cols, _dtype_code(t))
+    if ld == cols and t.is_contiguous():
+        return t
+    buf = torch.zeros(rows, ld, dtype=t.dtype, device=t.device)
+    buf[:, :cols] = t
+    return buf[:, :cols]
+
+
+def pitched_weights(params: Dict) -> Dict:
+    """A layer's parameter dict with the four weight matrices stored at
+    ee_preferred_row_pitch (see `pitched`); the other tensors as given."""
+    return {k: pitched(v) if k in ("w_qkv", "w_out", "w_fc1", "w_fc2") else v for k, v in params.items()}
 
 
 def ee_linear_splitk_workspace_size(M: int, N: int, splits: int) -> int:
@@ -300,7 +354,8 @@ class Layer:
         self.desc = LayerDesc(hidden, n_heads, head_dim, ffn, ln_eps, dtype, gelu, 1 if fuse_gelu else 0, block,
                               attention)
         self._weights = {k: weights[k] for k in WEIGHT_FIELDS}
-        w = LayerWeights(*[_ptr(self._weights[k]) for k in WEIGHT_FIELDS])
+        w = LayerWeights(*[_ptr(self._weights[k]) for k in WEIGHT_FIELDS],
+                         *[_row_pitch(self._weights[k]) for k, _ in PITCH_FIELDS])
         h = C.c_void_p()
         _check(lib().ee_layer_create(C.byref(self.desc), C.byref(w), C.byref(h)), "ee_layer_create")
         self.handle = h

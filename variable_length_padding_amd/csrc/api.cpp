@@ -23,7 +23,8 @@ using namespace ee;
 
 struct ee_layer {
   ee_layer_desc desc;
-  ee_layer_weights w;
+  ee_layer_weights w;  // ld_* resolved: the row pitch of each matrix, never 0
+  int ld_big;          // row pitch of the FC1 output in the workspace
 };
 
 namespace {
@@ -63,6 +64,16 @@ ee_status check_ptr(const void* p, const char* name) {
   if (!p) return fail(EE_ERR_INVALID_ARG, "%s is NULL", name);
   if (!aligned16(p)) return fail(EE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
   return EE_OK;
+}
+
+// Bytes spanned by `rows` rows of `cols` elements at a pitch of ld elements.
+size_t span(int64_t rows, int64_t cols, int64_t ld, size_t s) {
+  return rows <= 0 ? 0 : ((size_t)(rows - 1) * (size_t)ld + (size_t)cols) * s;
+}
+
+// cols, plus 128 bytes when a row is a multiple of 32 KiB (see ee.h).
+int64_t preferred_pitch(int64_t cols, size_t s) {
+  return (size_t)cols * s % 32768 == 0 ? cols + (int64_t)(128 / s) : cols;
 }
 
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
@@ -209,7 +220,7 @@ Plan plan_layer(const ee_layer_desc& d, int32_t B, int32_t P, int64_t T) {
   const size_t H = d.hidden, Hp = (size_t)d.n_heads * d.head_dim, F = d.ffn;
   p.x = take(t * H * s);
   p.ln = take(t * H * s);
-  p.big = take(t * std::max(3 * Hp, F) * s);
+  p.big = take(t * std::max<size_t>(3 * Hp, preferred_pitch((int64_t)F, s)) * s);
   p.o = take(t * Hp * s);
   p.h = take(t * H * s);
   if (d.attention == EE_ATTN_PADDED) {  // head-major padded q|k|v and output
@@ -225,15 +236,17 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // ---------------------------------------------------------------- launch helpers
 hipError_t gemm(ee_dtype dt, const void* A, const void* W, const void* bias, const void* R, int64_t M, int N, int K,
-                ee_epilogue epi, ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr,
+                const GemmPitch& ld, ee_epilogue epi, ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr,
                 size_t scratch_bytes = 0) {
-  if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K)) {
+  if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K, ld, A, W)) {
     const int splits = scratch && M <= kSplitkMaxRows ? gemm_f16_splitk_choice(M, N, K, scratch_bytes) : 1;
-    if (splits > 1) return launch_gemm_f16_splitk(A, W, bias, R, M, N, K, epi, g, C, splits, scratch, s);
-    return launch_gemm_f16_mfma(A, W, bias, R, M, N, K, epi, g, C, s);
+    if (splits > 1) return launch_gemm_f16_splitk(A, W, bias, R, M, N, K, ld, epi, g, C, splits, scratch, s);
+    return launch_gemm_f16_mfma(A, W, bias, R, M, N, K, ld, epi, g, C, s);
   }
-  return launch_gemm_valu(dt, A, W, bias, R, M, N, K, epi, g, C, s);
+  return launch_gemm_valu(dt, A, W, bias, R, M, N, K, ld, epi, g, C, s);
 }
+
+GemmPitch dense(int N, int K) { return GemmPitch{K, K, N}; }
 
 ee_status offsets_from_host(const int32_t* lens, int32_t B, int32_t P, int32_t* cu, int32_t* token_src,
                             int32_t* pad2pack, hipStream_t s) {
@@ -276,33 +289,36 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, hi
   void* h = at(ws, p.h);
   void* sk = p.splitk_bytes ? at(ws, p.splitk) : nullptr;
   const size_t skb = p.splitk_bytes;
+  // A [T, .] . W^T: activations dense except the FC1 output (pitch ld_big)
+  const GemmPitch ld_qkv{H, (int)w.ld_qkv, 3 * Hp}, ld_out{Hp, (int)w.ld_out, H};
+  const GemmPitch ld_fc1{H, (int)w.ld_fc1, L->ld_big}, ld_fc2{L->ld_big, (int)w.ld_fc2, H};
   auto fc1 = [&](const void* in) -> ee_status {
     if (d.fuse_gelu) {
-      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, EE_EPI_BIAS_GELU, d.gelu, big, s, sk, skb));
+      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, ld_fc1, EE_EPI_BIAS_GELU, d.gelu, big, s, sk, skb));
     } else {
-      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, EE_EPI_NONE, d.gelu, big, s, sk, skb));
-      EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, d.gelu, big, s));
+      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, ld_fc1, EE_EPI_NONE, d.gelu, big, s, sk, skb));
+      EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, L->ld_big, d.gelu, big, s));
     }
     return EE_OK;
   };
   if (d.block == EE_BLOCK_GPT_PRELN) {
     EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
-    EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
+    EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
     EE_TRY(attn(big, o, true));
-    EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb));
+    EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, ld_out, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb));
     EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
     EE_TRY(fc1(ln));
-    EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s, sk, skb));
+    EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, ld_fc2, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s, sk, skb));
     return EE_OK;
   }
   // post-LN encoder: GEMM, then bias + residual + LayerNorm in one pass
-  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
+  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
   EE_TRY(attn(big, o, false));
-  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
+  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, ld_out, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
   EE_LAUNCH("add_ln1", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_out, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, h, s));
   EE_TRY(fc1(h));
-  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
+  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, ld_fc2, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
   EE_LAUNCH("add_ln2", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_fc2, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, x, s));
   return EE_OK;
@@ -362,7 +378,7 @@ Plan plan_extend(const ee_layer_desc& d, int32_t B, int64_t T) {
   p.cu = take(4 * (size_t)(B + 1));
   p.x = take(t * H * s);
   p.ln = take(t * H * s);
-  p.big = take(t * std::max(3 * Hp, F) * s);
+  p.big = take(t * std::max<size_t>(3 * Hp, preferred_pitch((int64_t)F, s)) * s);
   p.o = take(t * Hp * s);
   p.h = take(t * H * s);
   if (d.dtype == EE_F16) {  // reserved at every T, so a size taken for T covers any smaller step
@@ -504,10 +520,23 @@ ee_status ee_layer_create(const ee_layer_desc* desc, const ee_layer_weights* wei
   static const char* const names[] = {"ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_out", "b_out",
                                       "ln2_g", "ln2_b", "w_fc1", "b_fc1", "w_fc2", "b_fc2"};
   for (int i = 0; i < 12; ++i) EE_TRY(check_ptr(ptrs[i], names[i]));
+  const int64_t H = desc->hidden, Hp = (int64_t)desc->n_heads * desc->head_dim, F = desc->ffn;
+  const size_t s = dtype_size(desc->dtype);
+  ee_layer_weights w = *weights;
+  int64_t* const lds[] = {&w.ld_qkv, &w.ld_out, &w.ld_fc1, &w.ld_fc2};
+  const int64_t rowlen[] = {H, Hp, H, F};
+  static const char* const ldnames[] = {"ld_qkv", "ld_out", "ld_fc1", "ld_fc2"};
+  for (int i = 0; i < 4; ++i) {
+    if (*lds[i] == 0) *lds[i] = rowlen[i];
+    if (*lds[i] < rowlen[i] || *lds[i] > INT32_MAX || (size_t)*lds[i] * s % 16)
+      return fail(EE_ERR_INVALID_ARG, "%s = %lld: need a pitch >= %lld elements, below 2^31, of 16-byte rows",
+                  ldnames[i], (long long)*lds[i], (long long)rowlen[i]);
+  }
   ee_layer* L = new (std::nothrow) ee_layer;
   if (!L) return fail(EE_ERR_OOM, "host allocation of the layer handle failed");
   L->desc = *desc;
-  L->w = *weights;
+  L->w = w;
+  L->ld_big = (int)preferred_pitch(F, s);
   *out = L;
   return EE_OK;
 }
@@ -677,12 +706,16 @@ ee_status ee_layernorm(const void* x, const void* gamma, const void* beta, int64
   return EE_OK;
 }
 
-ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual, int64_t M, int32_t N,
-                    int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, void* C, void* stream) {
+ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
+                            const void* residual, int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
+                            ee_gelu gelu, void* C, int64_t ldc, void* stream) {
   if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
   if (epi < EE_EPI_NONE || epi > EE_EPI_BIAS_GELU) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi);
   if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
   if (M < 0 || N < 1 || K < 1) return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
+  if (lda < K || ldw < K || ldc < N || lda > INT32_MAX || ldw > INT32_MAX || ldc > INT32_MAX)
+    return fail(EE_ERR_INVALID_ARG, "pitches lda %lld, ldw %lld, ldc %lld: need >= K, K, N and < 2^31",
+                (long long)lda, (long long)ldw, (long long)ldc);
   if (M > 4000000) return fail(EE_ERR_UNSUPPORTED, "M = %lld above 4,000,000", (long long)M);
   EE_TRY(check_ptr(W, "W"));
   if (epi != EE_EPI_NONE) EE_TRY(check_ptr(bias, "bias"));
@@ -691,14 +724,25 @@ ee_status ee_linear(const void* A, const void* W, const void* bias, const void* 
   EE_TRY(check_ptr(C, "C"));
   if (epi == EE_EPI_BIAS_RESIDUAL) EE_TRY(check_ptr(residual, "residual"));
   const size_t s = dtype_size(dtype);
-  const size_t nc = (size_t)M * N * s;
-  if (overlap(C, nc, A, (size_t)M * K * s) || overlap(C, nc, W, (size_t)N * K * s) ||
+  const size_t nc = span(M, N, ldc, s);
+  if (overlap(C, nc, A, span(M, K, lda, s)) || overlap(C, nc, W, span(N, K, ldw, s)) ||
       (epi != EE_EPI_NONE && overlap(C, nc, bias, (size_t)N * s)) ||
       (epi == EE_EPI_BIAS_RESIDUAL && overlap(C, nc, residual, nc)))
     return fail(EE_ERR_INVALID_ARG, "C overlaps an input");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  EE_LAUNCH("linear", st, gemm(dtype, A, W, bias, residual, M, N, K, epi, gelu, C, st));
+  const GemmPitch ld{(int)lda, (int)ldw, (int)ldc};
+  EE_LAUNCH("linear", st, gemm(dtype, A, W, bias, residual, M, N, K, ld, epi, gelu, C, st));
   return EE_OK;
+}
+
+ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual, int64_t M, int32_t N,
+                    int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, void* C, void* stream) {
+  return ee_linear_strided(A, K, W, K, bias, residual, M, N, K, dtype, epi, gelu, C, N, stream);
+}
+
+int64_t ee_preferred_row_pitch(int64_t cols, ee_dtype dtype) {
+  if (cols < 1 || !dtype_ok(dtype)) return 0;
+  return preferred_pitch(cols, dtype_size(dtype));
 }
 
 ee_status ee_linear_splitk_workspace_size(int64_t M, int32_t N, int32_t splits, size_t* bytes) {
@@ -717,7 +761,7 @@ ee_status ee_linear_splitk(const void* A, const void* W, const void* bias, const
   if (M < 0 || N < 1 || K < 1 || splits < 1 || splits > 64)
     return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1, 1 <= splits <= 64");
   if (M == 0) return EE_OK;
-  if (!gemm_f16_mfma_ok(M, N, K) || K % (64 * splits) != 0)
+  if (!gemm_f16_mfma_ok(M, N, K, dense(N, K), A, W) || K % (64 * splits) != 0)
     return fail(EE_ERR_UNSUPPORTED, "shape M=%lld N=%d K=%d splits=%d not supported", (long long)M, N, K, splits);
   EE_TRY(check_ptr(A, "A"));
   EE_TRY(check_ptr(W, "W"));
@@ -734,7 +778,8 @@ ee_status ee_linear_splitk(const void* A, const void* W, const void* bias, const
       overlap(ws, need, A, (size_t)M * K * 2) || overlap(ws, need, W, (size_t)N * K * 2))
     return fail(EE_ERR_INVALID_ARG, "C or the workspace overlaps an input");
   hipStream_t st = static_cast<hipStream_t>(stream);
-  EE_LAUNCH("linear", st, launch_gemm_f16_splitk(A, W, bias, residual, M, N, K, epi, gelu, C, splits, ws, st));
+  EE_LAUNCH("linear", st,
+            launch_gemm_f16_splitk(A, W, bias, residual, M, N, K, dense(N, K), epi, gelu, C, splits, ws, st));
   return EE_OK;
 }
 
@@ -751,7 +796,7 @@ ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t co
   const size_t n = (size_t)rows * cols * dtype_size(dtype);
   if (overlap(u, n, g, n)) return fail(EE_ERR_INVALID_ARG, "u and g overlap");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  EE_LAUNCH("bias_gelu", s, launch_bias_gelu(dtype, u, bias, rows, cols, gelu, g, s));
+  EE_LAUNCH("bias_gelu", s, launch_bias_gelu(dtype, u, bias, rows, cols, cols, gelu, g, s));
   return EE_OK;
 }
 

@@ -35,7 +35,12 @@
 //     (store_tile_staged); a direct per-element store covers N % 8 != 0.
 //   * Ragged M (and N): the buffer descriptors end at the last valid row, so
 //     out-of-range rows load zeros; their results are never stored.  K must be
-//     a multiple of 64, and 256 rows x K x 2 bytes must fit 32-bit offsets.
+//     a multiple of 64, and 256 rows at the operand's row pitch must fit
+//     32-bit offsets.
+//   * Row pitches (lda, ldw, ldc, in elements) may exceed the row lengths.
+//     A row stride that is a multiple of 32 KiB puts every row of a panel on
+//     the same few HBM channels: at K = 49152 (96 KiB rows) this kernel ran
+//     7% slower than with 128 bytes of padding per row of A and W.
 #include <algorithm>
 #include <type_traits>
 
@@ -148,7 +153,7 @@ template <int MF, int FM, int FN, int EPI>
 __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t (&acc)[FM][FN], float* __restrict__ stage,
                                                   int row0, int col0, int lane, const f16* __restrict__ bias,
                                                   const f16* __restrict__ R, f16* __restrict__ C, int M, int N,
-                                                  int gelu_form, float* __restrict__ Pp) {
+                                                  int ldc, int gelu_form, float* __restrict__ Pp) {
   using SE = StagedEpilogue<MF, FN>;
   constexpr int FPB = 1;  // fragment rows per band
   constexpr int PASSES = SE::kBandRows / SE::kRowsPerPass;
@@ -168,7 +173,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
     for (int it = 0; it < PASSES; ++it) {
       const int row = row0 + band * SE::kBandRows + it * SE::kRowsPerPass + rsub;
       if (EPI == EE_EPI_BIAS_RESIDUAL && row < M && col < N)
-        rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * N + col);
+        rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * ldc + col);
     }
 #pragma unroll
     for (int ii = 0; ii < FPB; ++ii)
@@ -197,7 +202,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
         half8 out;
 #pragma unroll
         for (int k = 0; k < 8; ++k) out[k] = (f16)(EPI == EE_EPI_BIAS_RESIDUAL ? v[k] + (float)rv[it][k] : v[k]);
-        *reinterpret_cast<half8*>(C + (int64_t)row * N + col) = out;
+        *reinterpret_cast<half8*>(C + (int64_t)row * ldc + col) = out;
       }
     }
     __syncthreads();  // the next band overwrites this wave's slice
@@ -209,7 +214,8 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
 template <int MF, int FM, int FN, int EPI>
 __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)[FM][FN], int row0, int col0, int lane,
                                            const f16* __restrict__ bias, const f16* __restrict__ R,
-                                           f16* __restrict__ C, int M, int N, int gelu_form, float* __restrict__ Pp) {
+                                           f16* __restrict__ C, int M, int N, int ldc, int gelu_form,
+                                           float* __restrict__ Pp) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int col = col0 + j * MF + lane % MF;
@@ -224,9 +230,9 @@ __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)
           Pp[(int64_t)row * N + col] = acc[i][j][e];
         } else if (row < M) {
           float v = acc[i][j][e] + bcol;
-          if (EPI == EE_EPI_BIAS_RESIDUAL) v += (float)R[(int64_t)row * N + col];
+          if (EPI == EE_EPI_BIAS_RESIDUAL) v += (float)R[(int64_t)row * ldc + col];
           if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
-          C[(int64_t)row * N + col] = (f16)v;
+          C[(int64_t)row * ldc + col] = (f16)v;
         }
       }
     }
@@ -234,11 +240,12 @@ __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)
 }
 
 template <int MF, int BM, int BN, int WGM, int WGN, int EPI>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16* __restrict__ A, const f16* __restrict__ W,
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16* __restrict__ A, int lda,
+                                                                 const f16* __restrict__ W, int ldw,
                                                                  const f16* __restrict__ bias,
                                                                  const f16* __restrict__ R, f16* __restrict__ C,
-                                                                 int M, int N, int K, int gelu_form, int tiles_m,
-                                                                 int tiles_n, float* __restrict__ P) {
+                                                                 int ldc, int M, int N, int K, int gelu_form,
+                                                                 int tiles_m, int tiles_n, float* __restrict__ P) {
   using FR = Frag<MF>;
   using acc_t = typename FR::acc_t;
   constexpr int NW = WGM * WGN;                // waves: WGM x WGN grid over the tile
@@ -269,20 +276,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
 #pragma unroll
   for (int j = 0; j < AJ; ++j) {
     const int r = wave * (BM / NW) + 8 * j + lr;
-    aoff[j] = (r * K + ((lp ^ lds_swizzle(r)) * 8)) * 2;
+    aoff[j] = (r * lda + ((lp ^ lds_swizzle(r)) * 8)) * 2;
   }
 #pragma unroll
   for (int j = 0; j < BJ; ++j) {
     const int r = wave * (BN / NW) + 8 * j + lr;
-    boff[j] = (r * K + ((lp ^ lds_swizzle(r)) * 8)) * 2;
+    boff[j] = (r * ldw + ((lp ^ lds_swizzle(r)) * 8)) * 2;
   }
   __amdgpu_buffer_rsrc_t arsrc, wrsrc;
   int m0 = 0, n0 = 0;
   auto set_tile = [&](int tile) {
     tile_origin<BM, BN>(tile, n_tiles, tiles_m, tiles_n, m0, n0);
-    arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * K), (short)0, min(BM, M - m0) * K * 2,
+    arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * lda), (short)0, min(BM, M - m0) * lda * 2,
                                               kBufferFlags);
-    wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * K), (short)0, min(BN, N - n0) * K * 2,
+    wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * ldw), (short)0, min(BN, N - n0) * ldw * 2,
                                               kBufferFlags);
   };
   // load q of a K tile: q < AJ -> rows of A, else rows of W
@@ -387,7 +394,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   using SE = StagedEpilogue<MF, FN>;
   constexpr bool kOverlap = NW * SE::kFloats * 4 <= STAGE * 2;
   static_assert(NW * SE::kFloats * 4 <= 2 * STAGE * 2, "epilogue staging exceeds the LDS ring");
-  const bool vec_ok = (N & 7) == 0 && ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(R)) & 15) == 0;
+  const bool vec_ok = (N & 7) == 0 && (ldc & 7) == 0 &&
+                      ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(R)) & 15) == 0;
   float* const stage_base = reinterpret_cast<float*>(kOverlap ? smem + STAGE : smem);
   int tile = blockIdx.x;
   if (tile >= n_tiles) return;
@@ -434,9 +442,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     float* const Pp = P + (int64_t)blockIdx.y * M * N;
     if (vec_ok)
       store_tile_staged<MF, FM, FN, EPI>(acc, stage_base + wave * SE::kFloats, row0, col0, lane, bias, R, C, M, N,
-                                         gelu_form, Pp);
+                                         ldc, gelu_form, Pp);
     else
-      store_tile<MF, FM, FN, EPI>(acc, row0, col0, lane, bias, R, C, M, N, gelu_form, Pp);
+      store_tile<MF, FM, FN, EPI>(acc, row0, col0, lane, bias, R, C, M, N, ldc, gelu_form, Pp);
     if (next >= n_tiles) break;
     tile = next;
     __syncthreads();  // every wave's staging is done before the ring is loaded again
@@ -462,8 +470,9 @@ int device_cus() {
 
 // max_wgs > 0: at most that many workgroups, each looping over tiles
 template <int MF, int BM, int BN, int WGM, int WGN>
-hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K, int epi,
-                      ee_gelu form, void* C, int splits, float* P, hipStream_t s, int max_wgs = 0) {
+hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K,
+                      const GemmPitch& ld, int epi, ee_gelu form, void* C, int splits, float* P, hipStream_t s,
+                      int max_wgs = 0) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int wgs = max_wgs > 0 ? std::min(tm * tn, max_wgs) : tm * tn;
   const dim3 grid((unsigned)wgs, (unsigned)splits), block(64 * WGM * WGN);
@@ -473,8 +482,8 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
   const f16* r = static_cast<const f16*>(R);
   f16* c = static_cast<f16*>(C);
 #define EE_GEMM_LAUNCH(E)                                                                                        \
-  hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E>), grid, block, 0, s, a, w, b, r, c, M, N, K, \
-                     (int)form, tm, tn, P)
+  hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E>), grid, block, 0, s, a, ld.a, w, ld.w, b, r, \
+                     c, ld.c, M, N, K, (int)form, tm, tn, P)
   switch (epi) {
     case EE_EPI_NONE: EE_GEMM_LAUNCH(EE_EPI_NONE); break;
     case EE_EPI_BIAS: EE_GEMM_LAUNCH(EE_EPI_BIAS); break;
@@ -492,7 +501,7 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
 template <int EPI, int V>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int splits, int64_t M, int N,
                                                           const f16* __restrict__ bias, const f16* __restrict__ R,
-                                                          f16* __restrict__ C, int gelu_form) {
+                                                          f16* __restrict__ C, int ldc, int gelu_form) {
   const int64_t per_row = N / V, total = M * per_row;
   for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int64_t row = i / per_row;
@@ -508,42 +517,46 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
 #pragma unroll
     for (int k = 0; k < V; ++k) {
       float x = v[k] + (kHasBias<EPI> ? (float)bias[col + k] : 0.f);
-      if (EPI == EE_EPI_BIAS_RESIDUAL) x += (float)R[row * N + col + k];
+      if (EPI == EE_EPI_BIAS_RESIDUAL) x += (float)R[row * ldc + col + k];
       if (EPI == EE_EPI_BIAS_GELU) x = gelu_f(x, gelu_form);
-      C[row * N + col + k] = (f16)x;
+      C[row * ldc + col + k] = (f16)x;
     }
   }
 }
 
 template <int EPI>
 hipError_t launch_reduce(const float* P, int splits, int64_t M, int N, const void* bias, const void* R, void* C,
-                         ee_gelu form, hipStream_t s) {
-  const bool vec = N % 8 == 0;
+                         int ldc, ee_gelu form, hipStream_t s) {
+  const bool vec = N % 8 == 0 && ldc % 8 == 0;
   const int64_t items = M * (vec ? N / 8 : N);
   const unsigned grid = (unsigned)std::min<int64_t>((items + 255) / 256, 4096);
   if (vec)
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI, 8>), dim3(grid), dim3(256), 0, s, P, splits, M, N,
-                       static_cast<const f16*>(bias), static_cast<const f16*>(R), static_cast<f16*>(C), (int)form);
+                       static_cast<const f16*>(bias), static_cast<const f16*>(R), static_cast<f16*>(C), ldc, (int)form);
   else
     hipLaunchKernelGGL((splitk_reduce_kernel<EPI, 1>), dim3(grid), dim3(256), 0, s, P, splits, M, N,
-                       static_cast<const f16*>(bias), static_cast<const f16*>(R), static_cast<f16*>(C), (int)form);
+                       static_cast<const f16*>(bias), static_cast<const f16*>(R), static_cast<f16*>(C), ldc, (int)form);
   return hipGetLastError();
 }
 
 }  // namespace
 
-bool gemm_f16_mfma_ok(int64_t M, int N, int K) {
-  return M >= 1 && M <= (1 << 30) && N >= 1 && K >= kBK && K % kBK == 0 && (int64_t)256 * K * 2 < (1ll << 31);
+bool gemm_f16_mfma_ok(int64_t M, int N, int K, const GemmPitch& ld, const void* A, const void* W) {
+  const bool pitches = ld.a >= K && ld.w >= K && ld.c >= N && ld.a % 8 == 0 && ld.w % 8 == 0 &&
+                       (int64_t)256 * std::max(ld.a, ld.w) * 2 < (1ll << 31);
+  const bool aligned = ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(W)) & 15) == 0;
+  return M >= 1 && M <= (1 << 30) && N >= 1 && K >= kBK && K % kBK == 0 && pitches && aligned;
 }
 
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
-                                int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
+                                int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_big >= 256)
-    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, epi, form, C, 1,
-                                                                      nullptr, s, EE_GEMM_PERSIST ? device_cus() : 0);
-  return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, epi, form, C, 1, nullptr, s);
+    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, ld, epi, form, C,
+                                                                      1, nullptr, s,
+                                                                      EE_GEMM_PERSIST ? device_cus() : 0);
+  return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, ld, epi, form, C, 1, nullptr, s);
 }
 
 // Measured at M = 32 on the GPT-3 decode shapes (weights streamed once): four
@@ -551,7 +564,7 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
 // FC2 237 vs 632, out 67 vs 171); two were slower than none wherever the
 // unsplit grid already had a workgroup per CU.
 int gemm_f16_splitk_choice(int64_t M, int N, int K, size_t scratch_bytes) {
-  if (M > 128 || !gemm_f16_mfma_ok(M, N, K)) return 1;
+  if (M > 128) return 1;
   const int64_t tiles = ((M + 127) / 128) * ((N + 127) / 128);
   for (int splits = 4; splits >= 2; splits /= 2) {
     const bool fits = K % (kBK * splits) == 0 && K / splits >= 4 * kBK &&
@@ -564,18 +577,21 @@ int gemm_f16_splitk_choice(int64_t M, int N, int K, size_t scratch_bytes) {
 size_t gemm_f16_splitk_bytes(int64_t M, int N, int splits) { return (size_t)splits * (size_t)M * (size_t)N * 4; }
 
 hipError_t launch_gemm_f16_splitk(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
-                                  int K, ee_epilogue epi, ee_gelu form, void* C, int splits, void* scratch,
-                                  hipStream_t s) {
+                                  int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, int splits,
+                                  void* scratch, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   float* P = static_cast<float*>(scratch);
-  hipError_t e = launch_cfg<32, 128, 128, 2, 2>(A, W, nullptr, nullptr, (int)M, N, K, kEpiPartial, form, nullptr,
-                                                splits, P, s);
+  // the partial sums are dense [splits][M][N]
+  const GemmPitch pld{ld.a, ld.w, N};
+  hipError_t e = launch_cfg<32, 128, 128, 2, 2>(A, W, nullptr, nullptr, (int)M, N, K, pld, kEpiPartial, form,
+                                                nullptr, splits, P, s);
   if (e != hipSuccess) return e;
   switch (epi) {
-    case EE_EPI_NONE: return launch_reduce<EE_EPI_NONE>(P, splits, M, N, bias, R, C, form, s);
-    case EE_EPI_BIAS: return launch_reduce<EE_EPI_BIAS>(P, splits, M, N, bias, R, C, form, s);
-    case EE_EPI_BIAS_RESIDUAL: return launch_reduce<EE_EPI_BIAS_RESIDUAL>(P, splits, M, N, bias, R, C, form, s);
-    case EE_EPI_BIAS_GELU: return launch_reduce<EE_EPI_BIAS_GELU>(P, splits, M, N, bias, R, C, form, s);
+    case EE_EPI_NONE: return launch_reduce<EE_EPI_NONE>(P, splits, M, N, bias, R, C, ld.c, form, s);
+    case EE_EPI_BIAS: return launch_reduce<EE_EPI_BIAS>(P, splits, M, N, bias, R, C, ld.c, form, s);
+    case EE_EPI_BIAS_RESIDUAL:
+      return launch_reduce<EE_EPI_BIAS_RESIDUAL>(P, splits, M, N, bias, R, C, ld.c, form, s);
+    case EE_EPI_BIAS_GELU: return launch_reduce<EE_EPI_BIAS_GELU>(P, splits, M, N, bias, R, C, ld.c, form, s);
   }
   return hipErrorInvalidValue;
 }

@@ -61,23 +61,34 @@ hipError_t launch_add_bias_residual_layernorm(ee_dtype dt, const void* u, const 
                                               hipStream_t s);
 
 // ---- bias_gelu.hip ----
-hipError_t launch_bias_gelu(ee_dtype dt, const void* u, const void* bias, int64_t rows, int cols,
+// u and g are [rows, ld] (ld >= cols, a multiple of 16 bytes)
+hipError_t launch_bias_gelu(ee_dtype dt, const void* u, const void* bias, int64_t rows, int cols, int ld,
                             ee_gelu form, void* g, hipStream_t s);
 
-// ---- gemm_f16.hip / gemm_f32.hip ----
-bool gemm_f16_mfma_ok(int64_t M, int N, int K);
+// ---- gemm_f16.hip / gemm_valu.hip ----
+// Row pitches, in elements, of a GEMM's operands: A [M, a], W [N, w], and
+// C and the residual R [M, c].
+struct GemmPitch {
+  int a, w, c;
+};
+// Whether the MFMA kernel takes this problem: K % 64 == 0, pitches of A and W
+// that are multiples of 8 (16-byte rows) and 16-byte aligned A and W.
+bool gemm_f16_mfma_ok(int64_t M, int N, int K, const GemmPitch& ld, const void* A, const void* W);
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M,
-                                int N, int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s);
+                                int N, int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C,
+                                hipStream_t s);
 // Split-K for small M: `splits` equal K ranges (K % (64 * splits) == 0) summed
 // into fp32 partials in scratch (gemm_f16_splitk_bytes), then reduced with the
-// epilogue.  gemm_f16_splitk_choice picks the split count (1 = do not split).
+// epilogue.  gemm_f16_splitk_choice picks the split count (1 = do not split)
+// for a problem gemm_f16_mfma_ok accepts.
 int gemm_f16_splitk_choice(int64_t M, int N, int K, size_t scratch_bytes);
 size_t gemm_f16_splitk_bytes(int64_t M, int N, int splits);
 hipError_t launch_gemm_f16_splitk(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
-                                  int K, ee_epilogue epi, ee_gelu form, void* C, int splits, void* scratch,
-                                  hipStream_t s);
+                                  int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, int splits,
+                                  void* scratch, hipStream_t s);
 hipError_t launch_gemm_valu(ee_dtype dt, const void* A, const void* W, const void* bias, const void* R,
-                            int64_t M, int N, int K, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s);
+                            int64_t M, int N, int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C,
+                            hipStream_t s);
 
 // ---- attention.hip ----
 bool attention_mfma_ok(ee_dtype dt, int head_dim);
