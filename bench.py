@@ -40,7 +40,7 @@ PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROOFLINE_KERNEL = "gemm_fc1"
 ROOFLINE_SYMBOL = "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, EE_EPI_BIAS_GELU>"
-ROOFLINE_MANGLED = "_ZN2ee12_GLOBAL__N_120gemm_f16_mfma_kernelILi16ELi256ELi256ELi2ELi2ELi3EEEvPKDF16_S3_S3_S3_PDF16_iiiiiiPf"
+ROOFLINE_MANGLED = "_ZN2ee12_GLOBAL__N_120gemm_f16_mfma_kernelILi16ELi256ELi256ELi2ELi2ELi3EEEvPKDF16_iS3_iS3_S3_PDF16_iiiiiiiPf"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fc1_gpt3-12l_pmc.json")
 GEMM_SOURCE = os.path.join(ROOT, "variable_length_padding_amd", "csrc", "gemm_f16.hip")
 
@@ -70,6 +70,9 @@ def _parse():
                     help="request-stream workload: batch size cap of both planners (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (scale reference for HBM byte counters)")
+    ap.add_argument("--residual", choices=("auto", "epilogue", "pass"), default="auto",
+                    help="where the pre-LN block adds its residuals: in the out/FC2 GEMM epilogues or in a "
+                         "separate pass (auto: the library's default, the epilogues)")
     ap.add_argument("--dense-weights", action="store_true",
                     help="weight matrices stored dense instead of at ee_preferred_row_pitch (ablation)")
     return ap.parse_args()
@@ -86,15 +89,16 @@ def _stored(args, params):
     return params if args.dense_weights else ee.pitched_weights(params)
 
 
-def _site_work(w, T, B, P, site):
+def _site_work(w, T, B, P, site, res_in_gemm=True):
     """(algorithmic flops, algorithmic HBM bytes) of one launch at a site, for
-    T rows run through the layer."""
+    T rows run through the layer (res_in_gemm: the out and FC2 GEMMs read the
+    residual in their epilogue)."""
     s = w.elem_bytes
     H, Hp, F = w.hidden, w.inner, w.ffn
     gemm = {"gemm_qkv": (H, 3 * Hp), "gemm_out": (Hp, H), "gemm_fc1": (H, F), "gemm_fc2": (F, H)}
     if site in gemm:
         K, N = gemm[site]
-        res = T * N * s if site in ("gemm_out", "gemm_fc2") else 0
+        res = T * N * s if res_in_gemm and site in ("gemm_out", "gemm_fc2") else 0
         return 2.0 * T * K * N, float((T * K + N * K + T * N) * s + res)
     if site in ("ln1", "ln2"):
         return 0.0, 2.0 * T * H * s
@@ -109,6 +113,10 @@ def _site_work(w, T, B, P, site):
     if site == "remove_heads":
         return 0.0, 2.0 * T * Hp * s
     if site in ("add_ln1", "add_ln2"):   # u and residual read, y written
+        return 0.0, 3.0 * T * H * s
+    if site == "res_ln2":                 # u and residual read, sum and LN(sum) written
+        return 0.0, 4.0 * T * H * s
+    if site == "res_add":                 # u and residual read, sum written
         return 0.0, 3.0 * T * H * s
     if site == "bias_gelu":
         return 0.0, 2.0 * T * F * s
@@ -434,7 +442,9 @@ def main():
     layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=dt, fuse_gelu=not args.no_fuse_gelu,
                        gelu=ee.GELU_ERF if bert else ee.GELU_TANH,
                        block=ee.BLOCK_BERT_POSTLN if bert else ee.BLOCK_GPT_PRELN,
-                       attention=ee.ATTN_PADDED if args.attention == "padded" else ee.ATTN_VARLEN)
+                       attention=ee.ATTN_PADDED if args.attention == "padded" else ee.ATTN_VARLEN,
+                       residual={"auto": ee.RESIDUAL_AUTO, "epilogue": ee.RESIDUAL_EPILOGUE,
+                                 "pass": ee.RESIDUAL_PASS}[args.residual])
               for p in params]
     ws = torch.empty(layers[0].workspace_size(B, P, T_run), dtype=torch.uint8, device=dev)
     y = torch.empty_like(x)
@@ -473,7 +483,7 @@ def main():
     for site, st in stats.items():
         n = st["launches"]
         avg_ms = st["total_ms"] / n
-        fl, by = _site_work(w, T_run, B, P, site)
+        fl, by = _site_work(w, T_run, B, P, site, res_in_gemm="res_ln2" not in stats)
         if site == "attention":
             fl = _attention_flops(w, run_lens, causal=not bert)
         k = {"launches_per_step": n / args.steps, "avg_ms": round(avg_ms, 5),
@@ -511,7 +521,7 @@ def main():
                    "hidden": w.hidden, "n_heads": w.n_heads, "head_dim": w.head_dim, "ffn": w.ffn,
                    "fuse_gelu": not args.no_fuse_gelu, "block": "bert-postln" if bert else "gpt-preln",
                    "attention": args.attention, "rows_run": T_run, "padding_removed": not args.no_pack,
-                   "weight_rows": "dense" if args.dense_weights else "preferred pitch"},
+                   "weight_rows": "dense" if args.dense_weights else "preferred pitch", "residual": args.residual},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "kernels": kernels,

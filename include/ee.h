@@ -98,6 +98,16 @@ typedef enum { EE_BLOCK_GPT_PRELN = 0, EE_BLOCK_BERT_POSTLN = 1 } ee_block;
  * Valid rows are the same either way. */
 typedef enum { EE_ATTN_VARLEN = 0, EE_ATTN_PADDED = 1 } ee_attention;
 
+/* Where the pre-LN block adds its two residuals (out projection + x, FC2 +
+ * h).  EPILOGUE: inside the GEMM's store, one rounding of acc + bias + residual.
+ * PASS: the GEMM stores acc + bias (rounded); a separate pass forms the rounded
+ * sum and, after the out projection, the second LayerNorm of it in the same
+ * pass.  At GPT-3 width and 4096 rows the two run at the same speed (the out
+ * GEMM gains what the passes' extra 200 MB per layer cost), so AUTO is
+ * EPILOGUE: one rounding, less traffic.  Post-LN blocks always add in their
+ * bias + residual + LayerNorm pass. */
+typedef enum { EE_RESIDUAL_AUTO = 0, EE_RESIDUAL_EPILOGUE = 1, EE_RESIDUAL_PASS = 2 } ee_residual;
+
 typedef struct {
   int32_t hidden;    /* H */
   int32_t n_heads;   /* nh */
@@ -109,6 +119,7 @@ typedef struct {
   int32_t fuse_gelu; /* 1: bias+GeLU in the FC1 GEMM epilogue; 0: separate bias+GeLU kernel */
   ee_block block;
   ee_attention attention;
+  ee_residual residual;  /* where a pre-LN layer adds its residuals (EE_RESIDUAL_AUTO if unsure) */
 } ee_layer_desc;
 
 /* Device pointers, all of the descriptor's dtype, borrowed (not copied) by

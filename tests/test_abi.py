@@ -36,7 +36,7 @@ def test_status_strings_and_version():
 
 def _desc(**kw):
     d = dict(hidden=64, n_heads=4, head_dim=16, ffn=256, ln_eps=1e-5, dtype=ee.F32, gelu=ee.GELU_TANH, fuse_gelu=1,
-             block=ee.BLOCK_GPT_PRELN, attention=ee.ATTN_VARLEN)
+             block=ee.BLOCK_GPT_PRELN, attention=ee.ATTN_VARLEN, residual=ee.RESIDUAL_AUTO)
     d.update(kw)
     return ee.LayerDesc(*[d[k] for k, _ in ee.LayerDesc._fields_])
 
@@ -54,7 +54,8 @@ def _create(desc, weights):
 @pytest.mark.parametrize("kw,status", [
     (dict(head_dim=24), 2), (dict(head_dim=256), 2), (dict(hidden=0), 1), (dict(ln_eps=0.0), 1),
     (dict(dtype=7), 1), (dict(gelu=5), 1), (dict(fuse_gelu=2), 1), (dict(hidden=66), 2),
-    (dict(hidden=65536 * 4, ffn=256), 2), (dict(block=2), 1), (dict(attention=3), 1),
+    (dict(hidden=65536 * 4, ffn=256), 2), (dict(block=2), 1), (dict(attention=3), 1), (dict(residual=3), 1),
+    (dict(residual=-1), 1),
 ])
 def test_layer_create_rejects_bad_descriptors(kw, status):
     st, h = _create(_desc(**kw), _weights())

@@ -19,12 +19,12 @@ pytestmark = pytest.mark.gpu
 
 
 class Decoder:
-    def __init__(self, w, seed, n_layers, prompts, max_new):
+    def __init__(self, w, seed, n_layers, prompts, max_new, residual=ee.RESIDUAL_AUTO):
         self.w = w
         dt = ee.F16 if w.dtype == "f16" else ee.F32
         self.params = [workloads.layer_params(w, seed, l, variant="affine") for l in range(n_layers)]
         self.layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, {k: v.to(DEV) for k, v in p.items()},
-                                dtype=dt) for p in self.params]
+                                dtype=dt, residual=residual) for p in self.params]
         caps = [n + max_new for n in prompts]
         self.slot_base = list(np.concatenate([[0], np.cumsum(caps)[:-1]]).astype(int))
         self.capacity = int(sum(caps)) + 7                      # a few slots nobody owns
@@ -89,10 +89,11 @@ def test_prefill_decode_and_mixed_steps(name, tol, ctol):
     assert torch.all(tail.view(torch.uint8) == 0xFF)
 
 
-def test_prefill_equals_padded_forward_bit_exact():
+@pytest.mark.parametrize("residual", [ee.RESIDUAL_EPILOGUE, ee.RESIDUAL_PASS])
+def test_prefill_equals_padded_forward_bit_exact(residual):
     w = workloads.get("gpt2-small")
     prompts = [17, 128, 1, 90]
-    dec = Decoder(w, 42, 2, prompts, max_new=0)
+    dec = Decoder(w, 42, 2, prompts, max_new=0, residual=residual)
     rows = [_token_rows(w, 200 + b, n) for b, n in enumerate(prompts)]
     x = torch.cat(rows).to(DEV)
     y = torch.empty_like(x)

@@ -18,12 +18,13 @@ from gpu_helpers import DEV, normwise_rel, say, to_host64, valid_mask
 pytestmark = pytest.mark.gpu
 
 
-def _run_layer(w, lens, x, params, fuse_gelu=True, gelu=ee.GELU_TANH, layers_params=None):
+def _run_layer(w, lens, x, params, fuse_gelu=True, gelu=ee.GELU_TANH, layers_params=None,
+               residual=ee.RESIDUAL_AUTO):
     dt = ee.F16 if w.dtype == "f16" else ee.F32
     plist = layers_params or [params]
     dev_params = [{k: v.to(DEV) for k, v in p.items()} for p in plist]
-    layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, dp, dtype=dt, gelu=gelu, fuse_gelu=fuse_gelu)
-              for dp in dev_params]
+    layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, dp, dtype=dt, gelu=gelu, fuse_gelu=fuse_gelu,
+                       residual=residual) for dp in dev_params]
     B, P, _ = x.shape
     ws = torch.empty(layers[0].workspace_size(B, P, sum(lens)), dtype=torch.uint8, device=DEV)
     xd = x.to(DEV)
@@ -99,20 +100,22 @@ def test_nan_pads_do_not_reach_valid_rows():
     assert torch.equal(y_r, y_n)
 
 
-def test_each_sequence_alone_matches_batch():
+@pytest.mark.parametrize("residual", [ee.RESIDUAL_EPILOGUE, ee.RESIDUAL_PASS])
+def test_each_sequence_alone_matches_batch(residual):
     """Sequences are independent: running one alone, unpadded, gives its rows of
     the batch bit for bit (every GEMM output element accumulates its K tiles in
     the same order whatever M and the tile shape are; attention is per
-    sequence, LayerNorm per row)."""
+    sequence, LayerNorm and the residual pass per row), in either residual
+    mode."""
     w = workloads.get("gpt2-small")
     lens = workloads.lengths(w, 21)
     x = workloads.activations(w, 21, w.batch, w.pad_len, lens)
     p = workloads.layer_params(w, 21, 0, variant="affine")
-    y = to_host64(_run_layer(w, lens, x, p))
+    y = to_host64(_run_layer(w, lens, x, p, residual=residual))
     for b in (0, 5):
         n = lens[b]
         w1 = dataclasses.replace(w, batch=1, pad_len=n)
-        y1 = to_host64(_run_layer(w1, [n], x[b:b + 1, :n].contiguous(), p))
+        y1 = to_host64(_run_layer(w1, [n], x[b:b + 1, :n].contiguous(), p, residual=residual))
         assert np.array_equal(y1[0], y[b, :n])
 
 

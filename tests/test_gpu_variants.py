@@ -98,10 +98,10 @@ def test_add_bias_residual_layernorm(dtype, H, tol):
     assert normwise_rel(to_host64(y), ref) <= tol
 
 
-def _run(w, lens, x, plist, block, attention, gelu=ee.GELU_TANH):
+def _run(w, lens, x, plist, block, attention, gelu=ee.GELU_TANH, residual=ee.RESIDUAL_AUTO):
     dt = ee.F16 if w.dtype == "f16" else ee.F32
     layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, {k: v.to(DEV) for k, v in p.items()}, dtype=dt,
-                       gelu=gelu, block=block, attention=attention) for p in plist]
+                       gelu=gelu, block=block, attention=attention, residual=residual) for p in plist]
     B, P, _ = x.shape
     ws = torch.empty(layers[0].workspace_size(B, P, sum(lens)), dtype=torch.uint8, device=DEV)
     xd = x.to(DEV)
@@ -165,16 +165,18 @@ def test_encoder_stack_and_nan_pads():
 
 
 @pytest.mark.parametrize("name", ["gpt2-small", "tiny-fp32"])
-def test_padding_kept_gives_the_same_valid_rows(name):
+@pytest.mark.parametrize("residual", [ee.RESIDUAL_EPILOGUE, ee.RESIDUAL_PASS])
+def test_padding_kept_gives_the_same_valid_rows(name, residual):
     """The result the method preserves: with right padding and the causal mask,
     running all B*P rows through the layers (padding kept) leaves the valid
-    rows exactly as the packed run computes them; only the work differs."""
+    rows exactly as the packed run computes them; only the work differs (in
+    either residual mode)."""
     w = workloads.get(name)
     lens = workloads.lengths(w, 77)
     x = workloads.activations(w, 77, w.batch, w.pad_len, lens, pad_fill="random")
     ps = [workloads.layer_params(w, 77, l, variant="affine") for l in range(2)]
-    y_rce = _run(w, lens, x, ps, ee.BLOCK_GPT_PRELN, ee.ATTN_VARLEN)
-    y_full = _run(w, [w.pad_len] * w.batch, x, ps, ee.BLOCK_GPT_PRELN, ee.ATTN_VARLEN)
+    y_rce = _run(w, lens, x, ps, ee.BLOCK_GPT_PRELN, ee.ATTN_VARLEN, residual=residual)
+    y_full = _run(w, [w.pad_len] * w.batch, x, ps, ee.BLOCK_GPT_PRELN, ee.ATTN_VARLEN, residual=residual)
     m = torch.from_numpy(valid_mask(lens, w.pad_len)).to(DEV)
     diff = (y_rce[m].float() - y_full[m].float()).abs().max().item()
     say(f"{name}: padding kept vs removed, max |diff| on valid rows {diff:.3e}")

@@ -32,6 +32,7 @@ GELU_TANH, GELU_ERF = 0, 1
 EPI_NONE, EPI_BIAS, EPI_BIAS_RESIDUAL, EPI_BIAS_GELU = 0, 1, 2, 3
 BLOCK_GPT_PRELN, BLOCK_BERT_POSTLN = 0, 1
 ATTN_VARLEN, ATTN_PADDED = 0, 1
+RESIDUAL_AUTO, RESIDUAL_EPILOGUE, RESIDUAL_PASS = 0, 1, 2
 MAX_BATCH = 512
 MAX_EXTEND_BATCH = 256
 
@@ -55,7 +56,7 @@ _STATUS = {0: "EE_OK", 1: "EE_ERR_INVALID_ARG", 2: "EE_ERR_UNSUPPORTED", 3: "EE_
 class LayerDesc(C.Structure):
     _fields_ = [("hidden", C.c_int32), ("n_heads", C.c_int32), ("head_dim", C.c_int32), ("ffn", C.c_int32),
                 ("ln_eps", C.c_float), ("dtype", C.c_int), ("gelu", C.c_int), ("fuse_gelu", C.c_int32),
-                ("block", C.c_int), ("attention", C.c_int)]
+                ("block", C.c_int), ("attention", C.c_int), ("residual", C.c_int)]
 
 
 WEIGHT_FIELDS = ("ln1_g", "ln1_b", "w_qkv", "b_qkv", "w_out", "b_out",
@@ -350,9 +351,9 @@ class Layer:
 
     def __init__(self, hidden: int, n_heads: int, head_dim: int, ffn: int, weights: Dict, dtype: int = F16,
                  ln_eps: float = 1e-5, gelu: int = GELU_TANH, fuse_gelu: bool = True, block: int = BLOCK_GPT_PRELN,
-                 attention: int = ATTN_VARLEN):
+                 attention: int = ATTN_VARLEN, residual: int = RESIDUAL_AUTO):
         self.desc = LayerDesc(hidden, n_heads, head_dim, ffn, ln_eps, dtype, gelu, 1 if fuse_gelu else 0, block,
-                              attention)
+                              attention, residual)
         self._weights = {k: weights[k] for k in WEIGHT_FIELDS}
         w = LayerWeights(*[_ptr(self._weights[k]) for k in WEIGHT_FIELDS],
                          *[_row_pitch(self._weights[k]) for k, _ in PITCH_FIELDS])

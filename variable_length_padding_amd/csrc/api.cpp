@@ -160,6 +160,8 @@ ee_status check_desc(const ee_layer_desc* d) {
     return fail(EE_ERR_INVALID_ARG, "unknown block %d", (int)d->block);
   if (d->attention != EE_ATTN_VARLEN && d->attention != EE_ATTN_PADDED)
     return fail(EE_ERR_INVALID_ARG, "unknown attention form %d", (int)d->attention);
+  if (d->residual != EE_RESIDUAL_AUTO && d->residual != EE_RESIDUAL_EPILOGUE && d->residual != EE_RESIDUAL_PASS)
+    return fail(EE_ERR_INVALID_ARG, "unknown residual mode %d", (int)d->residual);
   if (d->hidden < 1 || d->n_heads < 1 || d->ffn < 1)
     return fail(EE_ERR_INVALID_ARG, "hidden, n_heads and ffn must be >= 1");
   if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps)) return fail(EE_ERR_INVALID_ARG, "ln_eps must be finite and > 0");
@@ -181,13 +183,16 @@ ee_status check_desc(const ee_layer_desc* d) {
 bool desc_equal(const ee_layer_desc& a, const ee_layer_desc& b) {
   return a.hidden == b.hidden && a.n_heads == b.n_heads && a.head_dim == b.head_dim && a.ffn == b.ffn &&
          a.ln_eps == b.ln_eps && a.dtype == b.dtype && a.gelu == b.gelu && a.fuse_gelu == b.fuse_gelu &&
-         a.block == b.block && a.attention == b.attention;
+         a.block == b.block && a.attention == b.attention && a.residual == b.residual;
 }
 
 // ---------------------------------------------------------------- workspace
 struct Plan {
   size_t cu, token_src, pad2pack, x, ln, big, o, h, heads, o_heads, splitk, splitk_bytes, total;
 };
+
+// Whether the pre-LN residuals are added in a separate pass (EE_RESIDUAL_AUTO: in the epilogue).
+bool residual_pass(const ee_layer_desc& d) { return d.residual == EE_RESIDUAL_PASS; }
 
 // split-K partial sums of the small-M GEMMs of an extend step
 constexpr size_t kSplitkScratch = size_t(64) << 20;
@@ -305,6 +310,15 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, hi
     EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
     EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
     EE_TRY(attn(big, o, true));
+    if (residual_pass(d)) {
+      // h = (o W_out^T + b_out) + x and ln = LN2(h); x = (g W_fc2^T + b_fc2) + h
+      EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, nullptr, T, H, Hp, ld_out, EE_EPI_BIAS, d.gelu, h, s, sk, skb));
+      EE_LAUNCH("res_ln2", s, launch_residual_add_layernorm(d.dtype, h, x, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
+      EE_TRY(fc1(ln));
+      EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, nullptr, T, H, F, ld_fc2, EE_EPI_BIAS, d.gelu, x, s, sk, skb));
+      EE_LAUNCH("res_add", s, launch_residual_add_layernorm(d.dtype, x, h, x, nullptr, nullptr, T, H, 0.f, nullptr, s));
+      return EE_OK;
+    }
     EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, ld_out, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb));
     EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
     EE_TRY(fc1(ln));

@@ -56,6 +56,10 @@ hipError_t launch_cache_attention(ee_dtype dt, const void* qkv, const ExtendArg&
 int layernorm_max_hidden(ee_dtype dt);
 hipError_t launch_layernorm(ee_dtype dt, const void* x, const void* g, const void* b, int64_t rows, int H,
                             float eps, void* y, hipStream_t s);
+// sum = x + r (rounded to the storage type; sum may be x), then y = LN(sum)
+// when g and b are given, else only the sum.
+hipError_t launch_residual_add_layernorm(ee_dtype dt, const void* x, const void* r, void* sum, const void* g,
+                                         const void* b, int64_t rows, int H, float eps, void* y, hipStream_t s);
 hipError_t launch_add_bias_residual_layernorm(ee_dtype dt, const void* u, const void* bias, const void* res,
                                               const void* g, const void* b, int64_t rows, int H, float eps, void* y,
                                               hipStream_t s);

@@ -46,8 +46,12 @@ struct Vec16<float> {
 // A workgroup walks rows blockIdx.x, +gridDim.x, ...; the next row's vectors
 // are requested before the current row's two reductions and store, so the
 // loads of one row overlap the barriers and stores of the previous one.
-template <typename T, int VPT>
-__global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restrict__ x, const T* __restrict__ gamma,
+// ADD: the row is x + r, rounded to the storage type and written to `sum`
+// (which may be x itself: each element is read, then written, by one thread)
+// before it is normalised; NORM = false stops there (a plain residual add).
+template <typename T, int VPT, bool ADD, bool NORM>
+__global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* x, const T* __restrict__ r, T* sum,
+                                                               const T* __restrict__ gamma,
                                                                const T* __restrict__ beta, int64_t rows, int H,
                                                                float eps, T* __restrict__ y) {
   typedef typename Vec16<T>::type V;
@@ -55,61 +59,84 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* __restri
   __shared__ float s_red[kLnThreads / kWave];
   const int nvec = H / E;
   const float inv_h = 1.0f / (float)H;
-  V cur[VPT], nxt[VPT];
-  auto load = [&](V (&dst)[VPT], int64_t row) {
+  V cur[VPT], nxt[VPT], rcur[ADD ? VPT : 1], rnxt[ADD ? VPT : 1];
+  auto load = [&](V (&dst)[VPT], V (&rdst)[ADD ? VPT : 1], int64_t row) {
     const V* xr = reinterpret_cast<const V*>(x + row * H);
-#pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int c = threadIdx.x + i * kLnThreads;
-      if (c < nvec) dst[i] = __builtin_nontemporal_load(xr + c);
-    }
-  };
-  int64_t row = blockIdx.x;
-  if (row < rows) load(cur, row);
-  for (; row < rows; row += gridDim.x) {
-    const int64_t next = row + gridDim.x;
-    if (next < rows) load(nxt, next);
-    float s = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (threadIdx.x + i * kLnThreads < nvec)
-#pragma unroll
-        for (int e = 0; e < E; ++e) s += to_f32(cur[i][e]);
-    const float mean = block_sum(s, s_red) * inv_h;
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPT; ++i)
-      if (threadIdx.x + i * kLnThreads < nvec)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float d = to_f32(cur[i][e]) - mean;
-          q += d * d;
-        }
-    const float rstd = 1.0f / sqrtf(block_sum(q, s_red) * inv_h + eps);
-    V* yr = reinterpret_cast<V*>(y + row * H);
-    const V* gv = reinterpret_cast<const V*>(gamma);
-    const V* bv = reinterpret_cast<const V*>(beta);
+    const V* rr = reinterpret_cast<const V*>(r + row * H);
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = threadIdx.x + i * kLnThreads;
       if (c < nvec) {
-        const V g = gv[c], b = bv[c];
-        V o;
+        dst[i] = __builtin_nontemporal_load(xr + c);
+        if constexpr (ADD) rdst[i] = __builtin_nontemporal_load(rr + c);
+      }
+    }
+  };
+  int64_t row = blockIdx.x;
+  if (row < rows) load(cur, rcur, row);
+  for (; row < rows; row += gridDim.x) {
+    const int64_t next = row + gridDim.x;
+    if (next < rows) load(nxt, rnxt, next);
+    if constexpr (ADD) {
+      V* sr = reinterpret_cast<V*>(sum + row * H);
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = from_f32<T>((to_f32(cur[i][e]) - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
-        yr[c] = o;
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        if (c < nvec) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) cur[i][e] = from_f32<T>(to_f32(cur[i][e]) + to_f32(rcur[i][e]));
+          sr[c] = cur[i];
+        }
+      }
+    }
+    if constexpr (NORM) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (threadIdx.x + i * kLnThreads < nvec)
+#pragma unroll
+          for (int e = 0; e < E; ++e) s += to_f32(cur[i][e]);
+      const float mean = block_sum(s, s_red) * inv_h;
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+        if (threadIdx.x + i * kLnThreads < nvec)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float d = to_f32(cur[i][e]) - mean;
+            q += d * d;
+          }
+      const float rstd = 1.0f / sqrtf(block_sum(q, s_red) * inv_h + eps);
+      V* yr = reinterpret_cast<V*>(y + row * H);
+      const V* gv = reinterpret_cast<const V*>(gamma);
+      const V* bv = reinterpret_cast<const V*>(beta);
+#pragma unroll
+      for (int i = 0; i < VPT; ++i) {
+        const int c = threadIdx.x + i * kLnThreads;
+        if (c < nvec) {
+          const V g = gv[c], b = bv[c];
+          V o;
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            o[e] = from_f32<T>((to_f32(cur[i][e]) - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
+          yr[c] = o;
+        }
       }
     }
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) cur[i] = nxt[i];
+    for (int i = 0; i < VPT; ++i) {
+      cur[i] = nxt[i];
+      if constexpr (ADD) rcur[i] = rnxt[i];
+    }
   }
 }
 
 // One wave per row (4 rows per workgroup): the row is held in registers in
 // its storage type (VPL 16-byte vectors per lane), the two reductions are wave
-// shuffles, so rows never wait on each other at a barrier.
-template <typename T, int VPL>
-__global__ __launch_bounds__(kLnThreads) void layernorm_wave_kernel(const T* __restrict__ x,
+// shuffles, so rows never wait on each other at a barrier.  ADD and NORM as in
+// layernorm_kernel.
+template <typename T, int VPL, bool ADD, bool NORM>
+__global__ __launch_bounds__(kLnThreads) void layernorm_wave_kernel(const T* x, const T* __restrict__ r, T* sum,
                                                                     const T* __restrict__ gamma,
                                                                     const T* __restrict__ beta, int64_t rows,
                                                                     int H, float eps, T* __restrict__ y) {
@@ -128,35 +155,52 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_wave_kernel(const T* __r
       const int c = lane + i * kWave;
       if (c < nvec) v[i] = __builtin_nontemporal_load(xr + c);
     }
-    float s = 0.f;
+    if constexpr (ADD) {
+      const V* rr = reinterpret_cast<const V*>(r + row * H);
+      V* sr = reinterpret_cast<V*>(sum + row * H);
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (lane + i * kWave < nvec)
+      for (int i = 0; i < VPL; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nvec) {
+          const V rv = __builtin_nontemporal_load(rr + c);
 #pragma unroll
-        for (int e = 0; e < E; ++e) s += to_f32(v[i][e]);
-    const float mean = wave_sum(s) * inv_h;
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-      if (lane + i * kWave < nvec)
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float d = to_f32(v[i][e]) - mean;
-          q += d * d;
+          for (int e = 0; e < E; ++e) v[i][e] = from_f32<T>(to_f32(v[i][e]) + to_f32(rv[e]));
+          sr[c] = v[i];
         }
-    const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_h + eps);
-    V* yr = reinterpret_cast<V*>(y + row * H);
-    const V* gv = reinterpret_cast<const V*>(gamma);
-    const V* bv = reinterpret_cast<const V*>(beta);
+      }
+    }
+    if constexpr (NORM) {
+      float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-      const int c = lane + i * kWave;
-      if (c < nvec) {
-        const V g = gv[c], b = bv[c];
-        V o;
+      for (int i = 0; i < VPL; ++i)
+        if (lane + i * kWave < nvec)
 #pragma unroll
-        for (int e = 0; e < E; ++e) o[e] = from_f32<T>((to_f32(v[i][e]) - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
-        yr[c] = o;
+          for (int e = 0; e < E; ++e) s += to_f32(v[i][e]);
+      const float mean = wave_sum(s) * inv_h;
+      float q = 0.f;
+#pragma unroll
+      for (int i = 0; i < VPL; ++i)
+        if (lane + i * kWave < nvec)
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float d = to_f32(v[i][e]) - mean;
+            q += d * d;
+          }
+      const float rstd = 1.0f / sqrtf(wave_sum(q) * inv_h + eps);
+      V* yr = reinterpret_cast<V*>(y + row * H);
+      const V* gv = reinterpret_cast<const V*>(gamma);
+      const V* bv = reinterpret_cast<const V*>(beta);
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int c = lane + i * kWave;
+        if (c < nvec) {
+          const V g = gv[c], b = bv[c];
+          V o;
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            o[e] = from_f32<T>((to_f32(v[i][e]) - mean) * rstd * to_f32(g[e]) + to_f32(b[e]));
+          yr[c] = o;
+        }
       }
     }
   }
@@ -242,41 +286,59 @@ hipError_t launch_abrln_t(const void* u, const void* bias, const void* res, cons
   return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_ln_t(const void* x, const void* g, const void* b, int64_t rows, int H, float eps, void* y,
-                       hipStream_t s) {
+// y = LN(x) (r == nullptr), or sum = x + r then y = LN(sum) (gamma != nullptr)
+// or only sum = x + r (gamma == nullptr).
+template <typename T, bool ADD, bool NORM>
+hipError_t launch_ln_mode(const T* xp, const T* rp, T* sp, const T* gp, const T* bp, int64_t rows, int H, float eps,
+                          T* yp, hipStream_t s) {
   const int nvec = H / Vec16<T>::n;
-  // block kernel: a few workgroups per CU, each walking several rows
-  const unsigned grid = (unsigned)(rows > 2048 ? 2048 : rows);
-  const T* xp = static_cast<const T*>(x);
-  const T* gp = static_cast<const T*>(g);
-  const T* bp = static_cast<const T*>(b);
-  T* yp = static_cast<T*>(y);
   if (nvec <= 8 * kWave) {  // narrow rows: one wave per row
     const int64_t wgs = (rows + 3) / 4;
     const dim3 wg((unsigned)(wgs > (1 << 20) ? (1 << 20) : wgs)), blk(kLnThreads);
     const int vpl = (nvec + kWave - 1) / kWave;
+#define EE_LN_WAVE(V) \
+  hipLaunchKernelGGL((layernorm_wave_kernel<T, V, ADD, NORM>), wg, blk, 0, s, xp, rp, sp, gp, bp, rows, H, eps, yp)
     if (vpl <= 1)
-      hipLaunchKernelGGL((layernorm_wave_kernel<T, 1>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+      EE_LN_WAVE(1);
     else if (vpl <= 2)
-      hipLaunchKernelGGL((layernorm_wave_kernel<T, 2>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+      EE_LN_WAVE(2);
     else if (vpl <= 4)
-      hipLaunchKernelGGL((layernorm_wave_kernel<T, 4>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+      EE_LN_WAVE(4);
     else
-      hipLaunchKernelGGL((layernorm_wave_kernel<T, 8>), wg, blk, 0, s, xp, gp, bp, rows, H, eps, yp);
+      EE_LN_WAVE(8);
+#undef EE_LN_WAVE
     return hipGetLastError();
   }
+  // block kernel: a few workgroups per CU, each walking several rows
+  const dim3 grid((unsigned)(rows > 2048 ? 2048 : rows)), blk(kLnThreads);
+#define EE_LN_BLOCK(V) \
+  hipLaunchKernelGGL((layernorm_kernel<T, V, ADD, NORM>), grid, blk, 0, s, xp, rp, sp, gp, bp, rows, H, eps, yp)
   if (nvec <= 256)
-    hipLaunchKernelGGL((layernorm_kernel<T, 1>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+    EE_LN_BLOCK(1);
   else if (nvec <= 512)
-    hipLaunchKernelGGL((layernorm_kernel<T, 2>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+    EE_LN_BLOCK(2);
   else if (nvec <= 1024)
-    hipLaunchKernelGGL((layernorm_kernel<T, 4>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+    EE_LN_BLOCK(4);
   else if (nvec <= 2048)
-    hipLaunchKernelGGL((layernorm_kernel<T, 8>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+    EE_LN_BLOCK(8);
   else
-    hipLaunchKernelGGL((layernorm_kernel<T, 16>), dim3(grid), dim3(kLnThreads), 0, s, xp, gp, bp, rows, H, eps, yp);
+    EE_LN_BLOCK(16);
+#undef EE_LN_BLOCK
   return hipGetLastError();
+}
+
+template <typename T>
+hipError_t launch_ln_t(const void* x, const void* r, void* sum, const void* g, const void* b, int64_t rows, int H,
+                       float eps, void* y, hipStream_t s) {
+  const T* xp = static_cast<const T*>(x);
+  const T* rp = static_cast<const T*>(r);
+  T* sp = static_cast<T*>(sum);
+  const T* gp = static_cast<const T*>(g);
+  const T* bp = static_cast<const T*>(b);
+  T* yp = static_cast<T*>(y);
+  if (!r) return launch_ln_mode<T, false, true>(xp, rp, sp, gp, bp, rows, H, eps, yp, s);
+  if (g) return launch_ln_mode<T, true, true>(xp, rp, sp, gp, bp, rows, H, eps, yp, s);
+  return launch_ln_mode<T, true, false>(xp, rp, sp, gp, bp, rows, H, eps, yp, s);
 }
 
 }  // namespace
@@ -286,7 +348,15 @@ int layernorm_max_hidden(ee_dtype dt) { return 16 * kLnThreads * (dt == EE_F16 ?
 hipError_t launch_layernorm(ee_dtype dt, const void* x, const void* g, const void* b, int64_t rows, int H, float eps,
                             void* y, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  return dt == EE_F16 ? launch_ln_t<f16>(x, g, b, rows, H, eps, y, s) : launch_ln_t<float>(x, g, b, rows, H, eps, y, s);
+  return dt == EE_F16 ? launch_ln_t<f16>(x, nullptr, nullptr, g, b, rows, H, eps, y, s)
+                      : launch_ln_t<float>(x, nullptr, nullptr, g, b, rows, H, eps, y, s);
+}
+
+hipError_t launch_residual_add_layernorm(ee_dtype dt, const void* x, const void* r, void* sum, const void* g,
+                                         const void* b, int64_t rows, int H, float eps, void* y, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  return dt == EE_F16 ? launch_ln_t<f16>(x, r, sum, g, b, rows, H, eps, y, s)
+                      : launch_ln_t<float>(x, r, sum, g, b, rows, H, eps, y, s);
 }
 
 hipError_t launch_add_bias_residual_layernorm(ee_dtype dt, const void* u, const void* bias, const void* res,
