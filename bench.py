@@ -39,8 +39,8 @@ METRIC = "valid tokens/s per GPT layer fwd (packed) + % HBM/MFMA roofline, 1 GPU
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROOFLINE_KERNEL = "gemm_fc1"
-ROOFLINE_SYMBOL = "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, EE_EPI_BIAS_GELU>"
-ROOFLINE_MANGLED = "_ZN2ee12_GLOBAL__N_120gemm_f16_mfma_kernelILi16ELi256ELi256ELi2ELi2ELi3EEEvPKDF16_iS3_iS3_S3_PDF16_iiiiiiiPf"
+ROOFLINE_SYMBOL = "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, EE_EPI_BIAS_GELU, 2>"
+ROOFLINE_MANGLED = "_ZN2ee12_GLOBAL__N_120gemm_f16_mfma_kernelILi16ELi256ELi256ELi2ELi2ELi3ELi2EEEvPKDF16_iS3_iS3_S3_PDF16_iiiiiiiPf"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_fc1_gpt3-12l_pmc.json")
 GEMM_SOURCE = os.path.join(ROOT, "variable_length_padding_amd", "csrc", "gemm_f16.hip")
 

@@ -128,7 +128,8 @@ def _small_ints(shape, lo=-2, hi=2):
 @pytest.mark.parametrize("M,N,K", [(1, 64, 64), (37, 96, 128), (300, 256, 192), (516, 2304, 768),
                                    (1000, 1000, 640), (4112, 768, 3072), (2048, 4096, 12288),
                                    (4100, 4200, 320), (4096, 4096, 1024), (4096, 4096, 64), (4300, 4096, 192),
-                                   (4096, 4104, 128), (4096, 4099, 64)])
+                                   (4096, 4104, 128), (4096, 4099, 64), (4096, 4096, 256), (4096, 4352, 384),
+                                   (4096, 4096, 12288)])
 @pytest.mark.parametrize("epi", [ee.EPI_NONE, ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL])
 def test_gemm_integer_exact(M, N, K, epi):
     """Small-integer fp16 operands: every product and partial sum is an integer
@@ -152,6 +153,24 @@ def test_gemm_integer_exact(M, N, K, epi):
     got = C.cpu().numpy()
     assert np.array_equal(got.view(np.uint16), ref16.view(np.uint16)), \
         f"{np.count_nonzero(got != ref16)} of {got.size} differ"
+
+
+@pytest.mark.parametrize("K", [32768, 49152 + 64])
+def test_gemm_integer_exact_long_k(K):
+    """Long K ranges (>= 32768) take the three-W-stage ring of the 256 x 256 tile
+    (W requested two K tiles ahead): bit-exact on small-integer operands, checked
+    on sampled rows (rows are independent), bias + residual epilogue."""
+    M, N = 4096, 4096
+    A, W = _small_ints((M, K)), _small_ints((N, K))
+    bias, R = _small_ints((N,)), _small_ints((M, N), -8, 8)
+    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    ee.ee_linear(A.to(DEV), W.to(DEV), bias.to(DEV), R.to(DEV), ee.EPI_BIAS_RESIDUAL, C)
+    torch.cuda.synchronize()
+    rows = [0, 1, 255, 256, 2047, 3840, 4095]
+    exact = A[rows].double().numpy() @ W.double().numpy().T + bias.double().numpy() + R[rows].double().numpy()
+    assert np.abs(exact).max() < 2 ** 24
+    got = C[rows].cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(1, 1024, 1024, 2), (32, 12288, 4096, 8), (100, 4104, 1024, 4),

@@ -62,6 +62,13 @@ namespace {
 #ifndef EE_GEMM_PERSIST
 #define EE_GEMM_PERSIST 1
 #endif
+// Large problems: K ranges from this length on use three W stages in the LDS
+// ring (W requested two K tiles ahead, A one), shorter ones two (both one
+// ahead).  Three measured 1.7% faster on FC2 (K = 49152, where both operands
+// stream from HBM) and 1.6% slower on the QKV GEMM (K = 12288).
+#ifndef EE_GEMM_DEEP_W_K
+#define EE_GEMM_DEEP_W_K 32768
+#endif
 
 constexpr int kBK = 64;
 // Split-K partial store (internal): fp32 sums of one K range, no epilogue.
@@ -88,6 +95,17 @@ constexpr int kBufferFlags = 0x00020000;
 // only waits for LDS instructions (lgkmcnt), and the compiler does not count
 // a direct-to-LDS load as an LDS write.  The memory clobber keeps LDS reads below it.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Workgroup barrier that lets this wave's newest N direct-to-LDS loads stay in
+// flight: it waits for this wave's LDS reads (their stage may be refilled right
+// after) and all older loads, then s_barrier.  (Direct-to-LDS loads retire in
+// issue order among themselves.)  __syncthreads cannot be used here: its
+// fence makes the compiler wait for every load.
+template <int N>
+__device__ __forceinline__ void barrier_after_loads() {
+  static_assert(N == 8, "add the count");
+  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // Tile origin of this workgroup: XCD-contiguous ranges of workgroup ids,
 // walked in groups of 4 M-tiles (see the file comment).
@@ -239,7 +257,7 @@ __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)
   }
 }
 
-template <int MF, int BM, int BN, int WGM, int WGN, int EPI>
+template <int MF, int BM, int BN, int WGM, int WGN, int EPI, int WDEPTH>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16* __restrict__ A, int lda,
                                                                  const f16* __restrict__ W, int ldw,
                                                                  const f16* __restrict__ bias,
@@ -253,9 +271,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   constexpr int FM = WTM / MF, FN = WTN / MF;
   constexpr int NSTEP = kBK / FR::kK;          // MFMA K steps per K tile (4 or 2)
   constexpr int AJ = BM / (8 * NW), BJ = BN / (8 * NW);  // direct-to-LDS loads per wave per K tile (8 rows each)
-  constexpr int STAGE = (BM + BN) * kBK;     // halves per LDS stage
+  constexpr int ASZ = BM * kBK, WSZ = BN * kBK;  // halves per A / W stage
   static_assert(NSTEP == 2 || NSTEP == 4, "two or four K steps per K tile");
-  __shared__ __attribute__((aligned(16))) f16 smem[2 * STAGE];
+  // LDS ring: 2 A stages and WD W stages.  WD == 2: [A0 W0 | A1 W1].  WD == 3:
+  // [A0 | W0 | W1 | A1 | W2], so that A1 and W2 are adjacent: the epilogue
+  // stages through them while the next tile's A0, W0 and W1 load.
+  constexpr int WD = (BM == 256 && BN == 256 && BJ == 8) ? WDEPTH : 2;
+  static_assert(WD == 2 || WD == 3, "two or three W stages");
+  constexpr int RING = 2 * ASZ + WD * WSZ;
+  __shared__ __attribute__((aligned(16))) f16 smem[RING];
+  auto a_off = [](int st) { return WD == 2 ? st * (ASZ + WSZ) : (st ? ASZ + 2 * WSZ : 0); };
+  auto w_off = [](int st) { return WD == 2 ? st * (ASZ + WSZ) + ASZ : (st == 2 ? 2 * ASZ + 2 * WSZ : ASZ + st * WSZ); };
 
   // split-K: workgroup row y of the grid sums the y-th of gridDim.y equal K ranges
   const int k_len = K / (int)gridDim.y, kbeg = (int)blockIdx.y * k_len;
@@ -292,19 +318,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * ldw), (short)0, min(BN, N - n0) * ldw * 2,
                                               kBufferFlags);
   };
-  // load q of a K tile: q < AJ -> rows of A, else rows of W
-  auto dma_one = [&](int stage, int k0, int q) {
+  // load q of a tile's A rows (q < AJ, K offset ka into A stage as) or of its
+  // W rows (K offset kw into W stage ws); A loads are issued before W loads
+  auto dma_one = [&](int as, int ka, int ws, int kw, int q) {
     if (q < AJ) {
-      f16* sa = smem + stage * STAGE + (wave * (BM / NW) + 8 * q) * kBK;
-      buffer_load_lds16(arsrc, sa, aoff[q], (kbeg + k0) * 2);
+      f16* sa = smem + a_off(as) + (wave * (BM / NW) + 8 * q) * kBK;
+      buffer_load_lds16(arsrc, sa, aoff[q], (kbeg + ka) * 2);
     } else {
-      f16* sb = smem + stage * STAGE + BM * kBK + (wave * (BN / NW) + 8 * (q - AJ)) * kBK;
-      buffer_load_lds16(wrsrc, sb, boff[q - AJ], (kbeg + k0) * 2);
+      f16* sb = smem + w_off(ws) + (wave * (BN / NW) + 8 * (q - AJ)) * kBK;
+      buffer_load_lds16(wrsrc, sb, boff[q - AJ], (kbeg + kw) * 2);
     }
   };
-  auto dma = [&](int stage, int k0) {
+  auto dma_a = [&](int as, int ka) {
 #pragma unroll
-    for (int q = 0; q < AJ + BJ; ++q) dma_one(stage, k0, q);
+    for (int q = 0; q < AJ; ++q) dma_one(as, ka, 0, 0, q);
+  };
+  auto dma_w = [&](int ws, int kw) {
+#pragma unroll
+    for (int q = AJ; q < AJ + BJ; ++q) dma_one(0, 0, ws, kw, q);
   };
 
   // ---- wave / lane roles for the MFMA fragments.  Fragment rows are
@@ -313,22 +344,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   const int kg = lane / MF;  // which 8-wide K group of an MFMA step this lane feeds
   const int rsw = lds_swizzle(lane & 15);
   const int abase = (wm * WTM + lane % MF) * kBK;
-  const int bbase = BM * kBK + (wn * WTN + lane % MF) * kBK;
+  const int bbase = (wn * WTN + lane % MF) * kBK;
   // Reads are issued in the order the MFMAs below consume them (a0, b0..bN, a1..aM),
   // so each MFMA waits only for its own operands.
-  auto frag_one = [&](int stage, int kk, int r, half8 (&af)[FM], half8 (&bf)[FN]) {
-    const f16* s = smem + stage * STAGE;
+  auto frag_one = [&](int as, int ws, int kk, int r, half8 (&af)[FM], half8 (&bf)[FN]) {
+    const f16* sa = smem + a_off(as);
+    const f16* sw = smem + w_off(ws);
     const int ch = ((kk * (FR::kK / 8) + kg) ^ rsw) * 8;
     if (r == 0)
-      af[0] = *reinterpret_cast<const half8*>(s + abase + ch);
+      af[0] = *reinterpret_cast<const half8*>(sa + abase + ch);
     else if (r <= FN)
-      bf[r - 1] = *reinterpret_cast<const half8*>(s + bbase + (r - 1) * MF * kBK + ch);
+      bf[r - 1] = *reinterpret_cast<const half8*>(sw + bbase + (r - 1) * MF * kBK + ch);
     else
-      af[r - FN] = *reinterpret_cast<const half8*>(s + abase + (r - FN) * MF * kBK + ch);
+      af[r - FN] = *reinterpret_cast<const half8*>(sa + abase + (r - FN) * MF * kBK + ch);
   };
-  auto frags = [&](int stage, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
+  auto frags = [&](int as, int ws, int kk, half8 (&af)[FM], half8 (&bf)[FN]) {
 #pragma unroll
-    for (int r = 0; r < FM + FN; ++r) frag_one(stage, kk, r, af, bf);
+    for (int r = 0; r < FM + FN; ++r) frag_one(as, ws, kk, r, af, bf);
   };
 
   acc_t acc[FM][FN];
@@ -339,13 +371,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
       for (int j = 0; j < FN; ++j) acc[i][j] = FR::mfma(af[i], bf[j], acc[i][j]);
   };
 
-  // ---- main loop.  Stage kt&1 holds K tile kt.  The barrier at the end of
-  // tile kt both publishes tile kt+1 (each wave waited for its own loads) and
-  // retires every read of stage kt&1, which then receives tile kt+2 (clamped
-  // to the last tile: a redundant load into a stage nobody reads again keeps
-  // the loop body free of branches).  The MFMAs of the tile's last K step
-  // issue after the barrier, from fragments already in registers, while the
-  // next tile's first fragments and the new loads are in flight.
+  // ---- main loop.  A stage kt%2 and W stage kt%WD hold K tile kt.  The
+  // barrier at the end of tile kt both publishes tile kt+1 (each wave waited
+  // for its own loads of it) and retires every read of those stages, which
+  // then receive A of tile kt+2 and W of tile kt+WD (clamped to the last tile:
+  // a redundant load into a stage nobody reads again keeps the loop body free
+  // of branches).  With WD == 3 a W load has two K tiles of MFMAs to land: W
+  // streams from HBM, while A (the activations) mostly hits in the caches.
+  // The MFMAs of the tile's last K step issue after the barrier, from
+  // fragments already in registers, while the next tile's first fragments
+  // and the new loads are in flight.
   //
   // Within a K step the order is written out and fenced with sched_barrier:
   // the LDS reads of the next step are spread evenly over the MFMAs (reads in
@@ -355,19 +390,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   constexpr int NF = FM + FN;  // LDS reads per K step
   constexpr int NM = FM * FN;  // MFMAs per K step
   constexpr int NL = AJ + BJ;  // direct-to-LDS loads per K tile
-  // MFMAs of step X interleaved with the reads of step (rstage, rkk) into Y,
-  // and with loads of K offset dk into stage dstage when dk >= 0.
-  // (with_dma is a compile-time flag so the step stays one basic block)
-  auto step = [&](auto with_dma, const half8 (&xa)[FM], const half8 (&xb)[FN], int rstage, int rkk,
-                  half8 (&ya)[FM], half8 (&yb)[FN], int dstage, int dk) {
+  // MFMAs of step X interleaved with the reads of step rkk from stages
+  // (ras, rws) into Y, and (with_dma, a compile-time flag so the step stays
+  // one basic block) with the loads of A offset dka into stage das and of W
+  // offset dkw into stage dws.
+  auto step = [&](auto with_dma, const half8 (&xa)[FM], const half8 (&xb)[FN], int ras, int rws, int rkk,
+                  half8 (&ya)[FM], half8 (&yb)[FN], int das, int dka, int dws, int dkw) {
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       if constexpr (decltype(with_dma)::value) {
 #pragma unroll
-        for (int q = m * NL / NM; q < (m + 1) * NL / NM; ++q) dma_one(dstage, dk, q);
+        for (int q = m * NL / NM; q < (m + 1) * NL / NM; ++q) dma_one(das, dka, dws, dkw, q);
       }
 #pragma unroll
-      for (int r = m * NF / NM; r < (m + 1) * NF / NM; ++r) frag_one(rstage, rkk, r, ya, yb);
+      for (int r = m * NF / NM; r < (m + 1) * NF / NM; ++r) frag_one(ras, rws, rkk, r, ya, yb);
       const int i = m / FN, j = m % FN;
       acc[i][j] = FR::mfma(xa[i], xb[j], acc[i][j]);
       __builtin_amdgcn_sched_barrier(0);
@@ -379,28 +415,36 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   const std::integral_constant<bool, true> with_dma;
   // the K steps of a tile before its barrier (all but the last); NSTEP is even,
   // so the last step's fragments are always in fa1/fb1
-  auto steps_before_barrier = [&](int stage) {
-    step(no_dma, fa0, fb0, stage, 1, fa1, fb1, 0, 0);
+  auto steps_before_barrier = [&](int as, int ws) {
+    step(no_dma, fa0, fb0, as, ws, 1, fa1, fb1, 0, 0, 0, 0);
     if constexpr (NSTEP == 4) {
-      step(no_dma, fa1, fb1, stage, 2, fa0, fb0, 0, 0);
-      step(no_dma, fa0, fb0, stage, 3, fa1, fb1, 0, 0);
+      step(no_dma, fa1, fb1, as, ws, 2, fa0, fb0, 0, 0, 0, 0);
+      step(no_dma, fa0, fb0, as, ws, 3, fa1, fb1, 0, 0, 0, 0);
     }
   };
 
   // ---- tiles: one per workgroup, or several (a persistent launch, fewer
-  // workgroups than tiles).  When the epilogue's staging fits in stage 1, the
-  // next tile's first K tile is loaded into stage 0 while this tile's results
-  // are stored.
+  // workgroups than tiles).  When the epilogue's staging fits in the ring's
+  // second half (A1 and the last W stage), the next tile's first K tiles are
+  // loaded into the first half while this tile's results are stored.
   using SE = StagedEpilogue<MF, FN>;
-  constexpr bool kOverlap = NW * SE::kFloats * 4 <= STAGE * 2;
-  static_assert(NW * SE::kFloats * 4 <= 2 * STAGE * 2, "epilogue staging exceeds the LDS ring");
+  constexpr int kStageAt = a_off(1), kStageRoom = RING - kStageAt;  // halves
+  constexpr bool kOverlap = NW * SE::kFloats * 4 <= kStageRoom * 2;
+  static_assert(NW * SE::kFloats * 4 <= RING * 2, "epilogue staging exceeds the LDS ring");
   const bool vec_ok = (N & 7) == 0 && (ldc & 7) == 0 &&
                       ((reinterpret_cast<uintptr_t>(C) | reinterpret_cast<uintptr_t>(R)) & 15) == 0;
-  float* const stage_base = reinterpret_cast<float*>(kOverlap ? smem + STAGE : smem);
+  float* const stage_base = reinterpret_cast<float*>(kOverlap ? smem + kStageAt : smem);
+  // the loads of a tile's first K tile (A0, W0), which do not touch the
+  // staging area; the rest follow at the tile's start (the epilogue's
+  // barriers wait for every load in flight, so it gets no more than these)
+  auto early_loads = [&]() {
+    dma_a(0, 0);
+    dma_w(0, 0);
+  };
   int tile = blockIdx.x;
   if (tile >= n_tiles) return;
   set_tile(tile);
-  dma(0, 0);
+  early_loads();
   for (;;) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -408,27 +452,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < FR::kElems; ++e) acc[i][j][e] = 0.f;
-    // K tile 0 is in flight (issued above, or during the previous epilogue)
-    if (nk > 1) {
-      dma(1, kBK);
-      if constexpr (NL == 16)
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");  // K tile 0 landed; K tile 1 may still fly
-      else
-        wait_dma();
-    } else {
-      wait_dma();
-    }
+    // A0 and W0 are in flight (issued above, or during the previous epilogue)
+    dma_a(1, min(1, nk - 1) * kBK);
+    if constexpr (WD == 3) dma_w(1, min(1, nk - 1) * kBK);
+    dma_w(WD - 1, min(WD - 1, nk - 1) * kBK);
+    wait_dma();
     __syncthreads();
-    frags(0, 0, fa0, fb0);
-    int cur = 0;
+    frags(0, 0, 0, fa0, fb0);
+    int ca = 0, cw = 0;  // stages of K tile kt
     for (int kt = 0; kt + 1 < nk; ++kt) {
-      steps_before_barrier(cur);
-      wait_dma();
-      __syncthreads();
-      step(with_dma, fa1, fb1, cur ^ 1, 0, fa0, fb0, cur, min(kt + 2, nk - 1) * kBK);
-      cur ^= 1;
+      steps_before_barrier(ca, cw);
+      if constexpr (WD == 3) {
+        // A of tile kt+1 and W of tile kt+1 landed; W of tile kt+2 may still fly
+        barrier_after_loads<BJ>();
+      } else {
+        wait_dma();
+        __syncthreads();
+      }
+      const int na = ca ^ 1, nw = cw + 1 == WD ? 0 : cw + 1;
+      step(with_dma, fa1, fb1, na, nw, 0, fa0, fb0, ca, min(kt + 2, nk - 1) * kBK, cw,
+           min(kt + WD, nk - 1) * kBK);
+      ca = na;
+      cw = nw;
     }
-    steps_before_barrier(cur);
+    steps_before_barrier(ca, cw);
     mfmas(fa1, fb1);
     wait_dma();  // no load may still be writing LDS when it is reused or the workgroup retires
 
@@ -437,7 +484,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     __syncthreads();  // every wave is done reading the ring
     if (kOverlap && next < n_tiles) {
       set_tile(next);
-      dma(0, 0);
+      early_loads();
     }
     float* const Pp = P + (int64_t)blockIdx.y * M * N;
     if (vec_ok)
@@ -450,7 +497,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     __syncthreads();  // every wave's staging is done before the ring is loaded again
     if (!kOverlap) {
       set_tile(tile);
-      dma(0, 0);
+      early_loads();
     }
   }
 }
@@ -469,7 +516,7 @@ int device_cus() {
 }
 
 // max_wgs > 0: at most that many workgroups, each looping over tiles
-template <int MF, int BM, int BN, int WGM, int WGN>
+template <int MF, int BM, int BN, int WGM, int WGN, int WDEPTH = 2>
 hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K,
                       const GemmPitch& ld, int epi, ee_gelu form, void* C, int splits, float* P, hipStream_t s,
                       int max_wgs = 0) {
@@ -482,7 +529,7 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
   const f16* r = static_cast<const f16*>(R);
   f16* c = static_cast<f16*>(C);
 #define EE_GEMM_LAUNCH(E)                                                                                        \
-  hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E>), grid, block, 0, s, a, ld.a, w, ld.w, b, r, \
+  hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E, WDEPTH>), grid, block, 0, s, a, ld.a, w, ld.w, b, r, \
                      c, ld.c, M, N, K, (int)form, tm, tn, P)
   switch (epi) {
     case EE_EPI_NONE: EE_GEMM_LAUNCH(EE_EPI_NONE); break;
@@ -552,10 +599,14 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
                                 int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles_big >= 256)
-    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN>(A, W, bias, R, (int)M, N, K, ld, epi, form, C,
-                                                                      1, nullptr, s,
-                                                                      EE_GEMM_PERSIST ? device_cus() : 0);
+  if (tiles_big >= 256) {
+    const int wgs = EE_GEMM_PERSIST ? device_cus() : 0;
+    if (K >= EE_GEMM_DEEP_W_K)
+      return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(A, W, bias, R, (int)M, N, K, ld, epi, form,
+                                                                           C, 1, nullptr, s, wgs);
+    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 2>(A, W, bias, R, (int)M, N, K, ld, epi, form, C,
+                                                                         1, nullptr, s, wgs);
+  }
   return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, ld, epi, form, C, 1, nullptr, s);
 }
 
