@@ -15,12 +15,14 @@
 //     reads 2/3 of the LDS bytes per flop that a 128 x 64 block (two waves per
 //     SIMD) does; the chip is power-limited under this load and ran ~15% higher
 //     clocks with it (1.8 vs 1.5 GHz on the FC1 shape).
-//   * Two LDS stages (2 x 64 KiB of the 160 KiB per CU) filled by 16-byte
-//     direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds): no register
-//     staging and no LDS store instructions.  Tile kt+2 is requested right
-//     after the barrier that retires tile kt's stage, one load per four MFMAs
-//     (bunching them stalls MFMA issue), so a load has about a K tile of MFMA
-//     work to land; one barrier per K tile.
+//   * An LDS ring of 2 A stages and 2 W stages (4 x 32 KiB of the 160 KiB per
+//     CU) filled by 16-byte direct-to-LDS buffer loads (buffer_load_dwordx4
+//     ... lds): no register staging and no LDS store instructions.  Tile kt+2
+//     is requested right after the barrier that retires tile kt's stages, one
+//     load per four MFMAs (bunching them stalls MFMA issue), so a load has
+//     about a K tile of MFMA work to land; one barrier per K tile.  From
+//     K = 32768 the large tile keeps 3 W stages (the ring fills the 160 KiB)
+//     and requests W two K tiles ahead: there both operands stream from HBM.
 //   * MFMA fragments are double-buffered in registers: the LDS reads of K step
 //     kk+1 are in flight while the MFMAs of step kk issue.
 //   * LDS rows are 128 bytes (8 chunks of 16 B); chunk c of row r is stored at
