@@ -16,7 +16,7 @@ __all__ = [
     "EPI_NONE", "EPI_BIAS", "EPI_BIAS_RESIDUAL", "EPI_BIAS_GELU",
     "ee_compute_offsets", "ee_compute_offsets_mask", "ee_padding_workspace_size",
     "ee_remove_padding", "ee_rebuild_padding", "ee_layernorm", "ee_linear", "ee_bias_gelu",
-    "ee_linear_splitk", "ee_linear_splitk_workspace_size",
+    "ee_linear_splitk", "ee_linear_splitk_workspace_size", "ee_linear_streamk", "ee_linear_streamk_workspace_size",
     "ee_attention_varlen", "ee_attention_padded", "ee_transpose_padding_rebuild_heads",
     "ee_transpose_padding_remove_heads", "ee_add_bias_residual_layernorm",
     "BLOCK_GPT_PRELN", "BLOCK_BERT_POSTLN", "ATTN_VARLEN", "ATTN_PADDED",
@@ -116,6 +116,9 @@ _SIGS = {
     "ee_linear_splitk_workspace_size": (C.c_int, [_I64, _I32, _I32, C.POINTER(_SZ)]),
     "ee_linear_splitk": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _I32, _VP, _VP,
                                    _SZ, _VP]),
+    "ee_linear_streamk_workspace_size": (C.c_int, [_I64, _I32, _I32, C.POINTER(_SZ)]),
+    "ee_linear_streamk": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP, _VP, _SZ,
+                                    _VP]),
     "ee_attention_varlen": (C.c_int, [_VP, _VP, _I32, _I32, _I32, _I32, _I64, _I32, C.c_int, _VP, _VP]),
     "ee_attention_padded": (C.c_int, [_VP, _VP, _VP, _VP, _I32, _I32, _I32, _I32, _I32, C.c_int, _VP, _VP]),
     "ee_transpose_padding_rebuild_heads": (C.c_int, [_VP, _PI32, _I32, _I32, _I32, _I32, _I32, C.c_int, _VP, _VP,
@@ -298,6 +301,20 @@ def ee_linear_splitk(A, W, bias, residual, epi: int, C_out, splits: int, workspa
     _check(lib().ee_linear_splitk(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
                                   splits, _ptr(C_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "ee_linear_splitk")
+
+
+def ee_linear_streamk_workspace_size(M: int, N: int, K: int) -> int:
+    n = C.c_size_t(0)
+    _check(lib().ee_linear_streamk_workspace_size(M, N, K, C.byref(n)), "ee_linear_streamk_workspace_size")
+    return n.value
+
+
+def ee_linear_streamk(A, W, bias, residual, epi: int, C_out, workspace, gelu: int = GELU_TANH, stream=None):
+    M, K = A.shape
+    N = W.shape[0]
+    _check(lib().ee_linear_streamk(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
+                                   _ptr(C_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                   _stream(stream)), "ee_linear_streamk")
 
 
 def ee_bias_gelu(u, bias, g, gelu: int = GELU_TANH, stream=None):

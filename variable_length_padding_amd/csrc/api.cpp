@@ -244,6 +244,11 @@ hipError_t gemm(ee_dtype dt, const void* A, const void* W, const void* bias, con
                 const GemmPitch& ld, ee_epilogue epi, ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr,
                 size_t scratch_bytes = 0) {
   if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K, ld, A, W)) {
+    if (scratch) {
+      const StreamKPlan sk = gemm_f16_streamk_plan(M, N, K, ld);
+      if (sk.workgroups > 0 && sk.scratch_bytes <= scratch_bytes)
+        return launch_gemm_f16_streamk(sk, A, W, bias, R, M, N, ld, epi, g, C, scratch, s);
+    }
     const int splits = scratch && M <= kSplitkMaxRows ? gemm_f16_splitk_choice(M, N, K, scratch_bytes) : 1;
     if (splits > 1) return launch_gemm_f16_splitk(A, W, bias, R, M, N, K, ld, epi, g, C, splits, scratch, s);
     return launch_gemm_f16_mfma(A, W, bias, R, M, N, K, ld, epi, g, C, s);
@@ -794,6 +799,52 @@ ee_status ee_linear_splitk(const void* A, const void* W, const void* bias, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   EE_LAUNCH("linear", st,
             launch_gemm_f16_splitk(A, W, bias, residual, M, N, K, dense(N, K), epi, gelu, C, splits, ws, st));
+  return EE_OK;
+}
+
+ee_status ee_linear_streamk_workspace_size(int64_t M, int32_t N, int32_t K, size_t* bytes) {
+  if (M < 0 || N < 1 || K < 1 || !bytes) return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1 and an output");
+  if (M == 0) {
+    *bytes = 0;
+    return EE_OK;
+  }
+  const StreamKPlan p = gemm_f16_streamk_plan(M, N, K, dense(N, K));
+  if (p.workgroups < 1)
+    return fail(EE_ERR_UNSUPPORTED, "stream-K does not take M=%lld N=%d K=%d", (long long)M, N, K);
+  *bytes = p.scratch_bytes;
+  return EE_OK;
+}
+
+ee_status ee_linear_streamk(const void* A, const void* W, const void* bias, const void* residual, int64_t M,
+                            int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, void* C, void* ws,
+                            size_t ws_bytes, void* stream) {
+  if (dtype != EE_F16) return fail(EE_ERR_UNSUPPORTED, "stream-K is fp16 only");
+  if (epi < EE_EPI_NONE || epi > EE_EPI_BIAS_GELU) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi);
+  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+  if (M < 0 || N < 1 || K < 1) return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
+  if (M == 0) return EE_OK;
+  const StreamKPlan p = gemm_f16_streamk_plan(M, N, K, dense(N, K));
+  if (p.workgroups < 1 || !gemm_f16_mfma_ok(M, N, K, dense(N, K), A, W))
+    return fail(EE_ERR_UNSUPPORTED, "stream-K does not take M=%lld N=%d K=%d", (long long)M, N, K);
+  EE_TRY(check_ptr(A, "A"));
+  EE_TRY(check_ptr(W, "W"));
+  EE_TRY(check_ptr(C, "C"));
+  EE_TRY(check_ptr(ws, "workspace"));
+  if (epi != EE_EPI_NONE) EE_TRY(check_ptr(bias, "bias"));
+  if (epi == EE_EPI_BIAS_RESIDUAL) EE_TRY(check_ptr(residual, "residual"));
+  if (ws_bytes < p.scratch_bytes)
+    return fail(EE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, p.scratch_bytes);
+  const size_t nc = (size_t)M * N * 2, need = p.scratch_bytes;
+  if (overlap(C, nc, A, (size_t)M * K * 2) || overlap(C, nc, W, (size_t)N * K * 2) ||
+      (epi != EE_EPI_NONE && overlap(C, nc, bias, (size_t)N * 2)) ||
+      (epi == EE_EPI_BIAS_RESIDUAL && overlap(C, nc, residual, nc)) || overlap(ws, need, C, nc) ||
+      overlap(ws, need, A, (size_t)M * K * 2) || overlap(ws, need, W, (size_t)N * K * 2) ||
+      (epi != EE_EPI_NONE && overlap(ws, need, bias, (size_t)N * 2)) ||
+      (epi == EE_EPI_BIAS_RESIDUAL && overlap(ws, need, residual, nc)))
+    return fail(EE_ERR_INVALID_ARG, "C or the workspace overlaps an input");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  EE_LAUNCH("linear", st,
+            launch_gemm_f16_streamk(p, A, W, bias, residual, M, N, dense(N, K), epi, gelu, C, ws, st));
   return EE_OK;
 }
 
