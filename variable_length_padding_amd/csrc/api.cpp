@@ -109,9 +109,11 @@ hipError_t timed(const char* site, hipStream_t s, F&& launch) {
   if (!p.on) return launch();
   std::lock_guard<std::mutex> lk(p.mu);
   if (p.used == p.pool.size()) {
+    // timing-only events: no system-scope fence (a cache writeback) when they
+    // are recorded, which would stall the stream between the timed launches
     std::pair<hipEvent_t, hipEvent_t> e{};
-    hipError_t r = hipEventCreate(&e.first);
-    if (r == hipSuccess) r = hipEventCreate(&e.second);
+    hipError_t r = hipEventCreateWithFlags(&e.first, hipEventDisableSystemFence);
+    if (r == hipSuccess) r = hipEventCreateWithFlags(&e.second, hipEventDisableSystemFence);
     if (r != hipSuccess) return r;
     p.pool.push_back(e);
   }
