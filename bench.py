@@ -26,6 +26,7 @@ holds both plans' times, batch counts and padded-row ratios.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -66,6 +67,8 @@ def _parse():
     ap.add_argument("--decode-steps", type=int, default=0,
                     help="incremental decoding: prefill the batch's prompts, then time this many decode steps "
                          "(one new token per sequence each) through ee_stack_extend")
+    ap.add_argument("--decode-batch", type=int, default=0,
+                    help="incremental decoding: number of sequences (default: the workload's batch)")
     ap.add_argument("--max-batch", type=int, default=0,
                     help="request-stream workload: batch size cap of both planners (default: the workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -334,6 +337,8 @@ def _decode_bench(args):
 
     dev = torch.device("cuda:0")
     w = workloads.get(args.workload)
+    if args.decode_batch > 0:
+        w = dataclasses.replace(w, batch=args.decode_batch)
     prompts = workloads.lengths(w, args.seed)
     B, L, N = len(prompts), w.layers, args.decode_steps
     s_el = w.elem_bytes

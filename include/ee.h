@@ -255,16 +255,17 @@ EE_API ee_status ee_linear_splitk(const void* A, const void* W, const void* bias
                                   int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu,
                                   int32_t splits, void* C, void* ws, size_t ws_bytes, void* stream);
 
-/* ee_linear for fp16 with at most 32 rows of A (a decode step of up to 32
+/* ee_linear for fp16 with at most 128 rows of A (a decode step of up to 128
  * sequences), decomposed stream-K (Osama et al., "Stream-K: Work-centric
  * Parallel Decomposition for Dense Matrix-Matrix Multiplication", PPoPP 2023):
  * the (256-row N tile, 64-wide K tile) space of W is cut into equal
  * contiguous ranges, one per workgroup, whose fp32 partial sums go to the
- * workspace (ee_linear_streamk_workspace_size bytes, depends on M, N, K and
- * the device's CU count); a second kernel adds each tile's pieces in K order
- * and applies the epilogue.  The layer's extend step uses it whenever it takes
- * the shape.  Arguments as ee_linear; A, W, C and the residual dense.
- * Errors: EE_ERR_UNSUPPORTED for fp32, M > 32, K % 64 != 0 or a problem too
+ * workspace (ee_linear_streamk_workspace_size bytes, M x 1 KiB per slot,
+ * depends on M, N, K and the device's CU count); a second kernel adds each
+ * tile's pieces in K order and applies the epilogue.  The layer's extend step
+ * uses it whenever it takes the shape and its partials fit the extend
+ * workspace's 64 MiB.  Arguments as ee_linear; A, W, C and the residual dense.
+ * Errors: EE_ERR_UNSUPPORTED for fp32, M > 128, K % 64 != 0 or a problem too
  * small to give each workgroup 8 K tiles; EE_ERR_WORKSPACE for a small
  * workspace; EE_ERR_INVALID_ARG for overlapping buffers. */
 EE_API ee_status ee_linear_streamk_workspace_size(int64_t M, int32_t N, int32_t K, size_t* bytes);

@@ -1,14 +1,16 @@
-"""The stream-K GEMM for at most 32 rows of A (ee_linear_streamk), through the C ABI.
+"""The stream-K GEMM for at most 128 rows of A (ee_linear_streamk), through the C ABI.
 
 - Integer-exact: small-integer fp16 operands make every piece's partial sum
   and the sum of a tile's pieces integers below 2^24, exact in fp32 in any
   order, so the result must be the fp16 rounding of the exact sum, bit for
   bit.  Shapes: the four GEMMs of a GPT-3-width decode step at M = 32 (QKV,
-  out, FC1, FC2), and ragged ones: M < 32, N not a multiple of the 256-row
-  tile, N % 8 != 0 (the scalar reduce), more N tiles than CUs (two workgroups
-  per CU), and pieces crossing a tile boundary.
+  out, FC1, FC2), FC1 and FC2 at M = 128 and 64 (the 128- and 64-row A
+  tiles), and ragged ones: M below a tile height (1, 5, 7, 17, 33, 100), N not
+  a multiple of the 256-row tile, N % 8 != 0 (the scalar reduce), more N
+  tiles than CUs (two rounds of workgroups), and pieces crossing a tile
+  boundary.
 - Random data with the GeLU epilogue against the oracle (fp64 linear + gelu).
-- The workspace query and the errors (fp32, M > 32, a problem too small to
+- The workspace query and the errors (fp32, M > 128, a problem too small to
   give every workgroup 8 K tiles, a short workspace).
 Bars: bit-exact for the integer cases; normwise 2e-3 for random data (fp16
 output rounding plus fp32 accumulation)."""
@@ -58,13 +60,17 @@ def _exact_check(M, N, K, epi):
     (32, 12288, 12288, ee.EPI_BIAS_RESIDUAL),   # out projection
     (32, 49152, 12288, ee.EPI_BIAS),            # FC1 (GeLU below, on random data)
     (32, 12288, 49152, ee.EPI_BIAS_RESIDUAL),   # FC2
+    (128, 49152, 12288, ee.EPI_BIAS),           # FC1, 128 sequences
+    (64, 12288, 49152, ee.EPI_BIAS_RESIDUAL),   # FC2, 64 sequences
 ])
 def test_streamk_decode_shapes_integer_exact(M, N, K, epi):
     _exact_check(M, N, K, epi)
 
 
 @pytest.mark.parametrize("M,N,K", [(7, 1000, 64 * 600), (1, 777, 64 * 600), (5, 8200, 64 * 64),
-                                   (32, 2056, 64 * 256), (32, 76808, 64 * 16), (17, 4096, 64 * 130)])
+                                   (32, 2056, 64 * 256), (32, 76808, 64 * 16), (17, 4096, 64 * 130),
+                                   (33, 1000, 64 * 600), (100, 8200, 64 * 64), (128, 76808, 64 * 16),
+                                   (64, 4104, 64 * 130)])
 @pytest.mark.parametrize("epi", [ee.EPI_NONE, ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL])
 def test_streamk_ragged_integer_exact(M, N, K, epi):
     _exact_check(M, N, K, epi)
@@ -104,13 +110,13 @@ def test_streamk_repeated_calls_same_bits():
 
 def test_streamk_errors():
     with pytest.raises(ee.EEError, match="EE_ERR_UNSUPPORTED"):
-        ee.ee_linear_streamk_workspace_size(33, 12288, 12288)        # M above 32
+        ee.ee_linear_streamk_workspace_size(129, 12288, 12288)       # M above 128
     with pytest.raises(ee.EEError, match="EE_ERR_UNSUPPORTED"):
         ee.ee_linear_streamk_workspace_size(32, 768, 768)            # 36 K tiles in all
     assert ee.ee_linear_streamk_workspace_size(0, 768, 768) == 0
     M, N, K = 32, 4096, 64 * 512
     need = ee.ee_linear_streamk_workspace_size(M, N, K)
-    assert need > 0 and need % (32 * 256 * 4) == 0
+    assert need > 0 and need % (M * 256 * 4) == 0
     A = torch.zeros(M, K, dtype=torch.float16, device=DEV)
     W = torch.zeros(N, K, dtype=torch.float16, device=DEV)
     C = torch.empty(M, N, dtype=torch.float16, device=DEV)

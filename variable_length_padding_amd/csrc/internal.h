@@ -90,12 +90,14 @@ size_t gemm_f16_splitk_bytes(int64_t M, int N, int splits);
 hipError_t launch_gemm_f16_splitk(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
                                   int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, int splits,
                                   void* scratch, hipStream_t s);
-// Stream-K for M <= 32 (gemm_streamk.hip): every workgroup streams an equal
-// share of W's (N tile, K tile) space into fp32 partial sums in scratch
-// (plan.scratch_bytes), then a reduce adds each tile's pieces in K order and
-// applies the epilogue.  workgroups == 0: the kernel does not take the problem.
+// Stream-K for M <= kStreamKMaxRows (gemm_streamk.hip): every workgroup
+// streams an equal share of W's (N tile, K tile) space into fp32 partial sums
+// in scratch (plan.scratch_bytes), then a reduce adds each tile's pieces in K
+// order and applies the epilogue.  workgroups == 0: the kernel does not take
+// the problem.
+constexpr int64_t kStreamKMaxRows = 128;
 struct StreamKPlan {
-  int kt, tiles_n, per_wg, workgroups;
+  int tile_rows, kt, tiles_n, per_wg, workgroups;
   size_t scratch_bytes;
 };
 StreamKPlan gemm_f16_streamk_plan(int64_t M, int N, int K, const GemmPitch& ld);
