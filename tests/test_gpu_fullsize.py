@@ -150,3 +150,45 @@ def test_gpt3_width_decode_sampled():
                 assert err <= 2e-2
             r += n
         ctx = [c + n for c, n in zip(ctx, new)]
+
+
+@pytest.mark.parametrize("B", [72, 128])
+def test_gpt3_width_decode_wide_batch(B):
+    """Decode steps of more than 32 sequences at GPT-3 width (two layers): the
+    stream-K GEMMs with their 128-row A tile (72 rows ragged, and 128 full)
+    inside ee_stack_extend.  A prefill of short prompts (lengths 1..12), then
+    two decode steps; sequences 0, B/2 and B-1 are checked step by step against
+    the oracle's incremental forward (fp16 bar 2e-2); every output row is
+    finite."""
+    w = workloads.get("gpt3-12l")
+    g = torch.Generator().manual_seed(B)
+    prompts = torch.randint(1, 13, (B,), generator=g).tolist()
+    L = 2
+    params = [ee.pitched_weights(workloads.layer_params(w, SEED, l, device=DEV)) for l in range(L)]
+    hs = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=ee.F16) for p in params]
+    base = list(np.concatenate([[0], np.cumsum([n + 2 for n in prompts])[:-1]]).astype(int))
+    cap = sum(n + 2 for n in prompts)
+    cache = torch.empty(ee.ee_kv_cache_bytes(hs[0], L, cap), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(ee.ee_extend_workspace_size(hs[0], B, sum(prompts)), dtype=torch.uint8, device=DEV)
+    gd = torch.Generator(device=DEV).manual_seed(100 + B)
+    rows = [(torch.randn(n + 2, w.hidden, generator=gd, device=DEV)).half() for n in prompts]
+    p64 = [oracle.to_f64_params({k: v.cpu() for k, v in p.items()}) for p in params]
+    picks = (0, B // 2, B - 1)
+    ocache = {b: oracle.SequenceCache(L, w.n_heads, w.head_dim) for b in picks}
+    ctx = [0] * B
+    for step, new in enumerate([prompts, [1] * B, [1] * B]):
+        x = torch.cat([rows[b][ctx[b]:ctx[b] + n] for b, n in enumerate(new)])
+        y = torch.empty_like(x)
+        ee.ee_stack_extend(hs, x, new, ctx, base, cache, cap, y, ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y).all()
+        r = 0
+        for b, n in enumerate(new):
+            if b in picks:
+                ref = oracle.extend_sequence(ocache[b], rows[b][ctx[b]:ctx[b] + n].double().cpu().numpy(), p64,
+                                             w.n_heads, w.head_dim)
+                err = normwise_rel(to_host64(y[r:r + n]), ref)
+                say(f"gpt3 width decode B={B} step {step} sequence {b} ({n} new after {ctx[b]}): rel {err:.3e}")
+                assert err <= 2e-2
+            r += n
+        ctx = [c + n for c, n in zip(ctx, new)]
