@@ -328,6 +328,12 @@ typedef struct {
 } ee_kernel_stat;
 
 EE_API ee_status ee_profile_enable(int32_t on);
+/* Restricts the timing to one launch site (e.g. "gemm_fc1"); NULL or "" times
+ * every site again.  Each recorded event pair leaves a bubble of a few us in
+ * its stream, so timing only the kernel of interest keeps the rest of the work
+ * at full speed.  The name is copied.  EE_ERR_INVALID_ARG for a name of 32 or
+ * more characters. */
+EE_API ee_status ee_profile_filter(const char* site);
 /* Waits for the recorded events, writes up to `capacity` per-site totals into
  * `out` (host), sets *count, and clears the record. */
 EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* count);

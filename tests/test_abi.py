@@ -230,3 +230,14 @@ def test_layer_create_validates_weight_pitches(field, value, status):
     assert st == status
     if h.value:
         ee.lib().ee_layer_destroy(h)
+
+
+def test_profile_filter_validates_and_resets():
+    """ee_profile_filter copies a site name shorter than the stat name field,
+    rejects longer ones, and NULL or "" restore timing every site (host only)."""
+    lib = ee.lib()
+    assert lib.ee_profile_filter(b"gemm_fc1") == 0
+    assert lib.ee_profile_filter(b"x" * 31) == 0
+    assert lib.ee_profile_filter(b"x" * 32) == 1
+    assert lib.ee_profile_filter(b"") == 0
+    assert lib.ee_profile_filter(None) == 0

@@ -92,6 +92,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 struct Profiler {
   std::mutex mu;
   bool on = false;
+  std::string only;  // the one site timed, or empty for every site
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
   size_t used = 0;
   std::vector<std::pair<std::string, size_t>> recs;  // (site, pool index)
@@ -108,6 +109,7 @@ hipError_t timed(const char* site, hipStream_t s, F&& launch) {
   Profiler& p = prof();
   if (!p.on) return launch();
   std::lock_guard<std::mutex> lk(p.mu);
+  if (!p.only.empty() && p.only != site) return launch();
   if (p.used == p.pool.size()) {
     // timing-only events: no system-scope fence (a cache writeback) when they
     // are recorded, which would stall the stream between the timed launches
@@ -985,6 +987,15 @@ ee_status ee_profile_enable(int32_t on) {
   Profiler& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
   p.on = on != 0;
+  return EE_OK;
+}
+
+ee_status ee_profile_filter(const char* site) {
+  const size_t n = site ? std::strlen(site) : 0;
+  if (n >= sizeof(ee_kernel_stat{}.name)) return fail(EE_ERR_INVALID_ARG, "site name of %zu characters", n);
+  Profiler& p = prof();
+  std::lock_guard<std::mutex> lk(p.mu);
+  p.only.assign(site ? site : "", n);
   return EE_OK;
 }
 
