@@ -48,6 +48,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace ee {
 namespace {
@@ -77,37 +78,6 @@ constexpr int kBK = 64;
 constexpr int kEpiPartial = 4;
 template <int EPI>
 constexpr bool kHasBias = EPI == EE_EPI_BIAS || EPI == EE_EPI_BIAS_RESIDUAL || EPI == EE_EPI_BIAS_GELU;
-
-__device__ __forceinline__ int lds_swizzle(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
-
-// 16-byte direct-to-LDS buffer load, wrapped in a device-only function: the
-// builtin needs a device target feature, and calling it from a lambda (which
-// HIP compiles for both sides) makes the host pass drop the kernel's stub.
-__device__ __forceinline__ void buffer_load_lds16(__amdgpu_buffer_rsrc_t rsrc, void* lds, int voffset, int soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0, 0);
-}
-
-// Word 3 of a raw (unformatted, stride 0) buffer descriptor on gfx9-family GPUs.
-constexpr int kBufferFlags = 0x00020000;
-
-#define EE_LOCAL(p) ((__attribute__((address_space(3))) void*)(p))
-
-// Waits until this wave's direct-to-LDS loads have written LDS.  Needed before
-// the barrier that publishes them: the workgroup-scope fence of __syncthreads
-// only waits for LDS instructions (lgkmcnt), and the compiler does not count
-// a direct-to-LDS load as an LDS write.  The memory clobber keeps LDS reads below it.
-__device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Workgroup barrier that lets this wave's newest N direct-to-LDS loads stay in
-// flight: it waits for this wave's LDS reads (their stage may be refilled right
-// after) and all older loads, then s_barrier.  (Direct-to-LDS loads retire in
-// issue order among themselves.)  __syncthreads cannot be used here: its
-// fence makes the compiler wait for every load.
-template <int N>
-__device__ __forceinline__ void barrier_after_loads() {
-  static_assert(N == 8, "add the count");
-  asm volatile("s_waitcnt vmcnt(8) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Tile origin of this workgroup: XCD-contiguous ranges of workgroup ids,
 // walked in groups of 4 M-tiles (see the file comment).
@@ -504,19 +474,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   }
 }
 
-// Compute units of the current device (persistent launches use one workgroup per CU).
-int device_cus() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 // max_wgs > 0: at most that many workgroups, each looping over tiles
 template <int MF, int BM, int BN, int WGM, int WGN, int WDEPTH = 2>
 hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K,
@@ -590,6 +547,18 @@ hipError_t launch_reduce(const float* P, int splits, int64_t M, int N, const voi
 
 }  // namespace
 
+int device_cu_count() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev] = n;
+  }
+  return cus[dev];
+}
+
 bool gemm_f16_mfma_ok(int64_t M, int N, int K, const GemmPitch& ld, const void* A, const void* W) {
   const bool pitches = ld.a >= K && ld.w >= K && ld.c >= N && ld.a % 8 == 0 && ld.w % 8 == 0 &&
                        (int64_t)256 * std::max(ld.a, ld.w) * 2 < (1ll << 31);
@@ -602,7 +571,7 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
   if (M <= 0) return hipSuccess;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_big >= 256) {
-    const int wgs = EE_GEMM_PERSIST ? device_cus() : 0;
+    const int wgs = EE_GEMM_PERSIST ? device_cu_count() : 0;
     if (K >= EE_GEMM_DEEP_W_K)
       return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(A, W, bias, R, (int)M, N, K, ld, epi, form,
                                                                            C, 1, nullptr, s, wgs);

@@ -33,6 +33,7 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace ee {
 namespace {
@@ -49,32 +50,6 @@ template <int BM>
 constexpr int sk_depth() {
   return kSkLds / ((BM + kSkBN) * kBK * 2) < 4 ? kSkLds / ((BM + kSkBN) * kBK * 2) : 4;
 }
-
-// chunk c of LDS row r is stored at chunk c ^ f(r); a fragment read by 16
-// consecutive rows then spreads over the banks (f depends on r & 15 only)
-__device__ __forceinline__ int sk_swizzle(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
-
-__device__ __forceinline__ void sk_load_lds16(__amdgpu_buffer_rsrc_t rsrc, f16* lds, int voffset, int soffset) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16, voffset, soffset, 0,
-                                           0);
-}
-
-// Word 3 of a raw (unformatted, stride 0) buffer descriptor on gfx9-family GPUs.
-constexpr int kSkBufferFlags = 0x00020000;
-
-// Waits until at most N of this wave's vector memory operations are pending
-// and its LDS reads are done, then joins the workgroup barrier.  Direct-to-LDS
-// loads complete in issue order among themselves, so with the newest N
-// allowed to fly every older load has written LDS.  (The compiler does not
-// count a direct-to-LDS load as an LDS write, and __syncthreads would wait
-// for every load.)
-template <int N>
-__device__ __forceinline__ void sk_barrier_after_loads() {
-  static_assert(N >= 0 && N <= 63, "vmcnt holds 6 bits");
-  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ void sk_wait_all_loads() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 // 32x32x16 fragment geometry: element e of lane l of the accumulator sits at
 // row (e/4)*8 + (l/32)*4 + e%4 (from A) and column l%32 (from W); an operand
@@ -113,14 +88,14 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_streamk_kernel(const f16* 
 #pragma unroll
   for (int q = 0; q < NLA; ++q) {
     const int ra = wave * (BM / NW) + 8 * q + lr;
-    aoff[q] = (ra * lda + ((lp ^ sk_swizzle(ra)) * 8)) * 2;
+    aoff[q] = (ra * lda + ((lp ^ lds_swizzle(ra)) * 8)) * 2;
   }
 #pragma unroll
   for (int q = 0; q < NLW; ++q) {
     const int rw = wave * WTN + 8 * q + lr;
-    woff[q] = (rw * ldw + ((lp ^ sk_swizzle(rw)) * 8)) * 2;
+    woff[q] = (rw * ldw + ((lp ^ lds_swizzle(rw)) * 8)) * 2;
   }
-  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * lda * 2, kSkBufferFlags);
+  const __amdgpu_buffer_rsrc_t arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)A, (short)0, M * lda * 2, kBufferFlags);
 
   // The next K tile to load, (lt, lk), walks the range in order; once the
   // range's last tile is issued it stays there, so the loads past the range
@@ -134,13 +109,13 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_streamk_kernel(const f16* 
   auto issue_next = [&](int stage) {
     const int n0 = lt * BN;
     const __amdgpu_buffer_rsrc_t wrsrc = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(W + (int64_t)n0 * ldw), (short)0, min(BN, N - n0) * ldw * 2, kSkBufferFlags);
+        (void*)(W + (int64_t)n0 * ldw), (short)0, min(BN, N - n0) * ldw * 2, kBufferFlags);
     const int k2 = lk * kBK * 2;  // byte offset of the K tile
     f16* st = smem + stage * STAGE;
 #pragma unroll
-    for (int q = 0; q < NLA; ++q) sk_load_lds16(arsrc, st + (wave * (BM / NW) + 8 * q) * kBK, aoff[q], k2);
+    for (int q = 0; q < NLA; ++q) buffer_load_lds16(arsrc, st + (wave * (BM / NW) + 8 * q) * kBK, aoff[q], k2);
 #pragma unroll
-    for (int q = 0; q < NLW; ++q) sk_load_lds16(wrsrc, st + (BM + wave * WTN + 8 * q) * kBK, woff[q], k2);
+    for (int q = 0; q < NLW; ++q) buffer_load_lds16(wrsrc, st + (BM + wave * WTN + 8 * q) * kBK, woff[q], k2);
     if (--unissued > 0 && ++lk == kt) {
       lk = 0;
       ++lt;
@@ -155,7 +130,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_streamk_kernel(const f16* 
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  const int kg = lane >> 5, rsw = sk_swizzle(lane & 15);
+  const int kg = lane >> 5, rsw = lds_swizzle(lane & 15);
   const int a_row = (lane & 31) * kBK;
   const int w_row = (BM + wave * WTN + (lane & 31)) * kBK;
   auto multiply = [&](int stage) {
@@ -198,7 +173,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_streamk_kernel(const f16* 
   auto run = [&](int fa, int fb) {
     for (int f = fa; f < fb; ++f) {
       // tile f has landed for every wave; every wave is done with the stage of f-1
-      sk_barrier_after_loads<(D - 2) * NL>();
+      barrier_after_loads<(D - 2) * NL>();
       issue_next(ws);
       multiply(rs);
       rs = rs + 1 == D ? 0 : rs + 1;
@@ -220,7 +195,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_streamk_kernel(const f16* 
     run(split, f1);
     store_piece(tile + 1);
   }
-  sk_wait_all_loads();  // no load may still be writing LDS when the workgroup retires
+  wait_dma();  // no load may still be writing LDS when the workgroup retires
 }
 
 // C[m, n] = epilogue(sum over the pieces of tile n / kSkBN, in K order).
@@ -275,19 +250,6 @@ hipError_t launch_sk_reduce(const float* P, int M, int N, int kt, int per_wg, co
   return hipGetLastError();
 }
 
-// Compute units of the current device, cached per device.
-int cu_count() {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 // A-tile rows for M rows of A (0: more than the kernel takes).
 int sk_tile_rows(int64_t M) { return M <= 32 ? 32 : M <= 64 ? 64 : M <= kStreamKMaxRows ? 128 : 0; }
 
@@ -304,7 +266,7 @@ StreamKPlan gemm_f16_streamk_plan(int64_t M, int N, int K, const GemmPitch& ld) 
   if (total >= (1ll << 31)) return p;
   // at least one workgroup per N tile (so a range meets at most two tiles),
   // a whole number of rounds of one workgroup per CU (the ring fills the LDS)
-  const int cus = cu_count();
+  const int cus = device_cu_count();
   const int64_t wgs = (int64_t)cus * ((tiles_n + cus - 1) / cus);
   const int64_t per_wg = (total + wgs - 1) / wgs;
   if (per_wg < kSkMinPerWg) return p;

@@ -69,6 +69,9 @@ hipError_t launch_add_bias_residual_layernorm(ee_dtype dt, const void* u, const 
 hipError_t launch_bias_gelu(ee_dtype dt, const void* u, const void* bias, int64_t rows, int cols, int ld,
                             ee_gelu form, void* g, hipStream_t s);
 
+// Compute units of the current device, cached per device (gemm_f16.hip).
+int device_cu_count();
+
 // ---- gemm_f16.hip / gemm_valu.hip ----
 // Row pitches, in elements, of a GEMM's operands: A [M, a], W [N, w], and
 // C and the residual R [M, c].
