@@ -82,7 +82,7 @@ __global__ __launch_bounds__(64 * kSkWaves) void gemm_streamk_kernel(const f16* 
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
   // this lane's 16-byte chunk of each load: row lr of the load's 8, physical
-  // chunk lp, which holds the logical chunk lp ^ f(row)
+  // chunk lp, which holds the logical chunk lp ^ lds_swizzle(row)
   const int lr = lane >> 3, lp = lane & 7;
   int aoff[NLA], woff[NLW];
 #pragma unroll
