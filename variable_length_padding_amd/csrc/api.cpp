@@ -13,6 +13,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -54,8 +55,22 @@ ee_status hip_fail(hipError_t e, const char* what) {
   return fail(EE_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
 }
 
+// The int a caller passed for an enum argument or field.  The ABI's enums are
+// C enums, so any int can arrive; in C++ loading an enum object whose value
+// lies outside its enumerators' range is undefined, so validation reads the
+// object representation instead.
+template <class E>
+int ev(const E& e) {
+  static_assert(std::is_enum<E>::value && sizeof(E) == sizeof(int), "an int-sized enum");
+  int v;
+  std::memcpy(&v, &e, sizeof v);
+  return v;
+}
+
 size_t dtype_size(ee_dtype d) { return d == EE_F16 ? 2 : 4; }
 bool dtype_ok(int d) { return d == EE_F32 || d == EE_F16; }
+bool gelu_ok(int g) { return g == EE_GELU_TANH || g == EE_GELU_ERF; }
+bool epilogue_ok(int e) { return e >= EE_EPI_NONE && e <= EE_EPI_BIAS_GELU; }
 size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -157,15 +172,16 @@ ee_status check_lengths(const int32_t* lens, int32_t B, int32_t P, int64_t* tota
 
 ee_status check_desc(const ee_layer_desc* d) {
   if (!d) return fail(EE_ERR_INVALID_ARG, "desc is NULL");
-  if (!dtype_ok(d->dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)d->dtype);
-  if (d->gelu != EE_GELU_TANH && d->gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)d->gelu);
+  if (!dtype_ok(ev(d->dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(d->dtype));
+  if (!gelu_ok(ev(d->gelu))) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", ev(d->gelu));
   if (d->fuse_gelu != 0 && d->fuse_gelu != 1) return fail(EE_ERR_INVALID_ARG, "fuse_gelu must be 0 or 1");
-  if (d->block != EE_BLOCK_GPT_PRELN && d->block != EE_BLOCK_BERT_POSTLN)
-    return fail(EE_ERR_INVALID_ARG, "unknown block %d", (int)d->block);
-  if (d->attention != EE_ATTN_VARLEN && d->attention != EE_ATTN_PADDED)
-    return fail(EE_ERR_INVALID_ARG, "unknown attention form %d", (int)d->attention);
-  if (d->residual != EE_RESIDUAL_AUTO && d->residual != EE_RESIDUAL_EPILOGUE && d->residual != EE_RESIDUAL_PASS)
-    return fail(EE_ERR_INVALID_ARG, "unknown residual mode %d", (int)d->residual);
+  const int block = ev(d->block), attention = ev(d->attention), residual = ev(d->residual);
+  if (block != EE_BLOCK_GPT_PRELN && block != EE_BLOCK_BERT_POSTLN)
+    return fail(EE_ERR_INVALID_ARG, "unknown block %d", block);
+  if (attention != EE_ATTN_VARLEN && attention != EE_ATTN_PADDED)
+    return fail(EE_ERR_INVALID_ARG, "unknown attention form %d", attention);
+  if (residual != EE_RESIDUAL_AUTO && residual != EE_RESIDUAL_EPILOGUE && residual != EE_RESIDUAL_PASS)
+    return fail(EE_ERR_INVALID_ARG, "unknown residual mode %d", residual);
   if (d->hidden < 1 || d->n_heads < 1 || d->ffn < 1)
     return fail(EE_ERR_INVALID_ARG, "hidden, n_heads and ffn must be >= 1");
   if (!(d->ln_eps > 0.f) || !std::isfinite(d->ln_eps)) return fail(EE_ERR_INVALID_ARG, "ln_eps must be finite and > 0");
@@ -517,7 +533,7 @@ ee_status extend_impl(ee_layer* const* layers, int32_t n_layers, const void* d_x
 extern "C" {
 
 const char* ee_status_string(ee_status s) {
-  switch (s) {
+  switch (ev(s)) {
     case EE_OK: return "EE_OK";
     case EE_ERR_INVALID_ARG: return "EE_ERR_INVALID_ARG";
     case EE_ERR_UNSUPPORTED: return "EE_ERR_UNSUPPORTED";
@@ -651,10 +667,11 @@ ee_status ee_padding_workspace_size(int32_t batch, int32_t pad_len, size_t* byte
 }
 
 static ee_status padding_common(const void* src, const int32_t* seq_lens, int32_t batch, int32_t pad_len,
-                                int32_t hidden, ee_dtype dtype, void* dst, void* ws, size_t ws_bytes, int64_t* T,
+                                int32_t hidden, int dtype_i, void* dst, void* ws, size_t ws_bytes, int64_t* T,
                                 Plan* p) {
   EE_TRY(check_lengths(seq_lens, batch, pad_len, T, nullptr));
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!dtype_ok(dtype_i)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", dtype_i);
+  const ee_dtype dtype = static_cast<ee_dtype>(dtype_i);
   if (hidden < 1 || (size_t)hidden * dtype_size(dtype) % 16)
     return fail(EE_ERR_UNSUPPORTED, "hidden*sizeof(dtype) must be a positive multiple of 16 bytes");
   EE_TRY(check_ptr(src, "source"));
@@ -681,7 +698,7 @@ ee_status ee_remove_padding(const void* d_padded, const int32_t* seq_lens, int32
                             void* stream) {
   int64_t T = 0;
   Plan p{};
-  EE_TRY(padding_common(d_padded, seq_lens, batch, pad_len, hidden, dtype, d_packed, workspace, ws_bytes, &T, &p));
+  EE_TRY(padding_common(d_padded, seq_lens, batch, pad_len, hidden, ev(dtype), d_packed, workspace, ws_bytes, &T, &p));
   EE_TRY(check_padding_overlaps(d_padded, d_packed, workspace, p.total, batch, pad_len, T, hidden, dtype));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* cu = reinterpret_cast<int32_t*>(at(workspace, p.cu));
@@ -697,7 +714,7 @@ ee_status ee_rebuild_padding(const void* d_packed, const int32_t* seq_lens, int3
                              void* stream) {
   int64_t T = 0;
   Plan p{};
-  EE_TRY(padding_common(d_packed, seq_lens, batch, pad_len, hidden, dtype, d_padded, workspace, ws_bytes, &T, &p));
+  EE_TRY(padding_common(d_packed, seq_lens, batch, pad_len, hidden, ev(dtype), d_padded, workspace, ws_bytes, &T, &p));
   EE_TRY(check_padding_overlaps(d_padded, d_packed, workspace, p.total, batch, pad_len, T, hidden, dtype));
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t* cu = reinterpret_cast<int32_t*>(at(workspace, p.cu));
@@ -711,7 +728,7 @@ ee_status ee_rebuild_padding(const void* d_packed, const int32_t* seq_lens, int3
 
 ee_status ee_layernorm(const void* x, const void* gamma, const void* beta, int64_t rows, int32_t hidden, float eps,
                        ee_dtype dtype, void* y, void* stream) {
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!dtype_ok(ev(dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(dtype));
   if (rows < 0) return fail(EE_ERR_INVALID_ARG, "rows < 0");
   if (hidden < 1 || (size_t)hidden * dtype_size(dtype) % 16)
     return fail(EE_ERR_UNSUPPORTED, "hidden*sizeof(dtype) must be a positive multiple of 16 bytes");
@@ -729,12 +746,16 @@ ee_status ee_layernorm(const void* x, const void* gamma, const void* beta, int64
   return EE_OK;
 }
 
-ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
-                            const void* residual, int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
-                            ee_gelu gelu, void* C, int64_t ldc, void* stream) {
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (epi < EE_EPI_NONE || epi > EE_EPI_BIAS_GELU) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi);
-  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+// ee_linear_strided with the enum arguments as the ints the caller passed
+static ee_status linear_strided(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
+                                const void* residual, int64_t M, int32_t N, int32_t K, int dtype_i, int epi_i,
+                                int gelu_i, void* C, int64_t ldc, void* stream) {
+  if (!dtype_ok(dtype_i)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", dtype_i);
+  if (!epilogue_ok(epi_i)) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", epi_i);
+  if (!gelu_ok(gelu_i)) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", gelu_i);
+  const ee_dtype dtype = static_cast<ee_dtype>(dtype_i);
+  const ee_epilogue epi = static_cast<ee_epilogue>(epi_i);
+  const ee_gelu gelu = static_cast<ee_gelu>(gelu_i);
   if (M < 0 || N < 1 || K < 1) return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
   if (lda < K || ldw < K || ldc < N || lda > INT32_MAX || ldw > INT32_MAX || ldc > INT32_MAX)
     return fail(EE_ERR_INVALID_ARG, "pitches lda %lld, ldw %lld, ldc %lld: need >= K, K, N and < 2^31",
@@ -758,13 +779,19 @@ ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, int64_t l
   return EE_OK;
 }
 
+ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
+                            const void* residual, int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
+                            ee_gelu gelu, void* C, int64_t ldc, void* stream) {
+  return linear_strided(A, lda, W, ldw, bias, residual, M, N, K, ev(dtype), ev(epi), ev(gelu), C, ldc, stream);
+}
+
 ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual, int64_t M, int32_t N,
                     int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, void* C, void* stream) {
-  return ee_linear_strided(A, K, W, K, bias, residual, M, N, K, dtype, epi, gelu, C, N, stream);
+  return linear_strided(A, K, W, K, bias, residual, M, N, K, ev(dtype), ev(epi), ev(gelu), C, N, stream);
 }
 
 int64_t ee_preferred_row_pitch(int64_t cols, ee_dtype dtype) {
-  if (cols < 1 || !dtype_ok(dtype)) return 0;
+  if (cols < 1 || !dtype_ok(ev(dtype))) return 0;
   return preferred_pitch(cols, dtype_size(dtype));
 }
 
@@ -778,9 +805,9 @@ ee_status ee_linear_splitk_workspace_size(int64_t M, int32_t N, int32_t splits, 
 ee_status ee_linear_splitk(const void* A, const void* W, const void* bias, const void* residual, int64_t M,
                            int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, int32_t splits,
                            void* C, void* ws, size_t ws_bytes, void* stream) {
-  if (dtype != EE_F16) return fail(EE_ERR_UNSUPPORTED, "split-K is fp16 only");
-  if (epi < EE_EPI_NONE || epi > EE_EPI_BIAS_GELU) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi);
-  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+  if (ev(dtype) != EE_F16) return fail(EE_ERR_UNSUPPORTED, "split-K is fp16 only");
+  if (!epilogue_ok(ev(epi))) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", ev(epi));
+  if (!gelu_ok(ev(gelu))) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", ev(gelu));
   if (M < 0 || N < 1 || K < 1 || splits < 1 || splits > 64)
     return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1, 1 <= splits <= 64");
   if (M == 0) return EE_OK;
@@ -822,9 +849,9 @@ ee_status ee_linear_streamk_workspace_size(int64_t M, int32_t N, int32_t K, size
 ee_status ee_linear_streamk(const void* A, const void* W, const void* bias, const void* residual, int64_t M,
                             int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi, ee_gelu gelu, void* C, void* ws,
                             size_t ws_bytes, void* stream) {
-  if (dtype != EE_F16) return fail(EE_ERR_UNSUPPORTED, "stream-K is fp16 only");
-  if (epi < EE_EPI_NONE || epi > EE_EPI_BIAS_GELU) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", (int)epi);
-  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+  if (ev(dtype) != EE_F16) return fail(EE_ERR_UNSUPPORTED, "stream-K is fp16 only");
+  if (!epilogue_ok(ev(epi))) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", ev(epi));
+  if (!gelu_ok(ev(gelu))) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", ev(gelu));
   if (M < 0 || N < 1 || K < 1) return fail(EE_ERR_INVALID_ARG, "need M >= 0, N >= 1, K >= 1");
   if (M == 0) return EE_OK;
   const StreamKPlan p = gemm_f16_streamk_plan(M, N, K, dense(N, K));
@@ -854,8 +881,8 @@ ee_status ee_linear_streamk(const void* A, const void* W, const void* bias, cons
 
 ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t cols, ee_dtype dtype, ee_gelu gelu,
                        void* g, void* stream) {
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
-  if (gelu != EE_GELU_TANH && gelu != EE_GELU_ERF) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", (int)gelu);
+  if (!dtype_ok(ev(dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(dtype));
+  if (!gelu_ok(ev(gelu))) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", ev(gelu));
   if (rows < 0 || cols < 1) return fail(EE_ERR_INVALID_ARG, "need rows >= 0, cols >= 1");
   if ((size_t)cols * dtype_size(dtype) % 16) return fail(EE_ERR_UNSUPPORTED, "cols*sizeof(dtype) % 16 != 0");
   EE_TRY(check_ptr(bias, "bias"));
@@ -872,7 +899,7 @@ ee_status ee_bias_gelu(const void* u, const void* bias, int64_t rows, int32_t co
 ee_status ee_attention_varlen(const void* qkv, const int32_t* d_cu, int32_t batch, int32_t max_len, int32_t n_heads,
                               int32_t head_dim, int64_t total_tokens, int32_t causal, ee_dtype dtype, void* o,
                               void* stream) {
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!dtype_ok(ev(dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(dtype));
   if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
     return fail(EE_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", head_dim);
   if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 65535 || max_len < 0 || total_tokens < 0)
@@ -892,7 +919,7 @@ ee_status ee_attention_varlen(const void* qkv, const int32_t* d_cu, int32_t batc
 ee_status ee_attention_padded(const void* q, const void* k, const void* v, const int32_t* d_cu, int32_t batch,
                               int32_t pad_len, int32_t n_heads, int32_t head_dim, int32_t causal, ee_dtype dtype,
                               void* o, void* stream) {
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!dtype_ok(ev(dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(dtype));
   if (head_dim != 16 && head_dim != 32 && head_dim != 64 && head_dim != 128)
     return fail(EE_ERR_UNSUPPORTED, "head_dim %d not in {16, 32, 64, 128}", head_dim);
   if (batch < 1 || batch > 65535 || n_heads < 1 || n_heads > 65535 || pad_len < 1)
@@ -916,12 +943,12 @@ ee_status ee_transpose_padding_rebuild_heads(const void* d_packed, const int32_t
                                              ee_dtype dtype, void* d_heads, void* workspace, size_t ws_bytes,
                                              void* stream) {
   if (n_mats < 1 || n_heads < 1 || head_dim < 1) return fail(EE_ERR_INVALID_ARG, "n_mats, n_heads, head_dim >= 1");
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!dtype_ok(ev(dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(dtype));
   if ((size_t)head_dim * dtype_size(dtype) % 16) return fail(EE_ERR_UNSUPPORTED, "head_dim*sizeof(dtype) % 16 != 0");
   int64_t T = 0;
   Plan p{};
   const int32_t width = n_mats * n_heads * head_dim;
-  EE_TRY(padding_common(d_packed, seq_lens, batch, pad_len, width, dtype, d_heads, workspace, ws_bytes, &T, &p));
+  EE_TRY(padding_common(d_packed, seq_lens, batch, pad_len, width, ev(dtype), d_heads, workspace, ws_bytes, &T, &p));
   const size_t es = dtype_size(dtype);
   if (overlap(d_packed, (size_t)T * width * es, d_heads, (size_t)batch * pad_len * width * es) ||
       overlap(workspace, p.total, d_heads, (size_t)batch * pad_len * width * es) ||
@@ -940,12 +967,12 @@ ee_status ee_transpose_padding_remove_heads(const void* d_heads, const int32_t* 
                                             int32_t pad_len, int32_t n_heads, int32_t head_dim, ee_dtype dtype,
                                             void* d_packed, void* workspace, size_t ws_bytes, void* stream) {
   if (n_heads < 1 || head_dim < 1) return fail(EE_ERR_INVALID_ARG, "n_heads, head_dim >= 1");
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!dtype_ok(ev(dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(dtype));
   if ((size_t)head_dim * dtype_size(dtype) % 16) return fail(EE_ERR_UNSUPPORTED, "head_dim*sizeof(dtype) % 16 != 0");
   int64_t T = 0;
   Plan p{};
   const int32_t width = n_heads * head_dim;
-  EE_TRY(padding_common(d_heads, seq_lens, batch, pad_len, width, dtype, d_packed, workspace, ws_bytes, &T, &p));
+  EE_TRY(padding_common(d_heads, seq_lens, batch, pad_len, width, ev(dtype), d_packed, workspace, ws_bytes, &T, &p));
   const size_t es = dtype_size(dtype);
   if (overlap(d_packed, (size_t)T * width * es, d_heads, (size_t)batch * pad_len * width * es) ||
       overlap(workspace, p.total, d_heads, (size_t)batch * pad_len * width * es) ||
@@ -962,7 +989,7 @@ ee_status ee_transpose_padding_remove_heads(const void* d_heads, const int32_t* 
 ee_status ee_add_bias_residual_layernorm(const void* u, const void* bias, const void* residual, const void* gamma,
                                          const void* beta, int64_t rows, int32_t hidden, float eps, ee_dtype dtype,
                                          void* y, void* stream) {
-  if (!dtype_ok(dtype)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (!dtype_ok(ev(dtype))) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", ev(dtype));
   if (rows < 0) return fail(EE_ERR_INVALID_ARG, "rows < 0");
   if (hidden < 1 || (size_t)hidden * dtype_size(dtype) % 16)
     return fail(EE_ERR_UNSUPPORTED, "hidden*sizeof(dtype) must be a positive multiple of 16 bytes");
