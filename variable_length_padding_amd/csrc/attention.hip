@@ -24,6 +24,7 @@
 // Any other case (fp32, head_dim 16): a vector-ALU kernel, one query per lane.
 #include "device_common.h"
 #include "internal.h"
+#include "lds_dma.h"
 
 namespace ee {
 namespace {
@@ -177,6 +178,197 @@ __global__ __launch_bounds__(256) void attn_mfma_kernel(AttnAddr ad, const int32
   }
 }
 
+// ---- head_dim 64 / 128: the same algorithm, K and V double-buffered ----
+// Tile t+1 of K and V is fetched into registers (16-byte buffer loads) while
+// tile t is multiplied, then written to the other LDS stage; both are stored
+// row-major with the chunk swizzle k_swizzle, so the writes are 16-byte and
+// conflict-free.  The A operand of O^T += V^T . P^T (row d of V^T, 8 keys)
+// comes from two transposing LDS reads (ds_read_b64_tr_b16): within each
+// 16-lane group, element j of lane i is element i % 4 of the 8 bytes that
+// lane 4j + i / 4 of the group addresses.  Each lane therefore addresses key
+// (lane % 16) / 4 of its 4-key slice at d = 4 * (lane % 4) of its 16-wide d
+// slice and receives 4 keys of one d: no transposing LDS writes.  (Direct-to-
+// LDS loads are not used here: the compiler waits for every one in flight
+// before a transposing read.)  Key rows past the sequence are left to the
+// buffer descriptor, which ends at its last row: the row offset travels in the
+// lane offset (the range check does not cover the scalar offset), so those
+// rows load as zeros and their scores are masked.
+template <int HD>
+__device__ __forceinline__ half4 tr_read(const f16* p) {
+  typedef short short4_t __attribute__((ext_vector_type(4)));
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(p));
+  return __builtin_bit_cast(half4, v);
+}
+
+template <int HD, bool CAUSAL>
+__global__ __launch_bounds__(256) void attn_dma_kernel(AttnAddr ad, const int32_t* __restrict__ cu,
+                                                       float scale_log2) {
+  constexpr int KCH = HD / 8;          // 16-byte chunks per key row
+  constexpr int RPL = 64 / KCH;        // rows one wave covers per 16-byte access
+  constexpr int NLQ = kKB / 4 / RPL;   // accesses per wave per matrix per tile (8 rows per wave)
+  constexpr int NKK = HD / 16;         // MFMA K steps for S
+  constexpr int NDB = HD / 32;         // 32-row blocks of O^T
+  constexpr int TILE = kKB * HD;       // halves per matrix per stage
+  static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
+  __shared__ __attribute__((aligned(16))) f16 smem[2 * 2 * TILE];  // [stage][K | V]
+
+  const int b = blockIdx.y, head = blockIdx.z;
+  const int s0 = cu[b];
+  const int L = cu[b + 1] - s0;
+  const int q_start = blockIdx.x * kQB;
+  if (q_start >= L) return;  // uniform over the workgroup
+  const int64_t in_base = (ad.seq ? (int64_t)s0 * ad.in_row_stride : 0) + b * ad.in_batch_stride + head * ad.in_head_stride;
+  const int ld = (int)ad.in_row_stride;
+  const f16* qb = static_cast<const f16*>(ad.q) + in_base;
+  const int t = threadIdx.x, lane = t & 63, hk = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int q0 = q_start + wave * 32;
+  const int qi = q0 + (lane & 31);
+  const int qc = min(qi, L - 1);
+
+  // descriptors over this sequence's rows of k and v (head slice), ending at row L
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const f16*>(ad.k) + in_base), (short)0, L * ld * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(static_cast<const f16*>(ad.v) + in_base), (short)0, L * ld * 2, kBufferFlags);
+  // this lane's 16 bytes of each access: tile row r, physical chunk lp, which
+  // holds the row's logical chunk lp ^ k_swizzle(r)
+  const int lr = lane / KCH, lp = lane % KCH;
+  int roff[NLQ], lds_off[NLQ];
+#pragma unroll
+  for (int q = 0; q < NLQ; ++q) {
+    const int r = wave * (kKB / 4) + q * RPL + lr;
+    roff[q] = r * ld * 2 + ((lp ^ k_swizzle<HD>(r)) * 16);
+    lds_off[q] = r * HD + lp * 8;
+  }
+  u32x4 kn[NLQ], vn[NLQ];
+  auto fetch = [&](int k0) {
+    const int koff = k0 * ld * 2;
+#pragma unroll
+    for (int q = 0; q < NLQ; ++q) {
+      kn[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, roff[q] + koff, 0, 0));
+      vn[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, roff[q] + koff, 0, 0));
+    }
+  };
+  auto stash = [&](int stage) {
+    f16* sk = smem + stage * 2 * TILE;
+#pragma unroll
+    for (int q = 0; q < NLQ; ++q) {
+      *reinterpret_cast<u32x4*>(sk + lds_off[q]) = kn[q];
+      *reinterpret_cast<u32x4*>(sk + TILE + lds_off[q]) = vn[q];
+    }
+  };
+
+  half8 qf[NKK];
+  {
+    const f16* qrow = qb + (int64_t)qc * ld + hk * 8;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const half8*>(qrow + kk * 16);
+  }
+  floatx16 oacc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kend = CAUSAL ? min(L, q_start + kQB) : L;
+  const int wave_last_key = CAUSAL ? min(q0 + 31, L - 1) : L - 1;
+  const bool wave_active = q0 < L;
+  const int kswz = k_swizzle<HD>(lane & 31);
+  // transposing-read address of this lane within a V tile, for key slice
+  // base 0 and d block 0: key (lane % 16) / 4 + 4 * hk, d 16 * ((lane / 16) % 2) + 4 * (lane % 4)
+  const int tr_key = ((lane & 15) >> 2) + 4 * hk;
+  const int tr_d = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  fetch(0);
+  stash(0);
+  // q's fragments and tile 0 have arrived.  Said as an s_waitcnt the compiler
+  // reads: otherwise it keeps counting q's loads as pending inside the loop
+  // and waits for the next tile's fetch before the first MFMAs.
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0)
+  int stage = 0;
+  for (int k0 = 0; k0 < kend; k0 += kKB) {
+    // every wave's writes of this tile are visible and every wave is done
+    // with the other stage
+    __syncthreads();
+    const bool more = k0 + kKB < kend;
+    if (more) fetch(k0 + kKB);
+    const f16* sk = smem + stage * 2 * TILE;
+    const f16* sv = sk + TILE;
+    if (wave_active && k0 <= wave_last_key) {
+      floatx16 sacc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sacc[e] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        const half8 kf = *reinterpret_cast<const half8*>(sk + (lane & 31) * HD + (((kk * 2 + hk) ^ kswz) * 8));
+        sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sacc, 0, 0, 0);
+      }
+      // element e: key k0 + (e/4)*8 + hk*4 + e%4, query qi
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int key = k0 + (e >> 2) * 8 + hk * 4 + (e & 3);
+        const bool keep = CAUSAL ? key <= qi : key < L;
+        const float v = keep ? sacc[e] * scale_log2 : -INFINITY;
+        sacc[e] = v;
+        mloc = fmaxf(mloc, v);
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
+      const float m_new = fmaxf(m_run, mloc);  // finite: the first tile holds key 0 <= qi
+      const float alpha = exp2f(m_run - m_new);
+      half8 p0, p1;
+      float rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        p0[e] = (f16)exp2f(sacc[e] - m_new);
+        p1[e] = (f16)exp2f(sacc[8 + e] - m_new);
+        rs += (float)p0[e] + (float)p1[e];
+      }
+      rs += __shfl_xor(rs, 32, kWave);
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+        // keys 0..15 of the tile (slots: 8h + 4hk + j), then 16..31
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          half4 lo, hi;
+          {
+            const int key = 16 * m + tr_key, dd = d * 32 + tr_d;
+            lo = tr_read<HD>(sv + key * HD + (((dd >> 3) ^ k_swizzle<HD>(key)) * 8) + (dd & 7));
+          }
+          {
+            const int key = 16 * m + 8 + tr_key, dd = d * 32 + tr_d;
+            hi = tr_read<HD>(sv + key * HD + (((dd >> 3) ^ k_swizzle<HD>(key)) * 8) + (dd & 7));
+          }
+          const half8 va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, m ? p1 : p0, oacc[d], 0, 0, 0);
+        }
+      }
+    }
+    if (more) stash(stage ^ 1);
+    stage ^= 1;
+  }
+  if (qi < L) {
+    const float inv = 1.0f / l_run;
+    f16* orow = static_cast<f16*>(ad.o) + (ad.seq ? (int64_t)s0 * ad.out_row_stride : 0) + b * ad.out_batch_stride +
+                head * ad.out_head_stride + (int64_t)qi * ad.out_row_stride + hk * 4;
+#pragma unroll
+    for (int d = 0; d < NDB; ++d)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        half4 w;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = (f16)(oacc[d][g * 4 + e] * inv);
+        *reinterpret_cast<half4*>(orow + d * 32 + g * 8) = w;
+      }
+  }
+}
+
 // ---- vector-ALU fallback: one query per lane, 64 queries per workgroup ----
 constexpr int kVQ = 64;
 
@@ -253,6 +445,12 @@ template <bool CAUSAL>
 void launch_mfma(const AttnAddr& ad, const int32_t* cu, int B, int max_len, int nh, int hd, hipStream_t s) {
   const dim3 grid((unsigned)((max_len + kQB - 1) / kQB), (unsigned)B, (unsigned)nh), block(256);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);  // log2(e) / sqrt(hd)
+  // the DMA kernel addresses a sequence's rows with 32-bit byte offsets
+  if ((hd == 64 || hd == 128) && (int64_t)max_len * ad.in_row_stride * 2 < (int64_t(1) << 31)) {
+    if (hd == 64) hipLaunchKernelGGL((attn_dma_kernel<64, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
+    else hipLaunchKernelGGL((attn_dma_kernel<128, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
+    return;
+  }
   switch (hd) {
     case 32: hipLaunchKernelGGL((attn_mfma_kernel<32, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2); break;
     case 64: hipLaunchKernelGGL((attn_mfma_kernel<64, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2); break;
