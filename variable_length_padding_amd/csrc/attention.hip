@@ -200,8 +200,14 @@ __device__ __forceinline__ half4 tr_read(const f16* p) {
   return __builtin_bit_cast(half4, v);
 }
 
+// Waves per SIMD the register budget is sized for.  Three (166 VGPRs at
+// head_dim 128) ran at the same speed as two on the GPT-3 shapes; four spills.
+#ifndef EE_ATTN_WAVES_PER_SIMD
+#define EE_ATTN_WAVES_PER_SIMD 2
+#endif
+
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(256) void attn_dma_kernel(AttnAddr ad, const int32_t* __restrict__ cu,
+__global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_dma_kernel(AttnAddr ad, const int32_t* __restrict__ cu,
                                                        float scale_log2) {
   constexpr int KCH = HD / 8;          // 16-byte chunks per key row
   constexpr int RPL = 64 / KCH;        // rows one wave covers per 16-byte access
