@@ -207,7 +207,7 @@ __device__ __forceinline__ half4 tr_read(const f16* p) {
 #endif
 
 template <int HD, bool CAUSAL>
-__global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_dma_kernel(AttnAddr ad, const int32_t* __restrict__ cu,
+__global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(AttnAddr ad, const int32_t* __restrict__ cu,
                                                        float scale_log2) {
   constexpr int KCH = HD / 8;          // 16-byte chunks per key row
   constexpr int RPL = 64 / KCH;        // rows one wave covers per 16-byte access
@@ -451,10 +451,10 @@ template <bool CAUSAL>
 void launch_mfma(const AttnAddr& ad, const int32_t* cu, int B, int max_len, int nh, int hd, hipStream_t s) {
   const dim3 grid((unsigned)((max_len + kQB - 1) / kQB), (unsigned)B, (unsigned)nh), block(256);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);  // log2(e) / sqrt(hd)
-  // the DMA kernel addresses a sequence's rows with 32-bit byte offsets
+  // the transposing-read kernel addresses a sequence's rows with 32-bit byte offsets
   if ((hd == 64 || hd == 128) && (int64_t)max_len * ad.in_row_stride * 2 < (int64_t(1) << 31)) {
-    if (hd == 64) hipLaunchKernelGGL((attn_dma_kernel<64, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
-    else hipLaunchKernelGGL((attn_dma_kernel<128, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
+    if (hd == 64) hipLaunchKernelGGL((attn_tr_kernel<64, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
+    else hipLaunchKernelGGL((attn_tr_kernel<128, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
     return;
   }
   switch (hd) {
