@@ -153,3 +153,26 @@ def test_profile_records_every_launch_site():
     for site in ("offsets", "remove", "ln1", "gemm_qkv", "attention", "gemm_out", "ln2", "gemm_fc1", "gemm_fc2",
                  "rebuild"):
         assert stats[site]["launches"] == 1 and stats[site]["total_ms"] > 0
+
+
+def test_profile_filter_times_one_site():
+    """With ee_profile_filter("gemm_fc1") only that site is timed; with the
+    filter cleared every site is again; the outputs are the same bits."""
+    w = workloads.get("gpt2-small")
+    lens = workloads.lengths(w, 2)
+    x = workloads.activations(w, 2, w.batch, w.pad_len, lens)
+    p = workloads.layer_params(w, 2, 0)
+    ee.ee_profile_enable(True)
+    try:
+        ee.ee_profile_filter("gemm_fc1")
+        y1 = _run_layer(w, lens, x, p)
+        only = ee.ee_profile_collect()
+        ee.ee_profile_filter(None)
+        y2 = _run_layer(w, lens, x, p)
+        every = ee.ee_profile_collect()
+    finally:
+        ee.ee_profile_filter(None)
+        ee.ee_profile_enable(False)
+    assert set(only) == {"gemm_fc1"} and only["gemm_fc1"]["launches"] == 1 and only["gemm_fc1"]["total_ms"] > 0
+    assert {"gemm_fc1", "attention", "rebuild"} <= set(every)
+    assert torch.equal(y1, y2)
