@@ -35,7 +35,7 @@ values.  Parity pins: see tests/test_oracle_*.py.
 """
 from .layer import (  # noqa: F401
     offsets_from_lengths, offsets_from_mask, remove_padding, rebuild_padding,
-    layer_norm, gelu, linear, causal_attention_packed, causal_attention_padded,
+    layer_norm, gelu, linear, causal_attention_packed, causal_attention_query, causal_attention_padded,
     layer_forward_packed, layer_forward_padded, stack_forward_padded, stack_forward_packed,
     to_f64_params, transpose_padding_rebuild_heads, transpose_padding_remove_heads, attention_padded_heads,
     add_bias_residual_layernorm, attention_packed_bidirectional, attention_via_padded_heads,

@@ -171,6 +171,23 @@ def causal_attention_packed(qkv: np.ndarray, cu: Sequence[int], n_heads: int, he
     return o
 
 
+def causal_attention_query(qkv_seq: np.ndarray, i: int, n_heads: int, head_dim: int) -> np.ndarray:
+    """Output row [H'] of query i of one sequence, given that sequence's packed
+    rows qkv_seq [n, 3H'] (n > i): every head attends to keys 0 .. i, the
+    keys causal_attention_packed gives query i.  For checking single rows of
+    sequences too long to run whole."""
+    qkv_seq = np.asarray(qkv_seq, _F64)
+    if not 0 <= i < qkv_seq.shape[0]:
+        raise ValueError(f"query {i} outside the sequence's {qkv_seq.shape[0]} rows")
+    q, k, v = _split_qkv(qkv_seq, n_heads, head_dim)
+    scale = 1.0 / math.sqrt(head_dim)
+    o = np.zeros(n_heads * head_dim, dtype=_F64)
+    for n in range(n_heads):
+        c = slice(n * head_dim, (n + 1) * head_dim)
+        o[c] = _attend_one_query(q[i, c], k[:i + 1, c], v[:i + 1, c], scale)
+    return o
+
+
 def causal_attention_padded(qkv: np.ndarray, length: int, n_heads: int, head_dim: int) -> np.ndarray:
     """Attention of one padded sequence qkv [P, 3H'] with `length` valid tokens:
     position p attends to the keys J(p) = {j : j <= p and j < length}."""

@@ -6,7 +6,11 @@
 - One extend step at the largest batch (EE_MAX_EXTEND_BATCH = 256 sequences):
   a prefill of ragged prompts, then a decode step with a token for every
   sequence, checked step by step.
-Bars: fp16 <= 2e-2, fp32 <= 1e-4 normwise; pads exactly +0.0."""
+- Causal attention at GPT-3 width (96 heads of 128) over a sequence whose
+  QKV rows span more than 2^31 bytes, then one that starts past that point:
+  sampled queries and heads against the oracle's single-query form.
+Bars: fp16 <= 2e-2, fp32 <= 1e-4 normwise (attention: fp16 <= 3e-3); pads
+exactly +0.0."""
 import dataclasses
 
 import numpy as np
@@ -63,3 +67,35 @@ def test_extend_at_max_batch(name, tol):
         err = normwise_rel(got, ref)
         say(f"{name} extend at B={B}, step {k} (T={sum(new_len)}): rel {err:.3e}")
         assert np.all(np.isfinite(got)) and err <= tol
+
+
+def test_attention_rows_past_2gib():
+    """A 29200-token sequence at 96 heads of 128: its QKV rows span 2.15 GB, so
+    byte offsets within the sequence pass 2^31.  The second sequence starts
+    2.15 GB into the buffer.  Sampled queries of three heads against the
+    oracle (heads are independent, so the oracle gets those heads only)."""
+    nh, hd = 96, 128
+    Hp = nh * hd
+    lens = [29200, 100]
+    assert lens[0] * 3 * Hp * 2 >= 2 ** 31
+    T = sum(lens)
+    cu_h = np.array([0, lens[0], T], dtype=np.int32)
+    g = torch.Generator(device=DEV).manual_seed(2031)
+    qkv = torch.randn(T, 3 * Hp, device=DEV, generator=g, dtype=torch.float16)
+    o = torch.full((T, Hp), 7.0, dtype=torch.float16, device=DEV)
+    say(f"attention past 2 GiB: lens {lens}, qkv {qkv.numel() * 2 / 1e9:.2f} GB")
+    ee.ee_attention_varlen(qkv, torch.tensor(cu_h, device=DEV), len(lens), max(lens), nh, hd, o)
+    torch.cuda.synchronize()
+    heads = [0, 47, 95]
+    head_cols = np.concatenate([np.arange(h * hd, (h + 1) * hd) for h in heads])
+    cols = torch.tensor(np.concatenate([m * Hp + head_cols for m in range(3)]), device=DEV)
+    got, ref = [], []
+    for b, queries in ((0, [0, 1, 127, 128, 12345, 29199]), (1, [0, 57, 99])):
+        s0, s1 = int(cu_h[b]), int(cu_h[b + 1])
+        sub = qkv[s0:s1].index_select(1, cols).double().cpu().numpy()  # q | k | v of the three heads
+        for i in queries:
+            ref.append(oracle.causal_attention_query(sub[:i + 1], i, len(heads), hd))
+            got.append(o[s0 + i].double().cpu().numpy()[head_cols])
+    err = normwise_rel(np.stack(got), np.stack(ref))
+    say(f"attention past 2 GiB: {len(got)} sampled rows x {len(heads)} heads, rel {err:.2e}")
+    assert err <= 3e-3

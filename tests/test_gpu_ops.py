@@ -295,6 +295,26 @@ def test_attention_varlen_parity(dtype, hd, nh, tol):
         assert np.allclose(got[cu_h[b]], v[cu_h[b]], rtol=1e-3 if dtype == torch.float16 else 1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("dtype,hd,nh,tol", [
+    (torch.float16, 128, 1, 3e-3), (torch.float16, 64, 2, 3e-3), (torch.float16, 32, 2, 3e-3),
+    (torch.float32, 64, 1, 1e-5),
+])
+def test_attention_long_sequences(dtype, hd, nh, tol):
+    """Sequences of thousands of keys (up to 128 key tiles per query tile,
+    ragged ends) against the whole oracle."""
+    lens = [2048, 1, 4095, 777]
+    cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu_h[-1])
+    qkv = torch.randn(T, 3 * nh * hd, generator=GEN).to(dtype)
+    o = torch.full((T, nh * hd), 7.0, dtype=dtype, device=DEV)
+    ee.ee_attention_varlen(qkv.to(DEV), torch.tensor(cu_h, device=DEV), len(lens), max(lens), nh, hd, o)
+    torch.cuda.synchronize()
+    ref = oracle.causal_attention_packed(qkv.double().numpy(), cu_h, nh, hd)
+    err = normwise_rel(to_host64(o), ref)
+    say(f"attention long {dtype} hd={hd} nh={nh} lens={lens}: rel {err:.2e}")
+    assert err <= tol
+
+
 def test_attention_sequences_are_independent():
     """Permuting the sequences of the batch permutes the output rows exactly."""
     nh, hd = 4, 128

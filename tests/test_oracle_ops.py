@@ -125,6 +125,25 @@ def test_attention_matches_torch_sdpa_fp64(nh, hd):
         np.testing.assert_allclose(o[s0:s1], ref, rtol=1e-11, atol=1e-12)
 
 
+def test_attention_query_matches_torch_sdpa_fp64():
+    """The single-query form against torch's causal SDPA (fp64), row by row; rows
+    after the query change nothing (causality); out-of-range queries raise."""
+    nh, hd, L = 3, 32, 40
+    qkv = _qkv(L, nh, hd)
+    Hp = nh * hd
+    t = torch.from_numpy(qkv)
+    q = t[:, :Hp].reshape(-1, nh, hd).transpose(0, 1)
+    k = t[:, Hp:2 * Hp].reshape(-1, nh, hd).transpose(0, 1)
+    v = t[:, 2 * Hp:].reshape(-1, nh, hd).transpose(0, 1)
+    ref = F.scaled_dot_product_attention(q, k, v, is_causal=True).transpose(0, 1).reshape(-1, Hp).numpy()
+    for i in range(L):
+        o = oracle.causal_attention_query(qkv, i, nh, hd)
+        np.testing.assert_allclose(o, ref[i], rtol=1e-11, atol=1e-12)
+        assert np.array_equal(o, oracle.causal_attention_query(qkv[:i + 1], i, nh, hd))
+    with pytest.raises(ValueError):
+        oracle.causal_attention_query(qkv, L, nh, hd)
+
+
 def test_attention_batch_permutation_permutes_outputs():
     nh, hd = 2, 8
     lens = [3, 5, 2]
