@@ -44,4 +44,4 @@ from .layer import (  # noqa: F401
 from .batching import (  # noqa: F401
     Cost, batch_cost, token_seconds, fifo_batches, length_order, dp_runs, dynamic_batches, padded_rows,
 )
-from .decode import SequenceCache, extend_sequence, extend_batch  # noqa: F401
+from .decode import SequenceCache, extend_sequence, extend_batch, prefill_first_layer_cache  # noqa: F401

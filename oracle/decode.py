@@ -71,6 +71,22 @@ def extend_sequence(cache: SequenceCache, x_new: np.ndarray, params_list: List[D
     return x
 
 
+def prefill_first_layer_cache(cache: SequenceCache, x_new: np.ndarray, params: Dict, n_heads: int, head_dim: int,
+                              eps: float = 1e-5) -> None:
+    """Appends the first layer's keys and values of the new tokens x_new
+    [n, hidden] to a one-layer cache, without computing the tokens' outputs.
+    The first layer's keys and values depend on its inputs only (LayerNorm,
+    then the QKV projection), so this is the cache extend_sequence leaves,
+    for prompts too long to run the oracle's attention over every token."""
+    if len(cache.k) != 1:
+        raise ValueError("only a one-layer cache can be filled without the layer outputs")
+    p = to_f64_params(params)
+    Hp = n_heads * head_dim
+    qkv = linear(layer_norm(np.asarray(x_new, _F64), p["ln1_g"], p["ln1_b"], eps), p["w_qkv"], p["b_qkv"])
+    cache.k[0] = np.concatenate([cache.k[0], _heads(qkv[:, Hp:2 * Hp], n_heads, head_dim)], axis=1)
+    cache.v[0] = np.concatenate([cache.v[0], _heads(qkv[:, 2 * Hp:], n_heads, head_dim)], axis=1)
+
+
 def extend_batch(caches: List[SequenceCache], x_packed: np.ndarray, new_len: Sequence[int], params_list: List[Dict],
                  n_heads: int, head_dim: int, eps: float = 1e-5, gelu_form: str = "tanh") -> np.ndarray:
     """One extend step of a batch: x_packed [sum new_len, hidden], sequence by

@@ -58,6 +58,30 @@ def test_cache_holds_the_kv_projections_of_each_layer_input():
         inp = out
 
 
+def test_first_layer_cache_prefill_equals_extend():
+    """Filling a one-layer cache without the outputs leaves the cache that
+    extend_sequence leaves (bitwise for the same rows in one call, to rounding
+    in chunks), and the next step's output is the same."""
+    w, ps = _setup(n_layers=1)
+    x = workloads.activations(w, 10, 1, 12, [12]).double().numpy()[0]
+    ref = oracle.SequenceCache(1, w.n_heads, w.head_dim)
+    oracle.extend_sequence(ref, x[:11], ps, w.n_heads, w.head_dim)
+    one = oracle.SequenceCache(1, w.n_heads, w.head_dim)
+    oracle.prefill_first_layer_cache(one, x[:11], ps[0], w.n_heads, w.head_dim)
+    assert np.array_equal(one.k[0], ref.k[0]) and np.array_equal(one.v[0], ref.v[0])
+    chunks = oracle.SequenceCache(1, w.n_heads, w.head_dim)
+    oracle.prefill_first_layer_cache(chunks, x[:6], ps[0], w.n_heads, w.head_dim)
+    oracle.prefill_first_layer_cache(chunks, x[6:11], ps[0], w.n_heads, w.head_dim)
+    np.testing.assert_allclose(chunks.k[0], ref.k[0], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(chunks.v[0], ref.v[0], rtol=1e-12, atol=1e-13)
+    y_ref = oracle.extend_sequence(ref, x[11:], ps, w.n_heads, w.head_dim)
+    y_one = oracle.extend_sequence(one, x[11:], ps, w.n_heads, w.head_dim)
+    assert np.array_equal(y_one, y_ref)
+    with pytest.raises(ValueError):
+        oracle.prefill_first_layer_cache(oracle.SequenceCache(2, w.n_heads, w.head_dim), x, ps[0], w.n_heads,
+                                         w.head_dim)
+
+
 def test_one_decode_query_matches_torch_sdpa():
     w, ps = _setup(n_layers=1)
     x = workloads.activations(w, 10, 1, 12, [12]).double().numpy()[0]
