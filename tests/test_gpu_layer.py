@@ -88,6 +88,18 @@ def test_gpt2_small_edge_lengths(lens):
     _check(w, lens, y, ref, 2e-2, f"gpt2-small lens={lens[:4]}...")
 
 
+def test_gpt2_small_long_sequences():
+    """A padding length of 1024: one full sequence, ragged ones (several query
+    tiles of 128 and key tiles past them), an empty one and a single token."""
+    lens = [1024, 300, 0, 1, 777]
+    w = dataclasses.replace(workloads.get("gpt2-small"), batch=len(lens), pad_len=1024)
+    x = workloads.activations(w, 5, len(lens), w.pad_len, lens)
+    p = workloads.layer_params(w, 5, 0, variant="affine")
+    y = _run_layer(w, lens, x, p)
+    ref = oracle.layer_forward_padded(x.double().numpy(), lens, p, w.n_heads, w.head_dim)
+    _check(w, lens, y, ref, 2e-2, f"gpt2-small P=1024 lens={lens}")
+
+
 def test_nan_pads_do_not_reach_valid_rows():
     w = workloads.get("gpt2-small")
     lens = workloads.lengths(w, 11)

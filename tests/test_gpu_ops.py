@@ -299,19 +299,24 @@ def test_attention_varlen_parity(dtype, hd, nh, tol):
     (torch.float16, 128, 1, 3e-3), (torch.float16, 64, 2, 3e-3), (torch.float16, 32, 2, 3e-3),
     (torch.float32, 64, 1, 1e-5),
 ])
-def test_attention_long_sequences(dtype, hd, nh, tol):
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_long_sequences(dtype, hd, nh, tol, causal):
     """Sequences of thousands of keys (up to 128 key tiles per query tile,
-    ragged ends) against the whole oracle."""
+    ragged ends) against the whole oracle, causal and bidirectional."""
     lens = [2048, 1, 4095, 777]
     cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu_h[-1])
     qkv = torch.randn(T, 3 * nh * hd, generator=GEN).to(dtype)
     o = torch.full((T, nh * hd), 7.0, dtype=dtype, device=DEV)
-    ee.ee_attention_varlen(qkv.to(DEV), torch.tensor(cu_h, device=DEV), len(lens), max(lens), nh, hd, o)
+    ee.ee_attention_varlen(qkv.to(DEV), torch.tensor(cu_h, device=DEV), len(lens), max(lens), nh, hd, o,
+                           causal=causal)
     torch.cuda.synchronize()
-    ref = oracle.causal_attention_packed(qkv.double().numpy(), cu_h, nh, hd)
+    if causal:
+        ref = oracle.causal_attention_packed(qkv.double().numpy(), cu_h, nh, hd)
+    else:
+        ref = oracle.attention_packed_bidirectional(qkv.double().numpy(), cu_h, nh, hd)
     err = normwise_rel(to_host64(o), ref)
-    say(f"attention long {dtype} hd={hd} nh={nh} lens={lens}: rel {err:.2e}")
+    say(f"attention long causal={causal} {dtype} hd={hd} nh={nh} lens={lens}: rel {err:.2e}")
     assert err <= tol
 
 
