@@ -145,13 +145,13 @@ def gemm_code_sha256(path=GEMM_SOURCE):
     return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 
-def _traffic():
+def _traffic(workload):
     """HBM bytes per FC1 launch from the committed counter summary, if it was
-    taken on the current GEMM code."""
+    taken on this workload and on the current GEMM code."""
     try:
         with open(PMC_SUMMARY) as f:
             s = json.load(f)
-        if s.get("gemm_code_sha256") != gemm_code_sha256():
+        if s.get("workload") != workload or s.get("gemm_code_sha256") != gemm_code_sha256():
             return None
         return s["hbm_bytes_per_launch"]
     except (OSError, KeyError, ValueError):
@@ -543,7 +543,7 @@ def main():
     achieved = fc1_flops / (fc1_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": ROOFLINE_SYMBOL, "symbol": ROOFLINE_MANGLED, "achieved": round(achieved, 1),
                 "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                "traffic": _traffic() if not (args.no_pack or bert) else None, "avg_launch_ms": round(fc1_ms, 4),
+                "traffic": _traffic(w.name) if not (args.no_pack or bert) else None, "avg_launch_ms": round(fc1_ms, 4),
                 "flops_per_launch": fc1_flops}
 
     cpu = None

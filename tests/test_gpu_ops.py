@@ -129,7 +129,7 @@ def _small_ints(shape, lo=-2, hi=2):
                                    (1000, 1000, 640), (4112, 768, 3072), (2048, 4096, 12288),
                                    (4100, 4200, 320), (4096, 4096, 1024), (4096, 4096, 64), (4300, 4096, 192),
                                    (4096, 4104, 128), (4096, 4099, 64), (4096, 4096, 256), (4096, 4352, 384),
-                                   (4096, 4096, 12288)])
+                                   (4096, 4096, 12288), (4205, 9216, 512)])
 @pytest.mark.parametrize("epi", [ee.EPI_NONE, ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL])
 def test_gemm_integer_exact(M, N, K, epi):
     """Small-integer fp16 operands: every product and partial sum is an integer
@@ -153,6 +153,33 @@ def test_gemm_integer_exact(M, N, K, epi):
     got = C.cpu().numpy()
     assert np.array_equal(got.view(np.uint16), ref16.view(np.uint16)), \
         f"{np.count_nonzero(got != ref16)} of {got.size} differ"
+
+
+@pytest.mark.parametrize("M,N,epi,gelu", [(4205, 9216, ee.EPI_BIAS, ee.GELU_TANH),
+                                          (4205, 12288, ee.EPI_BIAS_GELU, ee.GELU_TANH),
+                                          (4205, 12288, ee.EPI_BIAS_RESIDUAL, ee.GELU_TANH),
+                                          (4300, 4096, ee.EPI_BIAS_GELU, ee.GELU_ERF)])
+def test_gemm_row_split_bit_identical(M, N, epi, gelu):
+    """Tile counts just past a multiple of the CU count run whole rounds of
+    256 x 256 tiles and the remaining rows on 128 x 128 tiles.  On random data
+    the result must equal, bit for bit, GEMMs over each 256-row block alone
+    (each small enough for 128 x 128 tiles only): every element sums the same
+    K tiles in the same order whichever tile computes it."""
+    K = 1024
+    A = torch.randn(M, K, generator=GEN).half().to(DEV)
+    W = (0.05 * torch.randn(N, K, generator=GEN)).half().to(DEV)
+    bias = (0.1 * torch.randn(N, generator=GEN)).half().to(DEV)
+    R = torch.randn(M, N, generator=GEN).half().to(DEV) if epi == ee.EPI_BIAS_RESIDUAL else None
+    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    ee.ee_linear(A, W, bias, R, epi, C, gelu=gelu)
+    parts = torch.empty_like(C)
+    for r0 in range(0, M, 256):
+        r1 = min(M, r0 + 256)
+        ee.ee_linear(A[r0:r1], W, bias, None if R is None else R[r0:r1], epi, parts[r0:r1], gelu=gelu)
+    torch.cuda.synchronize()
+    diff = (C != parts).any(dim=1).nonzero().flatten().tolist()
+    say(f"row split {M}x{N} epi={epi}: {len(diff)} rows differ from the per-block GEMMs")
+    assert not diff, f"rows {diff[:8]}... differ"
 
 
 @pytest.mark.parametrize("K", [32768, 49152 + 64])

@@ -566,17 +566,50 @@ bool gemm_f16_mfma_ok(int64_t M, int N, int K, const GemmPitch& ld, const void* 
   return M >= 1 && M <= (1 << 30) && N >= 1 && K >= kBK && K % kBK == 0 && pitches && aligned;
 }
 
+// Time of a 128 x 128 tile relative to a 256 x 256 tile of the same K (a
+// quarter of the work at a lower MFMA rate).
+constexpr double kSmallTileCost = 0.36;
+
+// Rows [0, m_big) of a large problem go to the 256 x 256 kernel and the rest
+// to 128 x 128 tiles.  A tile count just past a multiple of the CU count
+// leaves most CUs idle in the last round of 256 x 256 tiles; running only
+// whole rounds of 256-row tiles there and the remaining rows as 128 x 128
+// tiles ends sooner.  Every element sums its K tiles in the same order with
+// the same MFMA K depth in both kernels, so the split changes no bits.
+int64_t gemm_big_rows(int64_t M, int N, int cus) {
+  const int64_t tn = (N + 255) / 256, tiles = ((M + 255) / 256) * tn;
+  const int64_t whole = tiles / cus * cus;
+  if (whole == tiles) return M;
+  const int64_t m_tiles = whole / tn;  // 256-row tiles that fit in the whole rounds
+  const int64_t rest = M - m_tiles * 256;
+  if (m_tiles <= 0 || rest <= 0) return M;
+  const int64_t small = ((rest + 127) / 128) * ((N + 127) / 128);
+  const double t_plain = (double)((tiles + cus - 1) / cus);
+  const double t_split = (double)((m_tiles * tn + cus - 1) / cus) + kSmallTileCost * (double)((small + cus - 1) / cus);
+  return t_split < t_plain ? m_tiles * 256 : M;
+}
+
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
                                 int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_big >= 256) {
-    const int wgs = EE_GEMM_PERSIST ? device_cu_count() : 0;
+    const int cus = device_cu_count();
+    const int wgs = EE_GEMM_PERSIST ? cus : 0;
+    const int64_t m_big = gemm_big_rows(M, N, cus);
+    hipError_t e;
     if (K >= EE_GEMM_DEEP_W_K)
-      return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(A, W, bias, R, (int)M, N, K, ld, epi, form,
-                                                                           C, 1, nullptr, s, wgs);
-    return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 2>(A, W, bias, R, (int)M, N, K, ld, epi, form, C,
-                                                                         1, nullptr, s, wgs);
+      e = launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(A, W, bias, R, (int)m_big, N, K, ld, epi, form,
+                                                                        C, 1, nullptr, s, wgs);
+    else
+      e = launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 2>(A, W, bias, R, (int)m_big, N, K, ld, epi, form,
+                                                                        C, 1, nullptr, s, wgs);
+    if (e != hipSuccess || m_big == M) return e;
+    // the remaining rows: A, C and the residual from row m_big on
+    const f16* a = static_cast<const f16*>(A) + m_big * ld.a;
+    const f16* r = R ? static_cast<const f16*>(R) + m_big * ld.c : nullptr;
+    f16* c = static_cast<f16*>(C) + m_big * ld.c;
+    return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, (int)(M - m_big), N, K, ld, epi, form, c, 1, nullptr, s);
   }
   return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, ld, epi, form, C, 1, nullptr, s);
 }
