@@ -574,8 +574,10 @@ constexpr double kSmallTileCost = 0.36;
 // to 128 x 128 tiles.  A tile count just past a multiple of the CU count
 // leaves most CUs idle in the last round of 256 x 256 tiles; running only
 // whole rounds of 256-row tiles there and the remaining rows as 128 x 128
-// tiles ends sooner.  Every element sums its K tiles in the same order with
-// the same MFMA K depth in both kernels, so the split changes no bits.
+// tiles ends sooner.  Both kernels add an element's K tiles in the same order;
+// their MFMA shapes differ (16x16x32 and 32x32x16), and on gfx950 they give
+// the same bits for every element (tested on random data against GEMMs run
+// on each 256-row block alone), so the split changes no results.
 int64_t gemm_big_rows(int64_t M, int N, int cus) {
   const int64_t tn = (N + 255) / 256, tiles = ((M + 255) / 256) * tn;
   const int64_t whole = tiles / cus * cus;
