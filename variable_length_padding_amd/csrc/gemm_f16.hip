@@ -33,6 +33,9 @@
 //     the 8 XCDs, so ids are remapped to give each XCD a contiguous range, and
 //     that range walks tiles in groups of 4 M-tiles, so the workgroups that
 //     share an XCD's L2 share A and W panels.
+//   * A 256 x 256 tile count just past a multiple of the CU count runs whole
+//     rounds of 256-row tiles and the remaining rows as 128 x 128 tiles (a
+//     second launch), when that is estimated to end sooner (gemm_big_rows).
 //   * Epilogues go through LDS so C and the residual move in 16-byte vectors
 //     (store_tile_staged); a direct per-element store covers N % 8 != 0.
 //   * Ragged M (and N): the buffer descriptors end at the last valid row, so
