@@ -129,7 +129,7 @@ def _small_ints(shape, lo=-2, hi=2):
                                    (1000, 1000, 640), (4112, 768, 3072), (2048, 4096, 12288),
                                    (4100, 4200, 320), (4096, 4096, 1024), (4096, 4096, 64), (4300, 4096, 192),
                                    (4096, 4104, 128), (4096, 4099, 64), (4096, 4096, 256), (4096, 4352, 384),
-                                   (4096, 4096, 12288), (4205, 9216, 512)])
+                                   (4096, 4096, 12288), (4205, 9216, 512), (4205, 12288, 512)])
 @pytest.mark.parametrize("epi", [ee.EPI_NONE, ee.EPI_BIAS, ee.EPI_BIAS_RESIDUAL])
 def test_gemm_integer_exact(M, N, K, epi):
     """Small-integer fp16 operands: every product and partial sum is an integer
@@ -161,7 +161,8 @@ def test_gemm_integer_exact(M, N, K, epi):
                                           (4300, 4096, ee.EPI_BIAS_GELU, ee.GELU_ERF)])
 def test_gemm_row_split_bit_identical(M, N, epi, gelu):
     """Tile counts just past a multiple of the CU count run whole rounds of
-    256 x 256 tiles and the remaining rows on 128 x 128 tiles.  On random data
+    256 x 256 tiles and the remaining rows on 128 x 128 tiles (128 x 64 when
+    few: the 12288-wide shapes and 4300 x 4096).  On random data
     the result must equal, bit for bit, GEMMs over each 256-row block alone
     (each small enough for 128 x 128 tiles only): every element sums the same
     K tiles in the same order whichever tile computes it."""

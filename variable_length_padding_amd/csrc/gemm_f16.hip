@@ -614,7 +614,12 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
     const f16* a = static_cast<const f16*>(A) + m_big * ld.a;
     const f16* r = R ? static_cast<const f16*>(R) + m_big * ld.c : nullptr;
     f16* c = static_cast<f16*>(C) + m_big * ld.c;
-    return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, (int)(M - m_big), N, K, ld, epi, form, c, 1, nullptr, s);
+    const int64_t rest = M - m_big;
+    // Few remaining rows stream all of W through few tiles: 128 x 64 tiles
+    // (the same MFMA shape) put twice as many CUs on it.
+    if (((rest + 127) / 128) * ((N + 127) / 128) * 2 <= cus)
+      return launch_cfg<32, 128, 64, 2, 2>(a, W, bias, r, (int)rest, N, K, ld, epi, form, c, 1, nullptr, s);
+    return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, (int)rest, N, K, ld, epi, form, c, 1, nullptr, s);
   }
   return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, ld, epi, form, C, 1, nullptr, s);
 }
