@@ -218,7 +218,9 @@ EE_API ee_status ee_layernorm(const void* x, const void* gamma, const void* beta
 
 /* C[M, N] = epilogue(A[M, K] . W[N, K]^T): bias [N], residual [M, N] (may not
  * alias C).  fp16: MFMA kernels, fp32 accumulation, one rounding to fp16 at
- * the end.  fp32: fp32 FMA kernels.  M may be 0 (no work).  All matrices
+ * the end; row r of C depends only on row r of A (and of the residual), with
+ * the same bits whatever M is, so a sequence gives the same result alone or in
+ * any batch.  fp32: fp32 FMA kernels.  M may be 0 (no work).  All matrices
  * dense; ee_linear_strided is the general form. */
 EE_API ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual,
                     int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
