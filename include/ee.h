@@ -169,15 +169,24 @@ EE_API ee_status ee_layer_forward(ee_layer* layer, const void* x_padded, const i
                            int32_t batch, int32_t pad_len, void* y_padded,
                            void* workspace, size_t ws_bytes, void* stream);
 
-/* n_layers layers with one offsets/remove before and one rebuild after; the
- * packed output of layer l is the input of layer l+1.  All layers must share
- * one descriptor. */
+/* A stack (the EnergonAI README, "Scaling Ability" and "Latency": GPT-3
+ * stacks of 12, 24 and 48 layers with redundant-computation elimination):
+ * n_layers layers with one offsets/remove before and one rebuild after; the
+ * packed output of layer l is the input of layer l+1, so the padding is
+ * removed once per stack.  All layers must share one descriptor.  Arguments
+ * and errors as ee_layer_forward, plus EE_ERR_INVALID_ARG for n_layers < 1, a
+ * NULL layer or layers with different descriptors.  The workspace is that of
+ * one layer (ee_layer_workspace_size): layers reuse it in turn. */
 EE_API ee_status ee_stack_forward(ee_layer* const* layers, int32_t n_layers, const void* x_padded,
                            const int32_t* seq_lens, int32_t batch, int32_t pad_len,
                            void* y_padded, void* workspace, size_t ws_bytes, void* stream);
 
 /* ---- offsets (the attention mask prefix-summed into token offsets) ------- */
-/* From host lengths.  Writes, on `stream`:
+/* The packed position of every valid token, which the announcement article's
+ * "Runtime" ops need to move rows between the padded and the packed layout
+ * (the README's "Scaling Ability" and "Latency" runs give each sequence a
+ * length below the padding length).
+ * From host lengths.  Writes, on `stream`:
  *   d_cu        [batch+1]        cu[0]=0, cu[b+1]=cu[b]+len[b]
  *   d_token_src [batch*pad_len]  token_src[t] = b*pad_len + t - cu[b] for t < T
  *                                (entries >= T are left untouched)
@@ -199,13 +208,25 @@ EE_API ee_status ee_compute_offsets_mask(const uint8_t* d_mask, int32_t batch, i
 /* Bytes of workspace the two calls below need (the offsets arrays). */
 EE_API ee_status ee_padding_workspace_size(int32_t batch, int32_t pad_len, size_t* bytes);
 
-/* packed[t, :] = padded[token_src[t], :].  d_padded [batch, pad_len, hidden],
- * d_packed [T, hidden] (T = sum(len)); hidden*sizeof(dtype) % 16 == 0. */
+/* transpose_padding_remove (announcement article, "Runtime"), read as a row
+ * gather: packed[t, :] = padded[token_src[t], :], the valid rows in sequence
+ * order.  d_padded [batch, pad_len, hidden], d_packed [T, hidden] (T =
+ * sum(len), caller-owned, at least T rows); hidden*sizeof(dtype) % 16 == 0.
+ * seq_lens host.  workspace: ee_padding_workspace_size(batch, pad_len) bytes of
+ * device memory (the offsets arrays, rewritten by the call).  Errors:
+ * EE_ERR_INVALID_ARG for lengths outside [0, pad_len], batch outside
+ * [1, EE_MAX_BATCH], NULL or misaligned pointers, overlapping buffers;
+ * EE_ERR_UNSUPPORTED for a row that is not a multiple of 16 bytes;
+ * EE_ERR_WORKSPACE for a small workspace. */
 EE_API ee_status ee_remove_padding(const void* d_padded, const int32_t* seq_lens, int32_t batch,
                             int32_t pad_len, int32_t hidden, ee_dtype dtype, void* d_packed,
                             void* workspace, size_t ws_bytes, void* stream);
 
-/* padded[r, :] = packed[pad2pack[r], :], or +0.0 where pad2pack[r] = -1. */
+/* transpose_padding_rebuild (announcement article, "Runtime"; spelt
+ * "rebulid" there), read as a row scatter: padded[r, :] = packed[pad2pack[r], :],
+ * or +0.0 (bit pattern 0) where pad2pack[r] = -1, i.e. on every pad row, so the
+ * whole [batch, pad_len, hidden] output is written.  Arguments, workspace and
+ * errors as ee_remove_padding. */
 EE_API ee_status ee_rebuild_padding(const void* d_packed, const int32_t* seq_lens, int32_t batch,
                              int32_t pad_len, int32_t hidden, ee_dtype dtype, void* d_padded,
                              void* workspace, size_t ws_bytes, void* stream);
@@ -218,10 +239,17 @@ EE_API ee_status ee_layernorm(const void* x, const void* gamma, const void* beta
 
 /* C[M, N] = epilogue(A[M, K] . W[N, K]^T): bias [N], residual [M, N] (may not
  * alias C).  fp16: MFMA kernels, fp32 accumulation, one rounding to fp16 at
- * the end; row r of C depends only on row r of A (and of the residual), with
- * the same bits whatever M is, so a sequence gives the same result alone or in
- * any batch.  fp32: fp32 FMA kernels.  M may be 0 (no work).  All matrices
- * dense; ee_linear_strided is the general form. */
+ * the end; row r of C depends only on row r of A (and of the residual).  Every
+ * kernel adds an element's K tiles in the same order, so the bits do not
+ * depend on M either, and a sequence gives the same result alone or in any
+ * batch -- provided the two MFMA shapes the kernels use (16x16x32 for large
+ * problems, 32x32x16 for small ones and for the rows past whole rounds of
+ * large tiles) sum a K step in the same way.  That is measured on gfx950, not
+ * derived from a specification: random-data tests compare large GEMMs with
+ * GEMMs over each 256-row block alone (test_gemm_row_split_bit_identical) and
+ * sequences of 48-layer batches run alone (test_stream_sequence_alone_equals_batch).
+ * fp32: fp32 FMA kernels.  M may be 0 (no work).  All matrices dense;
+ * ee_linear_strided is the general form. */
 EE_API ee_status ee_linear(const void* A, const void* W, const void* bias, const void* residual,
                     int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
                     ee_gelu gelu, void* C, void* stream);
@@ -322,11 +350,17 @@ EE_API ee_status ee_add_bias_residual_layernorm(const void* u, const void* bias,
 
 /* ---- per-kernel timing ----------------------------------------------------- */
 /* While enabled, every kernel that the calls above launch from this process is
- * bracketed by a pair of hipEvents recorded on its launch stream. */
+ * bracketed by a pair of hipEvents recorded on its launch stream.  A GEMM site
+ * whose rows run as two launches (whole rounds of 256-row tiles, then the
+ * remaining rows on smaller tiles) records the second as site "<site>_rest",
+ * e.g. "gemm_fc1_rest". */
 typedef struct {
   char name[32];      /* launch site, e.g. "gemm_fc1", "attention", "remove" */
   int64_t launches;
   double total_ms;    /* sum of event-measured durations */
+  double flops;       /* sum of the launches' algorithmic flops (GEMM sites: 2*rows*N*K; else 0) */
+  char kernel[96];    /* the kernel the site launched, e.g. "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 2>"
+                         (template arguments in declaration order), "several kernels", or "" if not recorded */
 } ee_kernel_stat;
 
 EE_API ee_status ee_profile_enable(int32_t on);

@@ -2,7 +2,8 @@
 times (ee_stack_forward over the whole batch), on sampled outputs the CPU
 oracle computes one sequence at a time (sequences are independent, so a
 sampled sequence's rows are exact rows of the batch), plus properties that
-hold at any size.  These tests hold tens to ~180 GB of weights in HBM."""
+hold at any size.  These tests hold up to ~45 GB of weights in HBM; the
+48-layer request stream has a module of its own (test_gpu_stream.py)."""
 import numpy as np
 import pytest
 import torch
@@ -83,34 +84,6 @@ def test_gpt3_tp4_shard_sampled_sequences():
         err = normwise_rel(to_host64(y[b, :lens[b]]), ref[cu[i]:cu[i + 1]])
         say(f"gpt3-tp4-shard sequence {b} (len {lens[b]}): rel {err:.3e}")
         assert err <= 2e-2
-
-
-@pytest.mark.timeout(900)
-def test_gpt3_48l_stream_sequence_independence():
-    """The 48-layer request stream: two FIFO batches (the first and the last)
-    through all 48 layers; the shortest and longest sequence of each, run alone
-    and unpadded, must reproduce their rows of the batch bit for bit (the GEMM
-    K order does not depend on M or the tile, attention and LayerNorm are per
-    sequence / per row).  Pads +0.0, outputs finite."""
-    torch.cuda.empty_cache()
-    w = workloads.get("gpt3-48l-stream")
-    groups = workloads.request_stream(w, SEED)
-    params = [ee.pitched_weights(workloads.layer_params(w, SEED, l, device=DEV)) for l in range(w.layers)]
-    hs = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, p, dtype=ee.F16) for p in params]
-    for gi in (0, len(groups) - 1):
-        lens = groups[gi]
-        P = max(lens)                                  # padded to the batch's own maximum
-        x = workloads.activations(w, SEED, len(lens), P, lens, device=DEV, stream=1 + 1000 * (gi + 1))
-        y = _stack(hs, x, lens)
-        _pads_zero(y, lens)
-        assert torch.isfinite(y).all()
-        order = sorted(range(len(lens)), key=lambda b: lens[b])
-        for b in (order[0], order[-1]):
-            n = lens[b]
-            y1 = _stack(hs, x[b:b + 1, :n].contiguous(), [n])
-            same = torch.equal(y1[0], y[b, :n])
-            say(f"gpt3-48l-stream batch {gi} (T={sum(lens)}, P={P}) sequence {b} (len {n}) alone == in batch: {same}")
-            assert same
 
 
 def test_gpt3_width_decode_sampled():

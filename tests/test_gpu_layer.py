@@ -13,7 +13,7 @@ import torch
 import oracle
 import variable_length_padding_amd as ee
 import workloads
-from gpu_helpers import DEV, normwise_rel, say, to_host64, valid_mask
+from gpu_helpers import DEV, Guarded, normwise_rel, say, to_host64, valid_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -26,14 +26,17 @@ def _run_layer(w, lens, x, params, fuse_gelu=True, gelu=ee.GELU_TANH, layers_par
     layers = [ee.Layer(w.hidden, w.n_heads, w.head_dim, w.ffn, dp, dtype=dt, gelu=gelu, fuse_gelu=fuse_gelu,
                        residual=residual) for dp in dev_params]
     B, P, _ = x.shape
-    ws = torch.empty(layers[0].workspace_size(B, P, sum(lens)), dtype=torch.uint8, device=DEV)
+    gws = Guarded((layers[0].workspace_size(B, P, sum(lens)),), torch.uint8)
     xd = x.to(DEV)
-    y = torch.full_like(xd, 9.0)
+    gy = Guarded(xd.shape, xd.dtype, fill=9.0)
+    y = gy.t
     if len(layers) == 1:
-        layers[0].forward(xd, lens, y, ws)
+        layers[0].forward(xd, lens, y, gws.t)
     else:
-        ee.ee_stack_forward(layers, xd, lens, y, ws)
+        ee.ee_stack_forward(layers, xd, lens, y, gws.t)
     torch.cuda.synchronize()
+    gy.check("y")
+    gws.check("the workspace")
     return y
 
 
@@ -165,6 +168,14 @@ def test_profile_records_every_launch_site():
     for site in ("offsets", "remove", "ln1", "gemm_qkv", "attention", "gemm_out", "ln2", "gemm_fc1", "gemm_fc2",
                  "rebuild"):
         assert stats[site]["launches"] == 1 and stats[site]["total_ms"] > 0
+    # GEMM sites carry their algorithmic flops and the kernel they ran (few
+    # 256 x 256 tiles at this size: the 128 x 128 tile kernel)
+    T = sum(lens)
+    for site, (K, N, epi) in {"gemm_qkv": (768, 3 * 768, 1), "gemm_out": (768, 768, 2), "gemm_fc1": (768, 3072, 3),
+                              "gemm_fc2": (3072, 768, 2)}.items():
+        assert stats[site]["flops"] == 2.0 * T * K * N
+        assert stats[site]["kernel"] == f"gemm_f16_mfma_kernel<32, 128, 128, 2, 2, {epi}, 2>"
+    assert stats["attention"]["flops"] == 0 and not any(s.endswith("_rest") for s in stats)
 
 
 def test_profile_filter_times_one_site():

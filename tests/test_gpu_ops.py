@@ -10,7 +10,7 @@ import torch
 
 import oracle
 import variable_length_padding_amd as ee
-from gpu_helpers import DEV, normwise_rel, say, to_host64, valid_mask
+from gpu_helpers import DEV, Guarded, normwise_rel, say, to_host64, valid_mask
 
 pytestmark = pytest.mark.gpu
 
@@ -86,12 +86,18 @@ def test_remove_rebuild_bit_exact(dtype, H, lens, P):
     x[torch.from_numpy(~mask)] = float("nan")          # pads must never reach the output
     xd = x.to(DEV)
     T = sum(lens)
-    packed = torch.full((max(T, 1), H), 3.0, dtype=dtype, device=DEV)
-    ws = torch.empty(ee.ee_padding_workspace_size(B, P), dtype=torch.uint8, device=DEV)
+    gp = Guarded((max(T, 1), H), dtype, fill=3.0)
+    packed = gp.t
+    gws = Guarded((ee.ee_padding_workspace_size(B, P),), torch.uint8)
+    ws = gws.t
     ee.ee_remove_padding(xd, lens, packed, ws)
-    y = torch.full((B, P, H), 5.0, dtype=dtype, device=DEV)
+    gy = Guarded((B, P, H), dtype, fill=5.0)
+    y = gy.t
     ee.ee_rebuild_padding(packed, lens, y, ws)
     torch.cuda.synchronize()
+    gp.check("packed")
+    gy.check("y")
+    gws.check("the workspace")
     xn = x.numpy()
     ref_packed = oracle.remove_padding(xn, lens)
     if T:
@@ -111,9 +117,11 @@ def test_layernorm_parity(dtype, H, rows, tol):
     x = (torch.randn(rows, H, generator=GEN) * 3 + 0.7).to(dtype)
     g = (1 + 0.1 * torch.randn(H, generator=GEN)).to(dtype)
     b = (0.1 * torch.randn(H, generator=GEN)).to(dtype)
-    y = torch.empty(rows, H, dtype=dtype, device=DEV)
+    gy = Guarded((rows, H), dtype)
+    y = gy.t
     ee.ee_layernorm(x.to(DEV), g.to(DEV), b.to(DEV), 1e-5, y)
     torch.cuda.synchronize()
+    gy.check("y")
     ref = oracle.layer_norm(x.double().numpy(), g.double().numpy(), b.double().numpy(), 1e-5)
     err = normwise_rel(to_host64(y), ref)
     say(f"layernorm {dtype} H={H}: rel {err:.2e}")
@@ -139,10 +147,12 @@ def test_gemm_integer_exact(M, N, K, epi):
     A, W = _small_ints((M, K)), _small_ints((N, K))
     bias = _small_ints((N,)) if epi != ee.EPI_NONE else None
     R = _small_ints((M, N), -8, 8) if epi == ee.EPI_BIAS_RESIDUAL else None
-    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    gc = Guarded((M, N), torch.float16)
+    C = gc.t
     ee.ee_linear(A.to(DEV), W.to(DEV), None if bias is None else bias.to(DEV), None if R is None else R.to(DEV),
                  epi, C)
     torch.cuda.synchronize()
+    gc.check("C")
     exact = A.double().numpy() @ W.double().numpy().T
     if bias is not None:
         exact = exact + bias.double().numpy()
@@ -198,6 +208,46 @@ def test_gemm_integer_exact_long_k(K):
     exact = A[rows].double().numpy() @ W.double().numpy().T + bias.double().numpy() + R[rows].double().numpy()
     assert np.abs(exact).max() < 2 ** 24
     got = C[rows].cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
+
+
+@pytest.mark.parametrize("M,rest_kernel", [(4205, "gemm_f16_mfma_kernel<32, 128, 64, 2, 2, 2, 2>"),
+                                           (8457, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 2, 2>")])
+def test_gemm_integer_exact_row_split_long_k(M, rest_kernel):
+    """The FC2 shape of the layer (N = 12288, K = 49152, A and W rows at the
+    preferred 49216-element pitch) at row counts whose 256 x 256 tile count is
+    just past a multiple of the CU count: whole rounds of 256-row tiles on the
+    three-W-stage kernel (timed as site "linear"), the remaining rows on
+    smaller tiles (site "linear_rest").  Small-integer operands, so the result
+    is the fp16 rounding of the exact sum, bit for bit, on sampled rows of
+    both parts."""
+    N, K = 12288, 49152
+    ld = ee.ee_preferred_row_pitch(K)
+    assert ld == K + 64
+    A = torch.zeros(M, ld, dtype=torch.float16)
+    A[:, :K] = _small_ints((M, K))
+    W = torch.zeros(N, ld, dtype=torch.float16)
+    W[:, :K] = _small_ints((N, K))
+    bias, R = _small_ints((N,)), _small_ints((M, N), -8, 8)
+    Ad, Wd = A.to(DEV)[:, :K], W.to(DEV)[:, :K]
+    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    ee.ee_profile_enable(True)
+    try:
+        ee.ee_linear(Ad, Wd, bias.to(DEV), R.to(DEV), ee.EPI_BIAS_RESIDUAL, C)
+        st = ee.ee_profile_collect()
+    finally:
+        ee.ee_profile_enable(False)
+    torch.cuda.synchronize()
+    m_big = M // 256 * 256 if M == 4205 else 8192
+    assert st["linear"]["kernel"] == "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3>"
+    assert st["linear_rest"]["kernel"] == rest_kernel
+    assert st["linear"]["flops"] == 2.0 * m_big * N * K and st["linear_rest"]["flops"] == 2.0 * (M - m_big) * N * K
+    rows = [0, 1, 255, m_big - 1, m_big, m_big + 1, (m_big + M) // 2, M - 1]
+    exact = (A[rows, :K].double().numpy() @ W[:, :K].double().numpy().T + bias.double().numpy() +
+             R[rows].double().numpy())
+    assert np.abs(exact).max() < 2 ** 24
+    got = C[rows].cpu().numpy()
+    say(f"row split M={M} at K={K}: rest {M - m_big} rows on {rest_kernel}")
     assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
 
 
@@ -307,10 +357,12 @@ def test_attention_varlen_parity(dtype, hd, nh, tol):
     cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu_h[-1])
     qkv = torch.randn(T, 3 * nh * hd, generator=GEN).to(dtype)
-    o = torch.full((T, nh * hd), 7.0, dtype=dtype, device=DEV)
+    go = Guarded((T, nh * hd), dtype, fill=7.0)
+    o = go.t
     cu = torch.tensor(cu_h, device=DEV)
     ee.ee_attention_varlen(qkv.to(DEV), cu, len(lens), max(lens), nh, hd, o)
     torch.cuda.synchronize()
+    go.check("o")
     ref = oracle.causal_attention_packed(qkv.double().numpy(), cu_h, nh, hd)
     got = to_host64(o)
     err = normwise_rel(got, ref)
@@ -335,10 +387,12 @@ def test_attention_long_sequences(dtype, hd, nh, tol, causal):
     cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
     T = int(cu_h[-1])
     qkv = torch.randn(T, 3 * nh * hd, generator=GEN).to(dtype)
-    o = torch.full((T, nh * hd), 7.0, dtype=dtype, device=DEV)
+    go = Guarded((T, nh * hd), dtype, fill=7.0)
+    o = go.t
     ee.ee_attention_varlen(qkv.to(DEV), torch.tensor(cu_h, device=DEV), len(lens), max(lens), nh, hd, o,
                            causal=causal)
     torch.cuda.synchronize()
+    go.check("o")
     if causal:
         ref = oracle.causal_attention_packed(qkv.double().numpy(), cu_h, nh, hd)
     else:

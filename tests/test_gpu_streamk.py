@@ -127,4 +127,4 @@ def test_streamk_errors():
     with pytest.raises(ee.EEError, match="EE_ERR_UNSUPPORTED"):
         ee.ee_linear_streamk(A.float(), W.float(), None, None, ee.EPI_NONE, C.float(), ws)
     with pytest.raises(ee.EEError, match="EE_ERR_INVALID_ARG"):
-        ee.ee_linear_streamk(A, W, None, None, ee.EPI_NONE, A[:, :N], ws)   # C overlaps A
+        ee.ee_linear_streamk(A, W, None, None, ee.EPI_NONE, A.view(-1)[:M * N].view(M, N), ws)   # C overlaps A

@@ -40,7 +40,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, "libee.so")
+    """The in-tree libee.so, or the build EE_LIBRARY names (a host-sanitizer
+    build of the same sources, see build.py)."""
+    return os.environ.get("EE_LIBRARY") or os.path.join(_HERE, "libee.so")
 
 
 class EEError(RuntimeError):
@@ -72,7 +74,8 @@ class LayerWeights(C.Structure):
 
 
 class KernelStat(C.Structure):
-    _fields_ = [("name", C.c_char * 32), ("launches", C.c_int64), ("total_ms", C.c_double)]
+    _fields_ = [("name", C.c_char * 32), ("launches", C.c_int64), ("total_ms", C.c_double), ("flops", C.c_double),
+                ("kernel", C.c_char * 96)]
 
 
 class BatchCost(C.Structure):
@@ -204,9 +207,57 @@ def _lens(lens: Sequence[int]):
     return arr
 
 
+# ---------------------------------------------------------------- argument checks
+# Run before any library call: the library validates sizes and pointers, but
+# only the binding sees a tensor's shape, dtype, layout and device, and a
+# lengths list shorter than the batch would make the library read past it.
+def _torch_dtype(code: int):
+    import torch
+    return torch.float16 if code == F16 else torch.float32
+
+
+def _shape_ok(t, shape) -> bool:
+    return t.dim() == len(shape) and all(s is None or int(a) == int(s) for a, s in zip(t.shape, shape))
+
+
+def _need(t, name: str, shape=None, dtype=None, contiguous: bool = True):
+    """A tensor argument: its shape (None entries free), dtype and layout."""
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if shape is not None and not _shape_ok(t, shape):
+        want = "[" + ", ".join("*" if s is None else str(int(s)) for s in shape) + "]"
+        raise ValueError(f"{name} has shape {list(t.shape)}, need {want}")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, need {dtype}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _need_lens(lens: Sequence[int], batch: int, name: str = "lens"):
+    if len(lens) != batch:
+        raise ValueError(f"{name} has {len(lens)} entries for a batch of {batch}")
+
+
+def _need_gpu(**tensors):
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor (device {t.device})")
+
+
+def _need_workspace(ws, name: str = "workspace"):
+    _need(ws, name)
+    _need_gpu(**{name: ws})
+
+
 # ---------------------------------------------------------------- offsets
 def ee_compute_offsets(lens: Sequence[int], pad_len: int, cu, token_src, pad2pack, stream=None) -> int:
     """Host lengths -> device cu [B+1], token_src [B*P], pad2pack [B*P] (int32); returns T."""
+    import torch
+    B = len(lens)
+    _need(cu, "cu", (B + 1,), torch.int32)
+    _need(token_src, "token_src", (B * pad_len,), torch.int32)
+    _need(pad2pack, "pad2pack", (B * pad_len,), torch.int32)
+    _need_gpu(cu=cu, token_src=token_src, pad2pack=pad2pack)
     total = C.c_int32(0)
     _check(lib().ee_compute_offsets(_lens(lens), len(lens), pad_len, _ptr(cu), _ptr(token_src), _ptr(pad2pack),
                                     C.byref(total), _stream(stream)), "ee_compute_offsets")
@@ -215,7 +266,16 @@ def ee_compute_offsets(lens: Sequence[int], pad_len: int, cu, token_src, pad2pac
 
 def ee_compute_offsets_mask(mask, cu, token_src, pad2pack, total, stream=None):
     """Device uint8 mask [B, P] -> cu, token_src, pad2pack, total (device int32)."""
+    import torch
+    if mask is None or mask.dim() != 2:
+        raise ValueError("mask must be [batch, pad_len]")
     B, P = mask.shape
+    _need(mask, "mask", (B, P), torch.uint8)
+    _need(cu, "cu", (B + 1,), torch.int32)
+    _need(token_src, "token_src", (B * P,), torch.int32)
+    _need(pad2pack, "pad2pack", (B * P,), torch.int32)
+    _need(total, "total", (1,), torch.int32)
+    _need_gpu(mask=mask, cu=cu, token_src=token_src, pad2pack=pad2pack, total=total)
     _check(lib().ee_compute_offsets_mask(_ptr(mask), B, P, _ptr(cu), _ptr(token_src), _ptr(pad2pack), _ptr(total),
                                          _stream(stream)), "ee_compute_offsets_mask")
 
@@ -226,15 +286,31 @@ def ee_padding_workspace_size(batch: int, pad_len: int) -> int:
     return n.value
 
 
-def ee_remove_padding(padded, lens: Sequence[int], packed, workspace, stream=None):
+def _padding_args(padded, lens, packed, workspace, packed_name):
+    if padded is None or padded.dim() != 3:
+        raise ValueError("the padded tensor must be [batch, pad_len, hidden]")
     B, P, H = padded.shape
+    _need_lens(lens, B)
+    _dtype_code(padded)
+    _need(padded, "padded", (B, P, H))
+    T = sum(int(n) for n in lens)
+    _need(packed, packed_name, (None, H), padded.dtype)
+    if packed.shape[0] < T:
+        raise ValueError(f"{packed_name} has {packed.shape[0]} rows, need sum(lens) = {T}")
+    _need_gpu(padded=padded, **{packed_name: packed})
+    _need_workspace(workspace)
+    return B, P, H
+
+
+def ee_remove_padding(padded, lens: Sequence[int], packed, workspace, stream=None):
+    B, P, H = _padding_args(padded, lens, packed, workspace, "packed")
     _check(lib().ee_remove_padding(_ptr(padded), _lens(lens), B, P, H, _dtype_code(padded), _ptr(packed),
                                    _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "ee_remove_padding")
 
 
 def ee_rebuild_padding(packed, lens: Sequence[int], padded, workspace, stream=None):
-    B, P, H = padded.shape
+    B, P, H = _padding_args(padded, lens, packed, workspace, "packed")
     _check(lib().ee_rebuild_padding(_ptr(packed), _lens(lens), B, P, H, _dtype_code(padded), _ptr(padded),
                                     _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream)),
            "ee_rebuild_padding")
@@ -242,16 +318,40 @@ def ee_rebuild_padding(packed, lens: Sequence[int], padded, workspace, stream=No
 
 # ---------------------------------------------------------------- row ops
 def ee_layernorm(x, gamma, beta, eps: float, y, stream=None):
+    if x is None or x.dim() != 2:
+        raise ValueError("x must be [rows, hidden]")
     rows, H = x.shape
+    _dtype_code(x)
+    _need(x, "x", (rows, H))
+    _need(y, "y", (rows, H), x.dtype)
+    _need(gamma, "gamma", (H,), x.dtype)
+    _need(beta, "beta", (H,), x.dtype)
+    _need_gpu(x=x, y=y, gamma=gamma, beta=beta)
     _check(lib().ee_layernorm(_ptr(x), _ptr(gamma), _ptr(beta), rows, H, eps, _dtype_code(x), _ptr(y),
                               _stream(stream)), "ee_layernorm")
+
+
+def _linear_args(A, W, bias, residual, epi, C_out, strided):
+    if A is None or A.dim() != 2 or W is None or W.dim() != 2:
+        raise ValueError("A must be [M, K] and W [N, K]")
+    M, K = A.shape
+    N = W.shape[0]
+    _dtype_code(A)
+    _need(A, "A", (M, K), contiguous=not strided)
+    _need(W, "W", (N, K), A.dtype, contiguous=not strided)
+    _need(C_out, "C_out", (M, N), A.dtype, contiguous=not strided)
+    if epi != EPI_NONE or bias is not None:
+        _need(bias, "bias", (N,), A.dtype)
+    if epi == EPI_BIAS_RESIDUAL or residual is not None:
+        _need(residual, "residual", (M, N), A.dtype, contiguous=not strided)
+    _need_gpu(A=A, W=W, bias=bias, residual=residual, C_out=C_out)
+    return M, N, K
 
 
 def ee_linear(A, W, bias, residual, epi: int, C_out, gelu: int = GELU_TANH, stream=None):
     """C_out = epilogue(A . W^T); 2-D tensors whose rows may be strided
     (unit column stride): their row strides are passed as the pitches."""
-    M, K = A.shape
-    N = W.shape[0]
+    M, N, K = _linear_args(A, W, bias, residual, epi, C_out, strided=True)
     if all(t is None or t.is_contiguous() for t in (A, W, residual, C_out)):
         _check(lib().ee_linear(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
                                _ptr(C_out), _stream(stream)), "ee_linear")
@@ -297,8 +397,8 @@ def ee_linear_splitk_workspace_size(M: int, N: int, splits: int) -> int:
 
 def ee_linear_splitk(A, W, bias, residual, epi: int, C_out, splits: int, workspace, gelu: int = GELU_TANH,
                      stream=None):
-    M, K = A.shape
-    N = W.shape[0]
+    M, N, K = _linear_args(A, W, bias, residual, epi, C_out, strided=False)
+    _need_workspace(workspace)
     _check(lib().ee_linear_splitk(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
                                   splits, _ptr(C_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _stream(stream)), "ee_linear_splitk")
@@ -311,21 +411,37 @@ def ee_linear_streamk_workspace_size(M: int, N: int, K: int) -> int:
 
 
 def ee_linear_streamk(A, W, bias, residual, epi: int, C_out, workspace, gelu: int = GELU_TANH, stream=None):
-    M, K = A.shape
-    N = W.shape[0]
+    M, N, K = _linear_args(A, W, bias, residual, epi, C_out, strided=False)
+    _need_workspace(workspace)
     _check(lib().ee_linear_streamk(_ptr(A), _ptr(W), _ptr(bias), _ptr(residual), M, N, K, _dtype_code(A), epi, gelu,
                                    _ptr(C_out), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                    _stream(stream)), "ee_linear_streamk")
 
 
 def ee_bias_gelu(u, bias, g, gelu: int = GELU_TANH, stream=None):
+    if u is None or u.dim() != 2:
+        raise ValueError("u must be [rows, cols]")
     rows, cols = u.shape
+    _dtype_code(u)
+    _need(u, "u", (rows, cols))
+    _need(bias, "bias", (cols,), u.dtype)
+    _need(g, "g", (rows, cols), u.dtype)
+    _need_gpu(u=u, bias=bias, g=g)
     _check(lib().ee_bias_gelu(_ptr(u), _ptr(bias), rows, cols, _dtype_code(u), gelu, _ptr(g), _stream(stream)),
            "ee_bias_gelu")
 
 
 def ee_attention_varlen(qkv, cu, batch: int, max_len: int, n_heads: int, head_dim: int, o, causal: bool = True,
                         stream=None):
+    import torch
+    Hp = n_heads * head_dim
+    if qkv is None or qkv.dim() != 2:
+        raise ValueError("qkv must be [T, 3 * n_heads * head_dim]")
+    _dtype_code(qkv)
+    _need(qkv, "qkv", (None, 3 * Hp))
+    _need(o, "o", (qkv.shape[0], Hp), qkv.dtype)
+    _need(cu, "cu", (batch + 1,), torch.int32)
+    _need_gpu(qkv=qkv, o=o, cu=cu)
     _check(lib().ee_attention_varlen(_ptr(qkv), _ptr(cu), batch, max_len, n_heads, head_dim, qkv.shape[0],
                                      1 if causal else 0, _dtype_code(qkv), _ptr(o), _stream(stream)),
            "ee_attention_varlen")
@@ -333,14 +449,32 @@ def ee_attention_varlen(qkv, cu, batch: int, max_len: int, n_heads: int, head_di
 
 def ee_attention_padded(q, k, v, cu, o, causal: bool = True, stream=None):
     """q, k, v, o: [B, nh, P, hd] head-major padded; cu [B+1] device int32."""
+    import torch
+    if q is None or q.dim() != 4:
+        raise ValueError("q must be [batch, n_heads, pad_len, head_dim]")
     B, nh, P, hd = q.shape
+    _dtype_code(q)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _need(t, name, (B, nh, P, hd), q.dtype)
+    _need(cu, "cu", (B + 1,), torch.int32)
+    _need_gpu(q=q, k=k, v=v, o=o, cu=cu)
     _check(lib().ee_attention_padded(_ptr(q), _ptr(k), _ptr(v), _ptr(cu), B, P, nh, hd, 1 if causal else 0,
                                      _dtype_code(q), _ptr(o), _stream(stream)), "ee_attention_padded")
 
 
 def ee_transpose_padding_rebuild_heads(packed, lens: Sequence[int], heads, workspace, stream=None):
     """packed [T, n*nh*hd] -> heads [n, B, nh, P, hd] (pads zero)."""
+    if heads is None or heads.dim() != 5:
+        raise ValueError("heads must be [n_mats, batch, n_heads, pad_len, head_dim]")
     n, B, nh, P, hd = heads.shape
+    _need_lens(lens, B)
+    _dtype_code(heads)
+    _need(heads, "heads", (n, B, nh, P, hd))
+    _need(packed, "packed", (None, n * nh * hd), heads.dtype)
+    if packed.shape[0] < sum(int(x) for x in lens):
+        raise ValueError(f"packed has {packed.shape[0]} rows, need sum(lens) = {sum(int(x) for x in lens)}")
+    _need_gpu(packed=packed, heads=heads)
+    _need_workspace(workspace)
     _check(lib().ee_transpose_padding_rebuild_heads(_ptr(packed), _lens(lens), B, P, n, nh, hd, _dtype_code(heads),
                                                     _ptr(heads), _ptr(workspace),
                                                     workspace.numel() * workspace.element_size(), _stream(stream)),
@@ -349,7 +483,17 @@ def ee_transpose_padding_rebuild_heads(packed, lens: Sequence[int], heads, works
 
 def ee_transpose_padding_remove_heads(heads, lens: Sequence[int], packed, workspace, stream=None):
     """heads [B, nh, P, hd] -> packed [T, nh*hd]."""
+    if heads is None or heads.dim() != 4:
+        raise ValueError("heads must be [batch, n_heads, pad_len, head_dim]")
     B, nh, P, hd = heads.shape
+    _need_lens(lens, B)
+    _dtype_code(heads)
+    _need(heads, "heads", (B, nh, P, hd))
+    _need(packed, "packed", (None, nh * hd), heads.dtype)
+    if packed.shape[0] < sum(int(x) for x in lens):
+        raise ValueError(f"packed has {packed.shape[0]} rows, need sum(lens) = {sum(int(x) for x in lens)}")
+    _need_gpu(packed=packed, heads=heads)
+    _need_workspace(workspace)
     _check(lib().ee_transpose_padding_remove_heads(_ptr(heads), _lens(lens), B, P, nh, hd, _dtype_code(heads),
                                                    _ptr(packed), _ptr(workspace),
                                                    workspace.numel() * workspace.element_size(), _stream(stream)),
@@ -357,7 +501,15 @@ def ee_transpose_padding_remove_heads(heads, lens: Sequence[int], packed, worksp
 
 
 def ee_add_bias_residual_layernorm(u, bias, residual, gamma, beta, eps: float, y, stream=None):
+    if u is None or u.dim() != 2:
+        raise ValueError("u must be [rows, hidden]")
     rows, H = u.shape
+    _dtype_code(u)
+    _need(u, "u", (rows, H))
+    for name, t, shp in (("residual", residual, (rows, H)), ("y", y, (rows, H)), ("bias", bias, (H,)),
+                         ("gamma", gamma, (H,)), ("beta", beta, (H,))):
+        _need(t, name, shp, u.dtype)
+    _need_gpu(u=u, bias=bias, residual=residual, gamma=gamma, beta=beta, y=y)
     _check(lib().ee_add_bias_residual_layernorm(_ptr(u), _ptr(bias), _ptr(residual), _ptr(gamma), _ptr(beta), rows, H,
                                                 eps, _dtype_code(u), _ptr(y), _stream(stream)),
            "ee_add_bias_residual_layernorm")
@@ -385,8 +537,21 @@ class Layer:
                "ee_layer_workspace_size")
         return n.value
 
+    def check_io(self, x, lens: Sequence[int], y, workspace):
+        """The checks of forward()'s arguments (also used by ee_stack_forward)."""
+        if x is None or x.dim() != 3:
+            raise ValueError("x must be [batch, pad_len, hidden]")
+        B, P, H = x.shape
+        _need_lens(lens, B)
+        dt = _torch_dtype(self.desc.dtype)
+        _need(x, "x", (B, P, self.desc.hidden), dt)
+        _need(y, "y", (B, P, self.desc.hidden), dt)
+        _need_gpu(x=x, y=y)
+        _need_workspace(workspace)
+        return B, P
+
     def forward(self, x, lens: Sequence[int], y, workspace, stream=None):
-        B, P, _ = x.shape
+        B, P = self.check_io(x, lens, y, workspace)
         _check(lib().ee_layer_forward(self.handle, _ptr(x), _lens(lens), B, P, _ptr(y), _ptr(workspace),
                                       workspace.numel() * workspace.element_size(), _stream(stream)),
                "ee_layer_forward")
@@ -428,6 +593,19 @@ def ee_stack_extend(layers: List[Layer], x, new_len: Sequence[int], ctx_len: Seq
     B = len(new_len)
     if len(ctx_len) != B or len(slot_base) != B:
         raise ValueError("new_len, ctx_len and slot_base must have one entry per sequence")
+    if not layers:
+        raise ValueError("need at least one layer")
+    T = sum(int(n) for n in new_len)
+    dt = _torch_dtype(layers[0].desc.dtype)
+    H = layers[0].desc.hidden
+    _need(x, "x", (T, H), dt)
+    _need(y, "y", (T, H), dt)
+    _need(cache, "cache")
+    need = ee_kv_cache_bytes(layers[0], len(layers), capacity)
+    if cache.numel() * cache.element_size() < need:
+        raise ValueError(f"cache of {cache.numel() * cache.element_size()} bytes, need {need}")
+    _need_gpu(x=x, y=y, cache=cache)
+    _need_workspace(workspace)
     arr = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
     _check(lib().ee_stack_extend(arr, len(layers), _ptr(x), _lens(new_len), _lens(ctx_len), _lens(slot_base), B,
                                  _ptr(cache), int(capacity), _ptr(y), _ptr(workspace),
@@ -435,7 +613,9 @@ def ee_stack_extend(layers: List[Layer], x, new_len: Sequence[int], ctx_len: Seq
 
 
 def ee_stack_forward(layers: List[Layer], x, lens: Sequence[int], y, workspace, stream=None):
-    B, P, _ = x.shape
+    if not layers:
+        raise ValueError("need at least one layer")
+    B, P = layers[0].check_io(x, lens, y, workspace)
     arr = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
     _check(lib().ee_stack_forward(arr, len(layers), _ptr(x), _lens(lens), B, P, _ptr(y), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(stream)), "ee_stack_forward")
@@ -456,7 +636,8 @@ def ee_profile_collect() -> Dict[str, Dict[str, float]]:
     arr = (KernelStat * cap)()
     n = C.c_int32(0)
     _check(lib().ee_profile_collect(arr, cap, C.byref(n)), "ee_profile_collect")
-    return {arr[i].name.decode(): {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms)}
+    return {arr[i].name.decode(): {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms),
+                                   "flops": float(arr[i].flops), "kernel": arr[i].kernel.decode()}
             for i in range(n.value)}
 
 

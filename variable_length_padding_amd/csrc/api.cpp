@@ -110,7 +110,13 @@ struct Profiler {
   std::string only;  // the one site timed, or empty for every site
   std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
   size_t used = 0;
-  std::vector<std::pair<std::string, size_t>> recs;  // (site, pool index)
+  struct Rec {
+    std::string site;
+    size_t event;        // pool index
+    double flops;        // algorithmic flops of the launch (GEMMs; 0 elsewhere)
+    const char* kernel;  // static label of the kernel launched, or nullptr
+  };
+  std::vector<Rec> recs;
 };
 Profiler& prof() {
   static Profiler* p = new Profiler();  // never destroyed: events may outlive static teardown order
@@ -118,9 +124,10 @@ Profiler& prof() {
 }
 
 // Runs `launch` (which returns the launch's hipError_t); while profiling is on,
-// brackets it with two events recorded on `s`.
+// brackets it with two events recorded on `s`.  `flops` and `kernel` are
+// recorded with the launch.
 template <class F>
-hipError_t timed(const char* site, hipStream_t s, F&& launch) {
+hipError_t timed(const char* site, hipStream_t s, F&& launch, double flops = 0.0, const char* kernel = nullptr) {
   Profiler& p = prof();
   if (!p.on) return launch();
   std::lock_guard<std::mutex> lk(p.mu);
@@ -141,7 +148,7 @@ hipError_t timed(const char* site, hipStream_t s, F&& launch) {
   if (r != hipSuccess) return r;
   r = hipEventRecord(p.pool[i].second, s);
   if (r != hipSuccess) return r;
-  p.recs.emplace_back(site, i);
+  p.recs.push_back(Profiler::Rec{site, i, flops, kernel});
   return hipSuccess;
 }
 
@@ -260,21 +267,51 @@ Plan plan_layer(const ee_layer_desc& d, int32_t B, int32_t P, int64_t T) {
 char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 
 // ---------------------------------------------------------------- launch helpers
-hipError_t gemm(ee_dtype dt, const void* A, const void* W, const void* bias, const void* R, int64_t M, int N, int K,
-                const GemmPitch& ld, ee_epilogue epi, ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr,
-                size_t scratch_bytes = 0) {
+// One GEMM launch site.  With a scratch buffer (extend steps), small-M
+// problems run stream-K or split-K (two kernels, timed as one launch of
+// `site`).  The dense fp16 path runs as one or two parts (gemm_f16_parts):
+// the first is timed as `site`, a remainder of rows as `rest_site`.  Each
+// launch records its algorithmic flops, 2*rows*N*K.
+ee_status gemm_site(const char* site, const char* rest_site, ee_dtype dt, const void* A, const void* W,
+                    const void* bias, const void* R, int64_t M, int N, int K, const GemmPitch& ld, ee_epilogue epi,
+                    ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr, size_t scratch_bytes = 0) {
+  const double flops = 2.0 * (double)M * N * K;
   if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K, ld, A, W)) {
     if (scratch) {
       const StreamKPlan sk = gemm_f16_streamk_plan(M, N, K, ld);
-      if (sk.workgroups > 0 && sk.scratch_bytes <= scratch_bytes)
-        return launch_gemm_f16_streamk(sk, A, W, bias, R, M, N, ld, epi, g, C, scratch, s);
+      if (sk.workgroups > 0 && sk.scratch_bytes <= scratch_bytes) {
+        const hipError_t e = timed(
+            site, s, [&]() { return launch_gemm_f16_streamk(sk, A, W, bias, R, M, N, ld, epi, g, C, scratch, s); },
+            flops, "gemm_streamk_kernel + streamk_reduce_kernel");
+        return e == hipSuccess ? EE_OK : hip_fail(e, site);
+      }
     }
     const int splits = scratch && M <= kSplitkMaxRows ? gemm_f16_splitk_choice(M, N, K, scratch_bytes) : 1;
-    if (splits > 1) return launch_gemm_f16_splitk(A, W, bias, R, M, N, K, ld, epi, g, C, splits, scratch, s);
-    return launch_gemm_f16_mfma(A, W, bias, R, M, N, K, ld, epi, g, C, s);
+    if (splits > 1) {
+      const hipError_t e = timed(
+          site, s, [&]() { return launch_gemm_f16_splitk(A, W, bias, R, M, N, K, ld, epi, g, C, splits, scratch, s); },
+          flops, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 4, 2> + splitk_reduce_kernel");
+      return e == hipSuccess ? EE_OK : hip_fail(e, site);
+    }
+    GemmPart parts[2];
+    const int n = gemm_f16_parts(M, N, K, parts);
+    for (int i = 0; i < n; ++i) {
+      const char* at_site = i == 0 ? site : rest_site;
+      const hipError_t e = timed(
+          at_site, s, [&]() { return launch_gemm_f16_part(parts[i], A, W, bias, R, N, K, ld, epi, g, C, s); },
+          2.0 * (double)parts[i].rows * N * K, gemm_f16_kernel_label(parts[i].cfg, epi));
+      if (e != hipSuccess) return hip_fail(e, at_site);
+    }
+    return EE_OK;
   }
-  return launch_gemm_valu(dt, A, W, bias, R, M, N, K, ld, epi, g, C, s);
+  const hipError_t e = timed(
+      site, s, [&]() { return launch_gemm_valu(dt, A, W, bias, R, M, N, K, ld, epi, g, C, s); }, flops,
+      "gemm_valu_kernel");
+  return e == hipSuccess ? EE_OK : hip_fail(e, site);
 }
+
+// A GEMM launch site `site`; a second part of its rows is timed as site "_rest".
+#define EE_GEMM(site, ...) EE_TRY(gemm_site(site, site "_rest", __VA_ARGS__))
 
 GemmPitch dense(int N, int K) { return GemmPitch{K, K, N}; }
 
@@ -324,40 +361,40 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, hi
   const GemmPitch ld_fc1{H, (int)w.ld_fc1, L->ld_big}, ld_fc2{L->ld_big, (int)w.ld_fc2, H};
   auto fc1 = [&](const void* in) -> ee_status {
     if (d.fuse_gelu) {
-      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, ld_fc1, EE_EPI_BIAS_GELU, d.gelu, big, s, sk, skb));
+      EE_GEMM("gemm_fc1", d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, ld_fc1, EE_EPI_BIAS_GELU, d.gelu, big, s, sk, skb);
     } else {
-      EE_LAUNCH("gemm_fc1", s, gemm(d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, ld_fc1, EE_EPI_NONE, d.gelu, big, s, sk, skb));
+      EE_GEMM("gemm_fc1", d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, ld_fc1, EE_EPI_NONE, d.gelu, big, s, sk, skb);
       EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, L->ld_big, d.gelu, big, s));
     }
     return EE_OK;
   };
   if (d.block == EE_BLOCK_GPT_PRELN) {
     EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
-    EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
+    EE_GEMM("gemm_qkv", d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb);
     EE_TRY(attn(big, o, true));
     if (residual_pass(d)) {
       // h = (o W_out^T + b_out) + x and ln = LN2(h); x = (g W_fc2^T + b_fc2) + h
-      EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, nullptr, T, H, Hp, ld_out, EE_EPI_BIAS, d.gelu, h, s, sk, skb));
+      EE_GEMM("gemm_out", d.dtype, o, w.w_out, w.b_out, nullptr, T, H, Hp, ld_out, EE_EPI_BIAS, d.gelu, h, s, sk, skb);
       EE_LAUNCH("res_ln2", s, launch_residual_add_layernorm(d.dtype, h, x, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
       EE_TRY(fc1(ln));
-      EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, nullptr, T, H, F, ld_fc2, EE_EPI_BIAS, d.gelu, x, s, sk, skb));
+      EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, w.b_fc2, nullptr, T, H, F, ld_fc2, EE_EPI_BIAS, d.gelu, x, s, sk, skb);
       EE_LAUNCH("res_add", s, launch_residual_add_layernorm(d.dtype, x, h, x, nullptr, nullptr, T, H, 0.f, nullptr, s));
       return EE_OK;
     }
-    EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, ld_out, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb));
+    EE_GEMM("gemm_out", d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, ld_out, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb);
     EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
     EE_TRY(fc1(ln));
-    EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, ld_fc2, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s, sk, skb));
+    EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, ld_fc2, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s, sk, skb);
     return EE_OK;
   }
   // post-LN encoder: GEMM, then bias + residual + LayerNorm in one pass
-  EE_LAUNCH("gemm_qkv", s, gemm(d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb));
+  EE_GEMM("gemm_qkv", d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb);
   EE_TRY(attn(big, o, false));
-  EE_LAUNCH("gemm_out", s, gemm(d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, ld_out, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
+  EE_GEMM("gemm_out", d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, ld_out, EE_EPI_NONE, d.gelu, ln, s, sk, skb);
   EE_LAUNCH("add_ln1", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_out, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, h, s));
   EE_TRY(fc1(h));
-  EE_LAUNCH("gemm_fc2", s, gemm(d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, ld_fc2, EE_EPI_NONE, d.gelu, ln, s, sk, skb));
+  EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, ld_fc2, EE_EPI_NONE, d.gelu, ln, s, sk, skb);
   EE_LAUNCH("add_ln2", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_fc2, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, x, s));
   return EE_OK;
@@ -775,7 +812,7 @@ static ee_status linear_strided(const void* A, int64_t lda, const void* W, int64
     return fail(EE_ERR_INVALID_ARG, "C overlaps an input");
   hipStream_t st = static_cast<hipStream_t>(stream);
   const GemmPitch ld{(int)lda, (int)ldw, (int)ldc};
-  EE_LAUNCH("linear", st, gemm(dtype, A, W, bias, residual, M, N, K, ld, epi, gelu, C, st));
+  EE_GEMM("linear", dtype, A, W, bias, residual, M, N, K, ld, epi, gelu, C, st);
   return EE_OK;
 }
 
@@ -1030,10 +1067,16 @@ ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* cou
   if (!count || (capacity > 0 && !out)) return fail(EE_ERR_INVALID_ARG, "out/count must be non-NULL");
   Profiler& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
+  struct Agg {
+    int64_t launches = 0;
+    double ms = 0.0, flops = 0.0;
+    const char* kernel = nullptr;
+    bool several = false;
+  };
   std::vector<std::string> order;
-  std::map<std::string, std::pair<int64_t, double>> agg;
+  std::map<std::string, Agg> agg;
   for (const auto& r : p.recs) {
-    const auto& ev = p.pool[r.second];
+    const auto& ev = p.pool[r.event];
     hipError_t e = hipEventSynchronize(ev.second);
     float ms = 0.f;
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, ev.first, ev.second);
@@ -1042,19 +1085,30 @@ ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* cou
       p.used = 0;
       return hip_fail(e, "profile event");
     }
-    if (!agg.count(r.first)) order.push_back(r.first);
-    auto& a = agg[r.first];
-    a.first += 1;
-    a.second += ms;
+    if (!agg.count(r.site)) order.push_back(r.site);
+    Agg& a = agg[r.site];
+    a.launches += 1;
+    a.ms += ms;
+    a.flops += r.flops;
+    if (r.kernel) {
+      if (a.kernel && std::strcmp(a.kernel, r.kernel) != 0) a.several = true;
+      if (!a.kernel) a.kernel = r.kernel;
+    }
   }
   int32_t n = 0;
   for (const auto& name : order) {
     if (n < capacity) {
       ee_kernel_stat& k = out[n];
+      const Agg& a = agg[name];
       std::memset(&k, 0, sizeof k);
       std::strncpy(k.name, name.c_str(), sizeof k.name - 1);
-      k.launches = agg[name].first;
-      k.total_ms = agg[name].second;
+      k.launches = a.launches;
+      k.total_ms = a.ms;
+      k.flops = a.flops;
+      if (a.several)
+        std::strncpy(k.kernel, "several kernels", sizeof k.kernel - 1);
+      else if (a.kernel)
+        std::strncpy(k.kernel, a.kernel, sizeof k.kernel - 1);
     }
     ++n;
   }

@@ -23,6 +23,7 @@
 //
 // Any other case (fp32, head_dim 16): a vector-ALU kernel, one query per lane.
 #include "device_common.h"
+#include "attention_limits.h"
 #include "internal.h"
 #include "lds_dma.h"
 
@@ -30,7 +31,7 @@ namespace ee {
 namespace {
 
 constexpr int kQB = 128;  // queries per workgroup (MFMA kernel)
-constexpr int kKB = 32;   // keys per LDS tile
+constexpr int kKB = kAttnKeyTile;   // keys per LDS tile
 constexpr int kVtPitch = kKB + 4;  // halves per transposed-V row: 72 B, 8-byte aligned, conflict-free b64 reads
 
 // Where the rows of q, k, v and o live.  Row `row` of (sequence b, head h) of
@@ -451,8 +452,10 @@ template <bool CAUSAL>
 void launch_mfma(const AttnAddr& ad, const int32_t* cu, int B, int max_len, int nh, int hd, hipStream_t s) {
   const dim3 grid((unsigned)((max_len + kQB - 1) / kQB), (unsigned)B, (unsigned)nh), block(256);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);  // log2(e) / sqrt(hd)
-  // the transposing-read kernel addresses a sequence's rows with 32-bit byte offsets
-  if ((hd == 64 || hd == 128) && (int64_t)max_len * ad.in_row_stride * 2 < (int64_t(1) << 31)) {
+  // the transposing-read kernel addresses a sequence's rows with 32-bit byte
+  // offsets, up to row k0 + kKB - 1 of the last key tile (past the sequence's
+  // end: those loads fall outside the descriptor's range and read zeros)
+  if ((hd == 64 || hd == 128) && attn_tr_offsets_fit(max_len, ad.in_row_stride)) {
     if (hd == 64) hipLaunchKernelGGL((attn_tr_kernel<64, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
     else hipLaunchKernelGGL((attn_tr_kernel<128, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
     return;

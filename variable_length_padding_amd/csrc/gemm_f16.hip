@@ -594,34 +594,74 @@ int64_t gemm_big_rows(int64_t M, int N, int cus) {
   return t_split < t_plain ? m_tiles * 256 : M;
 }
 
+int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[2]) {
+  if (M <= 0) return 0;
+  const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
+  if (tiles_big < 256) {
+    parts[0] = GemmPart{0, M, kGemm128x128};
+    return 1;
+  }
+  const int cus = device_cu_count();
+  const int64_t m_big = gemm_big_rows(M, N, cus);
+  parts[0] = GemmPart{0, m_big, K >= EE_GEMM_DEEP_W_K ? kGemmBig3 : kGemmBig2};
+  if (m_big == M) return 1;
+  // Few remaining rows stream all of W through few tiles: 128 x 64 tiles
+  // (the same MFMA shape) put twice as many CUs on it.
+  const int64_t rest = M - m_big;
+  const bool narrow = ((rest + 127) / 128) * ((N + 127) / 128) * 2 <= cus;
+  parts[1] = GemmPart{m_big, rest, narrow ? kGemm128x64 : kGemm128x128};
+  return 2;
+}
+
+hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W, const void* bias, const void* R,
+                                int N, int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C,
+                                hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  // the part's rows of A, C and the residual
+  const f16* a = static_cast<const f16*>(A) + p.row0 * ld.a;
+  const f16* r = R ? static_cast<const f16*>(R) + p.row0 * ld.c : nullptr;
+  f16* c = static_cast<f16*>(C) + p.row0 * ld.c;
+  const int M = (int)p.rows;
+  const int wgs = EE_GEMM_PERSIST ? device_cu_count() : 0;
+  switch (p.cfg) {
+    case kGemmBig2:
+      return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1,
+                                                                          nullptr, s, wgs);
+    case kGemmBig3:
+      return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(a, W, bias, r, M, N, K, ld, epi, form, c, 1,
+                                                                          nullptr, s, wgs);
+    case kGemm128x64: return launch_cfg<32, 128, 64, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
+    case kGemm128x128: return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi) {
+  // gemm_f16_mfma_kernel's template arguments <MF, BM, BN, WGM, WGN, EPI, WDEPTH>
+  static const char* const labels[4][4] = {
+#define EE_L(cfg) {"gemm_f16_mfma_kernel<" cfg ", 0, 2>", "gemm_f16_mfma_kernel<" cfg ", 1, 2>", \
+                   "gemm_f16_mfma_kernel<" cfg ", 2, 2>", "gemm_f16_mfma_kernel<" cfg ", 3, 2>"}
+      EE_L("16, 256, 256, 2, 2"),
+      {"gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 0, 3>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 1, 3>",
+       "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 3>"},
+      EE_L("32, 128, 128, 2, 2"),
+      EE_L("32, 128, 64, 2, 2"),
+#undef EE_L
+  };
+  const int e = (int)epi;
+  if (cfg < 0 || cfg > 3 || e < 0 || e > 3) return "gemm_f16_mfma_kernel";
+  return labels[cfg][e];
+}
+
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
                                 int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
-  if (M <= 0) return hipSuccess;
-  const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles_big >= 256) {
-    const int cus = device_cu_count();
-    const int wgs = EE_GEMM_PERSIST ? cus : 0;
-    const int64_t m_big = gemm_big_rows(M, N, cus);
-    hipError_t e;
-    if (K >= EE_GEMM_DEEP_W_K)
-      e = launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(A, W, bias, R, (int)m_big, N, K, ld, epi, form,
-                                                                        C, 1, nullptr, s, wgs);
-    else
-      e = launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 2>(A, W, bias, R, (int)m_big, N, K, ld, epi, form,
-                                                                        C, 1, nullptr, s, wgs);
-    if (e != hipSuccess || m_big == M) return e;
-    // the remaining rows: A, C and the residual from row m_big on
-    const f16* a = static_cast<const f16*>(A) + m_big * ld.a;
-    const f16* r = R ? static_cast<const f16*>(R) + m_big * ld.c : nullptr;
-    f16* c = static_cast<f16*>(C) + m_big * ld.c;
-    const int64_t rest = M - m_big;
-    // Few remaining rows stream all of W through few tiles: 128 x 64 tiles
-    // (the same MFMA shape) put twice as many CUs on it.
-    if (((rest + 127) / 128) * ((N + 127) / 128) * 2 <= cus)
-      return launch_cfg<32, 128, 64, 2, 2>(a, W, bias, r, (int)rest, N, K, ld, epi, form, c, 1, nullptr, s);
-    return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, (int)rest, N, K, ld, epi, form, c, 1, nullptr, s);
+  GemmPart parts[2];
+  const int n = gemm_f16_parts(M, N, K, parts);
+  for (int i = 0; i < n; ++i) {
+    const hipError_t e = launch_gemm_f16_part(parts[i], A, W, bias, R, N, K, ld, epi, form, C, s);
+    if (e != hipSuccess) return e;
   }
-  return launch_cfg<32, 128, 128, 2, 2>(A, W, bias, R, (int)M, N, K, ld, epi, form, C, 1, nullptr, s);
+  return hipSuccess;
 }
 
 // Measured at M = 32 on the GPT-3 decode shapes (weights streamed once): four
