@@ -416,6 +416,29 @@ EE_API ee_status ee_stack_extend(ee_layer* const* layers, int32_t n_layers, cons
                                  int32_t batch, void* d_cache, int64_t capacity, void* d_y, void* ws,
                                  size_t ws_bytes, void* stream);
 
+/* ---- Extend step that allocates nothing ----
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops and harnesses that forbid hipMalloc.  The same step
+ * as ee_stack_extend (same arguments, kernels and results), with the
+ * workspace in a static device buffer of EE_NOALLOC_SCRATCH_BYTES that the
+ * library owns; the caller passes inputs, outputs and the cache only.  Each
+ * GPU the call runs on holds its own copy of the buffer until the process
+ * ends.  Every call on a GPU shares that GPU's buffer, so calls that overlap
+ * in time on one GPU (from two streams or threads) race; serialise them.
+ * A step whose workspace (ee_extend_workspace_size(layers[0], batch, T_new))
+ * exceeds the buffer returns EE_ERR_WORKSPACE before any device work: at
+ * GPT-3 width (H 12288, F 49152, 96 x 128 heads, fp16) that is about 340 new
+ * tokens; decode steps of up to EE_MAX_EXTEND_BATCH sequences fit.  Other
+ * errors as ee_stack_extend, plus EE_ERR_HIP if the buffer's device address
+ * cannot be obtained.  No hipMalloc, hipFree or allocating library routine is
+ * called; the step copies its new-token rows in and out with two
+ * device-to-device copies on `stream`, as ee_stack_extend does. */
+#define EE_NOALLOC_SCRATCH_BYTES (128u << 20)
+EE_API ee_status ee_stack_extend_noalloc(ee_layer* const* layers, int32_t n_layers, const void* d_x,
+                                         const int32_t* new_len, const int32_t* ctx_len, const int32_t* slot_base,
+                                         int32_t batch, void* d_cache, int64_t capacity, void* d_y, void* stream);
+
 /* ---- Batch planning over a request queue (host only; no device work) ----
  *
  * The announcement article's "Serving" section and the README's "Batching"

@@ -191,6 +191,31 @@ def test_extend_validation_happens_before_device_work():
         lib.ee_layer_destroy(h)
 
 
+def test_extend_noalloc_rejects_before_device_work():
+    """The no-allocation extend step's own checks (sizes that do not fit its
+    static buffer among them) run on the host before any HIP call."""
+    lib = ee.lib()
+    st, h = _create(_desc(), _weights())
+    assert st == 0
+    try:
+        arr = (C.c_void_p * 1)(h.value)
+
+        def I(*v):
+            return (C.c_int32 * len(v))(*v)
+        x, y, cache = 1 << 30, 1 << 31, 1 << 33
+        assert lib.ee_stack_extend_noalloc(None, 1, x, I(1), I(0), I(0), 1, cache, 8, y, None) == 1
+        assert lib.ee_stack_extend_noalloc(arr, 0, x, I(1), I(0), I(0), 1, cache, 8, y, None) == 1
+        assert lib.ee_stack_extend_noalloc(arr, 1, x, I(1), I(0), I(0), 0, cache, 8, y, None) == 1
+        assert lib.ee_stack_extend_noalloc(arr, 1, x, I(-1, 2), I(0, 0), I(0, 4), 2, cache, 8, y, None) == 1
+        n = C.c_size_t(0)
+        T = 2_000_000                      # a workspace of several GB: above the static buffer
+        assert lib.ee_extend_workspace_size(h, 1, T, C.byref(n)) == 0 and n.value > ee.NOALLOC_SCRATCH_BYTES
+        assert lib.ee_stack_extend_noalloc(arr, 1, x, I(T), I(0), I(0), 1, cache, T, y, None) == 3
+        assert b"no-allocation" in lib.ee_last_error()
+    finally:
+        lib.ee_layer_destroy(h)
+
+
 def test_preferred_row_pitch():
     lib = ee.lib()
     # a row that is a multiple of 32 KiB gets 128 bytes more; others stay dense

@@ -22,6 +22,7 @@ __all__ = [
     "BLOCK_GPT_PRELN", "BLOCK_BERT_POSTLN", "ATTN_VARLEN", "ATTN_PADDED",
     "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_filter", "ee_profile_collect",
     "ee_kv_cache_bytes", "ee_extend_workspace_size", "ee_extend_max_positions", "ee_stack_extend",
+    "ee_stack_extend_noalloc", "NOALLOC_SCRATCH_BYTES",
     "MAX_EXTEND_BATCH",
     "BatchCost", "ee_batch_cost_eval", "ee_plan_fifo", "ee_plan_dynamic", "batches_of",
     "EXPORTED_SYMBOLS", "lib_path",
@@ -138,6 +139,8 @@ _SIGS = {
     "ee_extend_max_positions": (C.c_int32, []),
     "ee_stack_extend": (C.c_int, [C.POINTER(_VP), _I32, _VP, _PI32, _PI32, _PI32, _I32, _VP, _I64, _VP, _VP, _SZ,
                                   _VP]),
+    "ee_stack_extend_noalloc": (C.c_int, [C.POINTER(_VP), _I32, _VP, _PI32, _PI32, _PI32, _I32, _VP, _I64, _VP,
+                                          _VP]),
     "ee_batch_cost_eval": (C.c_int, [_PI32, _I32, C.POINTER(BatchCost), C.POINTER(C.c_double)]),
     "ee_plan_fifo": (C.c_int, [_PI32, _I32, _I32, _PI32, _PI32]),
     "ee_plan_dynamic": (C.c_int, [_PI32, C.POINTER(C.c_double), _I32, _I32, _I64, C.POINTER(BatchCost), _PI32,
@@ -610,6 +613,34 @@ def ee_stack_extend(layers: List[Layer], x, new_len: Sequence[int], ctx_len: Seq
     _check(lib().ee_stack_extend(arr, len(layers), _ptr(x), _lens(new_len), _lens(ctx_len), _lens(slot_base), B,
                                  _ptr(cache), int(capacity), _ptr(y), _ptr(workspace),
                                  workspace.numel() * workspace.element_size(), _stream(stream)), "ee_stack_extend")
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def ee_stack_extend_noalloc(layers: List[Layer], x, new_len: Sequence[int], ctx_len: Sequence[int],
+                            slot_base: Sequence[int], cache, capacity: int, y, stream=None):
+    """ee_stack_extend without a workspace argument: the library's static
+    scratch buffer (NOALLOC_SCRATCH_BYTES per GPU) serves as the workspace."""
+    B = len(new_len)
+    if len(ctx_len) != B or len(slot_base) != B:
+        raise ValueError("new_len, ctx_len and slot_base must have one entry per sequence")
+    if not layers:
+        raise ValueError("need at least one layer")
+    T = sum(int(n) for n in new_len)
+    dt = _torch_dtype(layers[0].desc.dtype)
+    H = layers[0].desc.hidden
+    _need(x, "x", (T, H), dt)
+    _need(y, "y", (T, H), dt)
+    _need(cache, "cache")
+    need = ee_kv_cache_bytes(layers[0], len(layers), capacity)
+    if cache.numel() * cache.element_size() < need:
+        raise ValueError(f"cache of {cache.numel() * cache.element_size()} bytes, need {need}")
+    _need_gpu(x=x, y=y, cache=cache)
+    arr = (C.c_void_p * len(layers))(*[l.handle.value for l in layers])
+    _check(lib().ee_stack_extend_noalloc(arr, len(layers), _ptr(x), _lens(new_len), _lens(ctx_len), _lens(slot_base),
+                                         B, _ptr(cache), int(capacity), _ptr(y), _stream(stream)),
+           "ee_stack_extend_noalloc")
 
 
 def ee_stack_forward(layers: List[Layer], x, lens: Sequence[int], y, workspace, stream=None):

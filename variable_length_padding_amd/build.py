@@ -37,7 +37,7 @@ LIB = os.path.join(PKG, "libee.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "batching.cpp", "offsets.hip", "padding.hip", "layernorm.hip", "bias_gelu.hip",
-           "gemm_f16.hip", "gemm_streamk.hip", "gemm_valu.hip", "attention.hip", "decode.hip"]
+           "gemm_f16.hip", "gemm_streamk.hip", "gemm_valu.hip", "attention.hip", "decode.hip", "noalloc.hip"]
 
 # -packed-fp32-ops: keep the compiler from forming v_pk_*_f32 instructions.
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-result",

@@ -566,6 +566,13 @@ ee_status extend_impl(ee_layer* const* layers, int32_t n_layers, const void* d_x
 
 }  // namespace
 
+ee_status ee::stack_extend_into(ee_layer* const* layers, int32_t n_layers, const void* d_x, const int32_t* new_len,
+                                const int32_t* ctx_len, const int32_t* slot_base, int32_t batch, void* d_cache,
+                                int64_t capacity, void* d_y, void* ws, size_t ws_bytes, void* stream) {
+  return extend_impl(layers, n_layers, d_x, new_len, ctx_len, slot_base, batch, d_cache, capacity, d_y, ws, ws_bytes,
+                     stream);
+}
+
 // ======================================================================= ABI
 extern "C" {
 

@@ -19,6 +19,12 @@ struct LensArg {
 // Records `msg` as the calling thread's last error (ee_last_error) and returns s.
 ee_status set_error(ee_status s, const char* msg);
 
+// ee_stack_extend with an explicit workspace (api.cpp); the no-allocation
+// entry point passes its static scratch buffer.
+ee_status stack_extend_into(ee_layer* const* layers, int32_t n_layers, const void* d_x, const int32_t* new_len,
+                            const int32_t* ctx_len, const int32_t* slot_base, int32_t batch, void* d_cache,
+                            int64_t capacity, void* d_y, void* ws, size_t ws_bytes, void* stream);
+
 // ---- offsets.hip ----
 hipError_t launch_offsets(const LensArg& lens, int B, int P, int32_t* cu, int32_t* token_src,
                           int32_t* pad2pack, hipStream_t s);
