@@ -14,9 +14,10 @@ W untimed steps, then K timed ones.  Inputs and weights are resident in HBM
 before the timed region.  Prints one JSON line.
 
 Metric: valid tokens/s per layer = sum over the timed steps of T_batch * L /
-their summed time ("value").  "stream" gives the same rate over one pass of
-all 16 batches; "batching" the dynamic plan over the same requests (planned
-on a table of batch times measured at the start of the run), beside FIFO.
+their summed time ("value").  When the timed steps cover all 16 batches,
+"stream" gives the rate of the first pass over them, and "batching" runs the
+dynamic plan over the same requests (planned on a table of batch times
+measured in the run) beside FIFO; else both are null.
 
 roofline: the FC1 GEMM kernel (bias + GeLU epilogue, the largest single
 contraction; the GEMMs together take ~97% of a step): the algorithmic flops
@@ -62,8 +63,8 @@ DEFAULT_WORKLOAD = "gpt3-48l-stream"
 def _parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=16)
+    ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--seed", type=int, default=1234)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -409,16 +410,14 @@ def _stream_bench(args):
         return (sum(rows_b[j] for j in order2) if args.no_pack else T2) / K2
     kernels = _kernel_table(w, stats, K2, sum(ms2), rows_of_site, cap, sum(xs[j].shape[1] for j in order2) / K2,
                             _attention_flops(w, lens2) * L, True)
-    # the whole stream once (FIFO), from the timed steps when they covered it
-    if K >= nb:
-        stream_ms = sum(ms[:nb])
-    else:
-        stream_ms = sum(_timed_steps(ee, stream, [step(i) for i in range(nb)], "")[0])
-    stream_rate = T_all * L / (stream_ms / 1e3)
-    _log(f"whole stream, FIFO: {nb} batches, {stream_ms / 1e3:.2f} s, {stream_rate:.0f} valid tokens/s per layer")
+    # the whole stream once (FIFO): the first nb timed steps, when they cover it
+    stream_ms = sum(ms[:nb]) if K >= nb else None
+    if stream_ms is not None:
+        stream_rate = T_all * L / (stream_ms / 1e3)
+        _log(f"whole stream, FIFO: {nb} batches, {stream_ms / 1e3:.2f} s, {stream_rate:.0f} valid tokens/s per layer")
 
     batching = None
-    if not args.no_dynamic:
+    if not args.no_dynamic and stream_ms is not None:
         batching = _dynamic_vs_fifo(args, w, ee, torch, dev, stream, run, make_batches, lens, cap, P_max, T_all, L,
                                     stream_ms / 1e3, sum(rows_b))
     roofline = _roofline(w.name, st_fc1[ROOFLINE_SITE])
@@ -440,8 +439,9 @@ def _stream_bench(args):
                    "batching": "fifo", "step": "one FIFO batch through all layers, cycling the batches",
                    "timed_valid_tokens": tok_timed, "padding_removed": not args.no_pack,
                    "weight_rows": "dense" if args.dense_weights else "preferred pitch"},
-        "stream": {"batches": nb, "seconds": round(stream_ms / 1e3, 3), "value": round(stream_rate, 1),
-                   "padded_rows": sum(rows_b), "padded_ratio": round(sum(rows_b) / T_all, 4)},
+        "stream": None if stream_ms is None else {
+            "batches": nb, "seconds": round(stream_ms / 1e3, 3), "value": round(stream_rate, 1),
+            "padded_rows": sum(rows_b), "padded_ratio": round(sum(rows_b) / T_all, 4)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "batching": batching,

@@ -29,10 +29,10 @@
 //     chunk c ^ f(r), f(r) = ((r >> 1) & 7) ^ ((r & 1) << 2), so the 16 rows
 //     read by a quarter-wave land on distinct banks whether the LDS serves
 //     8 or 16 lanes of a 128-bit read per cycle.
-//   * Tile order: the hardware deals consecutive workgroup ids round-robin to
-//     the 8 XCDs, so ids are remapped to give each XCD a contiguous range, and
-//     that range walks tiles in groups of 4 M-tiles, so the workgroups that
-//     share an XCD's L2 share A and W panels.
+//   * Tile order (gemm_tile_order.h): the hardware deals consecutive workgroup
+//     ids round-robin to the 8 XCDs; each XCD walks its share of the tiles in
+//     groups of 4 M-tiles, so the workgroups that share an XCD's L2 share A and
+//     W panels, and pairs of XCDs split the N range of the same groups.
 //   * A 256 x 256 tile count just past a multiple of the CU count runs whole
 //     rounds of 256-row tiles and the remaining rows as 128 x 128 tiles (a
 //     second launch), when that is estimated to end sooner (gemm_big_rows).
@@ -50,6 +50,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "gemm_tile_order.h"
 #include "internal.h"
 #include "lds_dma.h"
 
@@ -81,23 +82,6 @@ constexpr int kBK = 64;
 constexpr int kEpiPartial = 4;
 template <int EPI>
 constexpr bool kHasBias = EPI == EE_EPI_BIAS || EPI == EE_EPI_BIAS_RESIDUAL || EPI == EE_EPI_BIAS_GELU;
-
-// Tile origin of this workgroup: XCD-contiguous ranges of workgroup ids,
-// walked in groups of 4 M-tiles (see the file comment).
-template <int BM, int BN>
-__device__ __forceinline__ void tile_origin(int tile, int n_tiles, int tiles_m, int tiles_n, int& m0, int& n0) {
-  int bid = tile;
-  const int nblk = n_tiles;
-  if ((nblk & 7) == 0) bid = (bid & 7) * (nblk >> 3) + (bid >> 3);
-  constexpr int GM = 4;
-  const int per_group = GM * tiles_n;
-  const int group = bid / per_group;
-  const int first_m = group * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int ig = bid - group * per_group;
-  m0 = (first_m + ig % gm) * BM;
-  n0 = (ig / gm) * BN;
-}
 
 // Fragment geometry of the two MFMA shapes used here.  Element e of lane l
 // of a fragment sits at (row(l, e), col(l)) of its MF x MF block:
@@ -287,7 +271,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   __amdgpu_buffer_rsrc_t arsrc, wrsrc;
   int m0 = 0, n0 = 0;
   auto set_tile = [&](int tile) {
-    tile_origin<BM, BN>(tile, n_tiles, tiles_m, tiles_n, m0, n0);
+    gemm_tile_origin(tile, n_tiles, tiles_m, tiles_n, BM, BN, m0, n0);
     arsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(A + (int64_t)m0 * lda), (short)0, min(BM, M - m0) * lda * 2,
                                               kBufferFlags);
     wrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)n0 * ldw), (short)0, min(BN, N - n0) * ldw * 2,
