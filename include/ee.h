@@ -403,10 +403,15 @@ EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32
  * range outside [0, capacity), overlapping slot ranges of sequences with
  * tokens, overlapping buffers, or a post-LN descriptor; EE_ERR_UNSUPPORTED
  * for head_dim outside {16, 32, 64, 128} or more than
- * ee_extend_max_positions() positions in one sequence; EE_ERR_WORKSPACE
- * when ws_bytes < ee_extend_workspace_size(layer, batch, T_new).  A size
- * taken for some T_new covers every step with fewer new tokens; fp16 sizes
- * include 64 MiB for the split-K partial sums of small steps. */
+ * ee_extend_max_positions() (2^31 - 1) positions in one sequence;
+ * EE_ERR_WORKSPACE when ws_bytes < ee_extend_workspace_size(layer, batch,
+ * T_new).  A size taken for some T_new covers every step with fewer new
+ * tokens; every size includes 64 MiB for partial sums: the small-M GEMMs'
+ * split-K / stream-K pieces, and the attention's per-key-chunk softmax
+ * states.  The attention over the cache splits each new token's keys into
+ * chunks (512 positions, doubled until the chunks' states fit the 64 MiB)
+ * and merges the chunks' softmax states in a second kernel, so no buffer
+ * grows with the context. */
 EE_API ee_status ee_kv_cache_bytes(const ee_layer* layer, int32_t n_layers, int64_t capacity, size_t* bytes);
 EE_API ee_status ee_extend_workspace_size(const ee_layer* layer, int32_t batch, int64_t max_new_tokens,
                                           size_t* bytes);

@@ -6,9 +6,10 @@
 - One extend step at the largest batch (EE_MAX_EXTEND_BATCH = 256 sequences):
   a prefill of ragged prompts, then a decode step with a token for every
   sequence, checked step by step.
-- A decode step whose sequence reaches the cache attention's position limit
-  (ee_extend_max_positions), after a GPU prefill of that length; one more
-  position is rejected on the host.
+- Extend steps over long contexts after a GPU prefill: past 32768 positions
+  (GPT-2-small width, 79 key chunks merged by the second kernel; a decode
+  step, then a mixed step of several new tokens) and 2000 positions at GPT-3
+  width (96 heads of 128).
 - Causal attention at GPT-3 width (96 heads of 128) over a sequence whose
   QKV rows span more than 2^31 bytes, then one that starts past that point:
   sampled queries and heads against the oracle's single-query form.
@@ -104,42 +105,44 @@ def test_attention_rows_past_2gib():
     assert err <= 3e-3
 
 
-def test_decode_at_max_positions():
-    """gpt2-small, one layer: a prompt of ee_extend_max_positions() - 1 tokens
-    and a short one, prefilled on the GPU, then a decode step that brings the
-    first sequence to the limit.  The oracle's cache of the long prompt is its
+@pytest.mark.parametrize("name,prompts,steps", [
+    ("gpt2-small", [40000, 5], [[1, 1], [3, 2]]),     # past 32768 positions: 79 key chunks, then a mixed step
+    ("gpt3-12l", [2000, 1, 700], [[1, 1, 1]]),         # GPT-3 width (96 heads of 128): 4 key chunks
+])
+def test_decode_long_context(name, prompts, steps):
+    """One layer: long prompts prefilled on the GPU, then extend steps over the
+    long cache.  The cache attention splits the keys into chunks whose softmax
+    states a second kernel merges.  The oracle's cache of a long prompt is its
     first layer's keys and values (no attention over the prompt is needed for
-    them); the decode step and both caches are checked against it."""
-    w = workloads.get("gpt2-small")
-    M = ee.ee_extend_max_positions()
-    prompts = [M - 1, 5]
-    dec = Decoder(w, 77, 1, prompts, max_new=1)
-    rows = [_token_rows(w, 900 + b, prompts[b] + 1) for b in range(2)]
-    x = torch.cat([rows[b][:prompts[b]] for b in range(2)]).to(DEV)
+    them); every step's outputs and both caches are checked against it."""
+    w = workloads.get(name)
+    dec = Decoder(w, 77, 1, prompts, max_new=sum(s[0] for s in steps) + 3)
+    B = len(prompts)
+    extra = [sum(s[b] for s in steps) for b in range(B)]
+    rows = [_token_rows(w, 900 + b, prompts[b] + extra[b]) for b in range(B)]
+    x = torch.cat([rows[b][:prompts[b]] for b in range(B)]).to(DEV)
     y = torch.empty_like(x)
-    ws = torch.empty(ee.ee_extend_workspace_size(dec.layers[0], 2, x.shape[0]), dtype=torch.uint8, device=DEV)
-    say(f"decode at the position limit: prefill {prompts}")
-    ee.ee_stack_extend(dec.layers, x, prompts, [0, 0], dec.slot_base, dec.cache, dec.capacity, y, ws)
+    ws = torch.empty(ee.ee_extend_workspace_size(dec.layers[0], B, x.shape[0]), dtype=torch.uint8, device=DEV)
+    say(f"{name} long context: prefill {prompts}")
+    ee.ee_stack_extend(dec.layers, x, prompts, [0] * B, dec.slot_base, dec.cache, dec.capacity, y, ws)
     torch.cuda.synchronize()
-    for b in range(2):
+    for b in range(B):
         oracle.prefill_first_layer_cache(dec.ocaches[b], rows[b][:prompts[b]].double().numpy(), dec.params[0],
                                          w.n_heads, w.head_dim)
     dec.ctx = list(prompts)
-    got, ref = dec.step(torch.cat([rows[0][-1:], rows[1][-1:]]), [1, 1])
-    err = normwise_rel(got, ref)
-    say(f"decode step at {dec.ctx[0]} positions: rel {err:.3e}")
-    assert dec.ctx[0] == M
-    assert np.all(np.isfinite(got)) and err <= 2e-2
+    pos = list(prompts)
+    for new in steps:
+        toks = torch.cat([rows[b][pos[b]:pos[b] + new[b]] for b in range(B)])
+        got, ref = dec.step(toks, new)
+        err = normwise_rel(got, ref)
+        say(f"{name}: step of {new} new tokens after {pos} positions: rel {err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= 2e-2
+        pos = [p + n for p, n in zip(pos, new)]
+    assert dec.ctx == pos and max(pos) > (32768 if name == "gpt2-small" else 2000)
     cv = dec.cache_view()
-    for b in range(2):
+    for b in range(B):
         n, s0 = dec.ctx[b], dec.slot_base[b]
         k = cv[0, 0, :, s0:s0 + n].double().cpu().numpy()
         v = cv[0, 1, :, s0:s0 + n].double().cpu().numpy()
         assert normwise_rel(k, dec.ocaches[b].k[0]) <= 2e-3 and normwise_rel(v, dec.ocaches[b].v[0]) <= 2e-3
-    # one more position is rejected before any device work
-    ws1 = torch.empty(ee.ee_extend_workspace_size(dec.layers[0], 2, 1), dtype=torch.uint8, device=DEV)
-    y1 = torch.empty(1, w.hidden, dtype=w.torch_dtype, device=DEV)
-    assert dec.slot_base[0] + M + 1 <= dec.capacity  # so the position limit is what rejects it
-    with pytest.raises(ee.EEError) as e:
-        ee.ee_stack_extend(dec.layers, y1, [1, 0], dec.ctx, dec.slot_base, dec.cache, dec.capacity, y1.clone(), ws1)
-    assert e.value.status == 2  # EE_ERR_UNSUPPORTED
+    assert ee.ee_extend_max_positions() == 2 ** 31 - 1

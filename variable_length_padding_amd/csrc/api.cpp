@@ -457,10 +457,11 @@ Plan plan_extend(const ee_layer_desc& d, int32_t B, int64_t T) {
   p.big = take(t * std::max<size_t>(3 * Hp, preferred_pitch((int64_t)F, s)) * s);
   p.o = take(t * Hp * s);
   p.h = take(t * H * s);
-  if (d.dtype == EE_F16) {  // reserved at every T, so a size taken for T covers any smaller step
-    p.splitk = take(kSplitkScratch);
-    p.splitk_bytes = kSplitkScratch;
-  }
+  // partial sums (the small-M GEMMs' split-K / stream-K pieces, then the cache
+  // attention's per-chunk softmax states), reserved at every T, so a size
+  // taken for T covers any smaller step
+  p.splitk = take(kSplitkScratch);
+  p.splitk_bytes = kSplitkScratch;
   p.total = off;
   return p;
 }
@@ -553,8 +554,11 @@ ee_status extend_impl(ee_layer* const* layers, int32_t n_layers, const void* d_x
       if (prefill) {  // attention among the new tokens only: the packed varlen kernel
         EE_LAUNCH("attention", s, launch_attention(d.dtype, qkv, cu, B, max_new, nh, hd, true, o, s));
       } else {
-        EE_LAUNCH("cache_attention", s, launch_cache_attention(d.dtype, qkv, arg, cu, B, nh, hd, max_pos, capacity,
-                                                               layer_cache, layer_cache + kv_half, o, s));
+        // the chunks' softmax partials use the GEMMs' partial-sum region, idle
+        // between the QKV GEMM's reduce and the out GEMM
+        EE_LAUNCH("cache_attention", s,
+                  launch_cache_attention(d.dtype, qkv, arg, cu, B, T, nh, hd, max_pos, capacity, layer_cache,
+                                         layer_cache + kv_half, o, at(ws, p.splitk), p.splitk_bytes, s));
       }
       return EE_OK;
     }));

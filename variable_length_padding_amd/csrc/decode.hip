@@ -11,6 +11,9 @@
 // Sequence b owns the slots slot_base[b] .. slot_base[b] + ctx + new - 1, so
 // the cache is packed by sequence (no padding to a batch maximum) and the keys
 // of one (sequence, head) are one contiguous block.
+#include <algorithm>
+#include <climits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -81,126 +84,187 @@ struct Vec8<float> {
   }
 };
 
-__device__ __forceinline__ float block_reduce(float v, bool is_max, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const float o = __shfl_xor(v, d, kWave);
-    v = is_max ? fmaxf(v, o) : v + o;
-  }
-  __syncthreads();  // red may still be read from the previous reduction
-  if (lane == 0) red[wave] = v;
-  __syncthreads();
-  float r = red[0];
-#pragma unroll
-  for (int w = 1; w < kExtendThreads / 64; ++w) r = is_max ? fmaxf(r, red[w]) : r + red[w];
-  return r;
-}
+// Running softmax state of one query over a set of keys, in the exp2
+// domain (scores pre-multiplied by log2(e) / sqrt(head_dim)): m = the largest
+// score, l = sum of 2^(s - m), acc = sum of 2^(s - m) v.  An empty set is
+// (-inf, 0, 0).  Merging rescales both sides to the larger maximum.
+__device__ __forceinline__ float rescale(float m, float to) { return m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - to); }
 
-// Attention of the new tokens over the cache.  One workgroup per (head,
-// sequence); the new queries of the sequence one after another, query i at
-// position p = ctx + i seeing keys 0..p (causal).
-//   scores: a key is read by LPK lanes at 8 elements each (a whole row per
-//           lane group, coalesced), partial dot products summed by shuffles;
-//           scores go to LDS (dynamic, >= p + 1 floats);
-//   softmax: block max and sum; exp(s - max) in place;
-//   P.V:    the same key partition: a lane group reads a key's V row in
-//           16-byte chunks and accumulates its 8 dims; shuffles sum the key
-//           groups of a wave, LDS the four waves.
-template <typename T, int HD>
-__global__ __launch_bounds__(kExtendThreads) void cache_attention_kernel(const T* __restrict__ qkv, ExtendArg arg,
-                                                                       const int32_t* __restrict__ cu, int nh,
-                                                                       int64_t capacity, const T* __restrict__ kc,
-                                                                       const T* __restrict__ vc, T* __restrict__ o) {
+// Attention of the new tokens over the cache, split over key chunks.  One
+// workgroup per (chunk, head, new token): query t of sequence b at position
+// p = ctx + i sees keys 0..p; the chunk is keys [c*chunk, (c+1)*chunk) of
+// those.  A lane group of LPK = HD/8 lanes reads a key row (8 elements per
+// lane, coalesced) and owns 8 dims of the output; the groups step through the
+// chunk KB keys at a time with an online softmax (one rescale per block of
+// KB keys), so no score buffer is kept and the context is not limited by LDS.
+// The groups' states are merged by shuffles, the four waves' in LDS.  With
+// one chunk (FINAL) the normalised output is stored directly; otherwise the
+// chunk's (m, l, acc[HD]) go to `part`, and cache_attn_merge_kernel combines
+// the chunks.
+template <typename T, int HD, bool FINAL>
+__global__ __launch_bounds__(kExtendThreads) void cache_attn_chunk_kernel(
+    const T* __restrict__ qkv, ExtendArg arg, const int32_t* __restrict__ cu, int B, int64_t T_new, int nh,
+    int64_t capacity, const T* __restrict__ kc, const T* __restrict__ vc, int chunk, int n_chunks,
+    float* __restrict__ part, T* __restrict__ o) {
   constexpr int LPK = HD / 8;            // lanes per key row
-  constexpr int KPW = 64 / LPK;          // keys per wave per pass
+  constexpr int GPW = 64 / LPK;          // lane groups per wave
   constexpr int NW = kExtendThreads / 64;
+  constexpr int G = NW * GPW;            // lane groups per workgroup
+  constexpr int KB = 4;                  // keys per lane group per step
   static_assert(64 % LPK == 0, "a key row must be split over a power-of-two lane group");
-  extern __shared__ float smem[];
-  float* red = smem;                       // NW floats
-  float* part = smem + NW;                 // NW * HD floats
-  float* scores = part + NW * HD;          // >= max position + 1 floats
-  const int h = blockIdx.x, b = blockIdx.y;
-  const int n_new = arg.new_len[b];
-  if (n_new == 0) return;
+  __shared__ float red[NW][HD + 2];
+  const int c = blockIdx.x, h = blockIdx.y;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int gl = lane / LPK, ch = lane % LPK;
+  const int grp = wave * GPW + gl;
   const int Hp = nh * HD;
-  const int64_t row_len = 3 * (int64_t)Hp;
-  const T* K = kc + ((int64_t)h * capacity + arg.slot_base[b]) * HD;
-  const T* V = vc + ((int64_t)h * capacity + arg.slot_base[b]) * HD;
-  const float scale = 1.0f / sqrtf((float)HD);
-  const int g = lane / LPK, c = lane % LPK;  // key within the wave's pass, chunk of the row
-
-  for (int i = 0; i < n_new; ++i) {
-    const int64_t row = cu[b] + i;
-    const int nk = arg.ctx_len[b] + i + 1;
+  const float qscale = kLog2e / sqrtf((float)HD);
+  for (int64_t t = blockIdx.z; t < T_new; t += gridDim.z) {
+    const int b = seq_of(cu, B, t);
+    const int nk = arg.ctx_len[b] + (int)(t - cu[b]) + 1;
+    const int k0 = c * chunk;
+    const int k1 = min(nk, k0 + chunk);
+    const T* K = kc + ((int64_t)h * capacity + arg.slot_base[b]) * HD + ch * 8;
+    const T* V = vc + ((int64_t)h * capacity + arg.slot_base[b]) * HD + ch * 8;
     float q[8];
-    Vec8<T>::load(qkv + row * row_len + h * HD + c * 8, q);
+    Vec8<T>::load(qkv + t * 3 * (int64_t)Hp + h * HD + ch * 8, q);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) q[e] *= scale;
-    float m = -INFINITY;
-    for (int j0 = wave * KPW; j0 < nk; j0 += NW * KPW) {
-      const int j = j0 + g;
-      float s = 0.f;
-      if (j < nk) {
-        float k[8];
-        Vec8<T>::load(K + (int64_t)j * HD + c * 8, k);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) s += q[e] * k[e];
-      }
-#pragma unroll
-      for (int d = LPK / 2; d >= 1; d >>= 1) s += __shfl_xor(s, d, kWave);
-      if (j < nk) {
-        if (c == 0) scores[j] = s;
-        m = fmaxf(m, s);
-      }
-    }
-    m = block_reduce(m, true, red);
-    float l = 0.f;
-    for (int j = threadIdx.x; j < nk; j += kExtendThreads) {
-      const float e = __builtin_amdgcn_exp2f((scores[j] - m) * kLog2e);
-      scores[j] = e;
-      l += e;
-    }
-    l = block_reduce(l, false, red);  // its barriers also publish the exponentials
-    float acc[8];
+    for (int e = 0; e < 8; ++e) q[e] *= qscale;
+    float m = -INFINITY, l = 0.f, acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-    for (int j0 = wave * KPW; j0 < nk; j0 += NW * KPW) {
-      const int j = j0 + g;
-      if (j < nk) {
-        const float pj = scores[j];
-        float v[8];
-        Vec8<T>::load(V + (int64_t)j * HD + c * 8, v);
+    // every lane of a group runs the same trip count, so the shuffles below
+    // never straddle a branch
+    for (int j0 = k0 + grp * KB; j0 < k1; j0 += G * KB) {
+      float s[KB];
+      float mb = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] += pj * v[e];
+      for (int kk = 0; kk < KB; ++kk) {
+        const int j = j0 + kk;
+        float d = 0.f;
+        if (j < k1) {
+          float k[8];
+          Vec8<T>::load(K + (int64_t)j * HD, k);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) d += q[e] * k[e];
+        }
+#pragma unroll
+        for (int x = LPK / 2; x >= 1; x >>= 1) d += __shfl_xor(d, x, kWave);
+        s[kk] = j < k1 ? d : -INFINITY;
+        mb = fmaxf(mb, s[kk]);
       }
+      const float mn = fmaxf(m, mb);  // finite: key j0 < k1 is in the block
+      const float r = rescale(m, mn);
+      l *= r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] *= r;
+#pragma unroll
+      for (int kk = 0; kk < KB; ++kk) {
+        const int j = j0 + kk;
+        if (j < k1) {
+          const float pj = __builtin_amdgcn_exp2f(s[kk] - mn);
+          float v[8];
+          Vec8<T>::load(V + (int64_t)j * HD, v);
+          l += pj;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] += pj * v[e];
+        }
+      }
+      m = mn;
     }
+    // the lane groups of a wave
 #pragma unroll
-    for (int d = LPK; d < 64; d <<= 1)
+    for (int x = LPK; x < 64; x <<= 1) {
+      const float mo = __shfl_xor(m, x, kWave), lo = __shfl_xor(l, x, kWave);
+      float ao[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += __shfl_xor(acc[e], d, kWave);
-    if (g == 0)
+      for (int e = 0; e < 8; ++e) ao[e] = __shfl_xor(acc[e], x, kWave);
+      const float mn = fmaxf(m, mo);
+      const float ra = rescale(m, mn), rb = rescale(mo, mn);
+      l = l * ra + lo * rb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) part[wave * HD + c * 8 + e] = acc[e];
+      for (int e = 0; e < 8; ++e) acc[e] = acc[e] * ra + ao[e] * rb;
+      m = mn;
+    }
+    if (gl == 0) {
+      if (ch == 0) {
+        red[wave][0] = m;
+        red[wave][1] = l;
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) red[wave][2 + ch * 8 + e] = acc[e];
+    }
     __syncthreads();
     for (int d = threadIdx.x; d < HD; d += kExtendThreads) {
-      float s = 0.f;
+      float M = red[0][0];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) s += part[w * HD + d];
-      o[row * Hp + h * HD + d] = (T)(s / l);
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, red[w][0]);
+      float L = 0.f, A = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = rescale(red[w][0], M);
+        L += red[w][1] * f;
+        A += red[w][2 + d] * f;
+      }
+      if constexpr (FINAL) {
+        o[t * Hp + h * HD + d] = from_f32<T>(A / L);
+      } else {
+        float* pp = part + ((t * nh + h) * (int64_t)n_chunks + c) * (HD + 2);
+        if (d == 0) {
+          pp[0] = M;
+          pp[1] = L;
+        }
+        pp[2 + d] = A;
+      }
     }
-    __syncthreads();  // scores and part are rewritten by the next query
+    __syncthreads();  // red is rewritten for the next token
+  }
+}
+
+// o = the chunks' states of one (token, head) merged: rescaled to the
+// largest maximum, summed in chunk order, normalised.
+template <typename T, int HD>
+__global__ __launch_bounds__(HD) void cache_attn_merge_kernel(const float* __restrict__ part, int64_t T_new, int nh,
+                                                              int n_chunks, T* __restrict__ o) {
+  const int h = blockIdx.x, d = threadIdx.x;
+  for (int64_t t = blockIdx.y; t < T_new; t += gridDim.y) {
+    const float* pp = part + (t * nh + h) * (int64_t)n_chunks * (HD + 2);
+    float M = -INFINITY;
+    for (int c = 0; c < n_chunks; ++c) M = fmaxf(M, pp[(int64_t)c * (HD + 2)]);
+    float L = 0.f, A = 0.f;
+    for (int c = 0; c < n_chunks; ++c) {
+      const float* q = pp + (int64_t)c * (HD + 2);
+      const float f = rescale(q[0], M);
+      L += q[1] * f;
+      A += q[2 + d] * f;
+    }
+    o[t * (int64_t)nh * HD + h * HD + d] = from_f32<T>(A / L);
   }
 }
 
 template <typename T, int HD>
-hipError_t launch_cache_attn_t(const void* qkv, const ExtendArg& arg, const int32_t* cu, int B, int nh,
-                               int max_pos, int64_t capacity, const void* kc, const void* vc, void* o, hipStream_t s) {
-  const size_t lds = sizeof(float) * ((size_t)(kExtendThreads / 64) * (HD + 1) + (size_t)max_pos);
-  hipLaunchKernelGGL((cache_attention_kernel<T, HD>), dim3(nh, B), dim3(kExtendThreads), lds, s,
-                     static_cast<const T*>(qkv), arg, cu, nh, capacity, static_cast<const T*>(kc),
-                     static_cast<const T*>(vc), static_cast<T*>(o));
+hipError_t launch_cache_attn_t(const void* qkv, const ExtendArg& arg, const int32_t* cu, int B, int64_t T_new, int nh,
+                               int max_pos, int64_t capacity, const void* kc, const void* vc, void* o, void* scratch,
+                               size_t scratch_bytes, hipStream_t s) {
+  const CacheAttnPlan p = cache_attention_plan(T_new, nh, HD, max_pos, scratch_bytes);
+  if (p.n_chunks < 1) return hipErrorInvalidValue;
+  const unsigned gz = (unsigned)(T_new < 65535 ? T_new : 65535);
+  const T* q = static_cast<const T*>(qkv);
+  const T* k = static_cast<const T*>(kc);
+  const T* v = static_cast<const T*>(vc);
+  T* out = static_cast<T*>(o);
+  float* part = static_cast<float*>(scratch);
+  if (p.n_chunks == 1) {
+    hipLaunchKernelGGL((cache_attn_chunk_kernel<T, HD, true>), dim3(1, nh, gz), dim3(kExtendThreads), 0, s, q, arg, cu,
+                       B, T_new, nh, capacity, k, v, p.chunk, 1, nullptr, out);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL((cache_attn_chunk_kernel<T, HD, false>), dim3(p.n_chunks, nh, gz), dim3(kExtendThreads), 0, s, q,
+                     arg, cu, B, T_new, nh, capacity, k, v, p.chunk, p.n_chunks, part, out);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((cache_attn_merge_kernel<T, HD>), dim3(nh, gz), dim3(HD), 0, s, part, T_new, nh, p.n_chunks,
+                     out);
   return hipGetLastError();
 }
 
@@ -210,9 +274,25 @@ bool cache_attention_ok(int head_dim) {
   return head_dim == 16 || head_dim == 32 || head_dim == 64 || head_dim == 128;
 }
 
-// scores of one query (4 bytes per position) plus the partial sums stay
-// within 64 KiB of dynamic LDS
-int cache_attention_max_positions() { return 15360; }
+// The cache attention keeps no per-position buffer, so the context is bounded
+// only by the cache's 32-bit slot range.
+int cache_attention_max_positions() { return INT32_MAX; }
+
+CacheAttnPlan cache_attention_plan(int64_t T_new, int nh, int hd, int max_pos, size_t scratch_bytes) {
+  CacheAttnPlan p{0, 0};
+  if (T_new < 1 || nh < 1 || max_pos < 1) return p;
+  const double per_chunk = (double)T_new * nh * (hd + 2) * 4.0;  // partial-state bytes per chunk
+  int64_t chunk = kCacheAttnChunk;
+  int64_t n = (max_pos + chunk - 1) / chunk;
+  while (n > 1 && (double)n * per_chunk > (double)scratch_bytes) {
+    chunk *= 2;
+    n = (max_pos + chunk - 1) / chunk;
+  }
+  if (n > 1 && (double)n * per_chunk > (double)scratch_bytes) return p;
+  p.chunk = (int)std::min<int64_t>(chunk, INT32_MAX);
+  p.n_chunks = (int)n;
+  return p;
+}
 
 hipError_t launch_extend_cu(const ExtendArg& arg, int B, int32_t* cu, hipStream_t s) {
   hipLaunchKernelGGL(extend_cu_kernel, dim3(1), dim3(64), 0, s, arg, B, cu);
@@ -229,12 +309,14 @@ hipError_t launch_append_kv(const void* qkv, const ExtendArg& arg, const int32_t
 }
 
 hipError_t launch_cache_attention(ee_dtype dt, const void* qkv, const ExtendArg& arg, const int32_t* cu, int B,
-                                  int nh, int hd, int max_pos, int64_t capacity, const void* kc, const void* vc,
-                                  void* o, hipStream_t s) {
-#define EE_CACHE_ATTN(HDV)                                                                                     \
-  if (hd == HDV)                                                                                               \
-    return dt == EE_F16 ? launch_cache_attn_t<f16, HDV>(qkv, arg, cu, B, nh, max_pos, capacity, kc, vc, o, s) \
-                        : launch_cache_attn_t<float, HDV>(qkv, arg, cu, B, nh, max_pos, capacity, kc, vc, o, s);
+                                  int64_t T_new, int nh, int hd, int max_pos, int64_t capacity, const void* kc,
+                                  const void* vc, void* o, void* scratch, size_t scratch_bytes, hipStream_t s) {
+#define EE_CACHE_ATTN(HDV)                                                                                         \
+  if (hd == HDV)                                                                                                   \
+    return dt == EE_F16 ? launch_cache_attn_t<f16, HDV>(qkv, arg, cu, B, T_new, nh, max_pos, capacity, kc, vc, o,  \
+                                                        scratch, scratch_bytes, s)                                 \
+                        : launch_cache_attn_t<float, HDV>(qkv, arg, cu, B, T_new, nh, max_pos, capacity, kc, vc, o, \
+                                                          scratch, scratch_bytes, s);
   EE_CACHE_ATTN(16)
   EE_CACHE_ATTN(32)
   EE_CACHE_ATTN(64)

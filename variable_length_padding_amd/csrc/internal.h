@@ -54,9 +54,19 @@ int cache_attention_max_positions();
 hipError_t launch_extend_cu(const ExtendArg& arg, int B, int32_t* cu, hipStream_t s);
 hipError_t launch_append_kv(const void* qkv, const ExtendArg& arg, const int32_t* cu, int B, int64_t T, int nh,
                             int head_bytes, int64_t capacity, void* cache, hipStream_t s);
+// Cache attention over key chunks of `chunk` positions (n_chunks per query):
+// each chunk's softmax state is a partial in scratch, merged by a second
+// kernel (none when n_chunks == 1).  The chunk length starts at
+// kCacheAttnChunk and doubles until the partials fit scratch_bytes;
+// n_chunks == 0: they never fit.
+constexpr int kCacheAttnChunk = 512;
+struct CacheAttnPlan {
+  int chunk, n_chunks;
+};
+CacheAttnPlan cache_attention_plan(int64_t T_new, int nh, int hd, int max_pos, size_t scratch_bytes);
 hipError_t launch_cache_attention(ee_dtype dt, const void* qkv, const ExtendArg& arg, const int32_t* cu, int B,
-                                  int nh, int hd, int max_pos, int64_t capacity, const void* kc, const void* vc,
-                                  void* o, hipStream_t s);
+                                  int64_t T_new, int nh, int hd, int max_pos, int64_t capacity, const void* kc,
+                                  const void* vc, void* o, void* scratch, size_t scratch_bytes, hipStream_t s);
 
 // ---- layernorm.hip ----
 int layernorm_max_hidden(ee_dtype dt);
