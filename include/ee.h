@@ -364,6 +364,15 @@ typedef struct {
 } ee_kernel_stat;
 
 EE_API ee_status ee_profile_enable(int32_t on);
+/* Debug mode: while on, every kernel launch of the calls above is followed by
+ * hipStreamSynchronize of its stream, so an asynchronous failure (a memory
+ * fault, an illegal instruction) is returned as EE_ERR_HIP by the call that
+ * launched the failing kernel, with that launch site in ee_last_error()
+ * (e.g. "gemm_fc1: ..."), instead of surfacing at a later call.  It also
+ * makes every call synchronous: for debugging, never under graph capture.
+ * Setting EE_DEBUG_SYNC=1 in the environment before the library loads turns
+ * it on from the start.  Always EE_OK. */
+EE_API ee_status ee_debug_sync(int32_t on);
 /* Restricts the timing to one launch site (e.g. "gemm_fc1"); NULL or "" times
  * every site again.  Each recorded event pair leaves a bubble of a few us in
  * its stream, so timing only the kernel of interest keeps the rest of the work

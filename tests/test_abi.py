@@ -216,6 +216,11 @@ def test_extend_noalloc_rejects_before_device_work():
         lib.ee_layer_destroy(h)
 
 
+def test_debug_sync_toggles_without_device_work():
+    lib = ee.lib()
+    assert lib.ee_debug_sync(1) == 0 and lib.ee_debug_sync(0) == 0
+
+
 def test_preferred_row_pitch():
     lib = ee.lib()
     # a row that is a multiple of 32 KiB gets 128 bytes more; others stay dense

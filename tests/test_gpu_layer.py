@@ -199,3 +199,20 @@ def test_profile_filter_times_one_site():
     assert set(only) == {"gemm_fc1"} and only["gemm_fc1"]["launches"] == 1 and only["gemm_fc1"]["total_ms"] > 0
     assert {"gemm_fc1", "attention", "rebuild"} <= set(every)
     assert torch.equal(y1, y2)
+
+
+def test_debug_sync_mode_gives_the_same_bits():
+    """With ee_debug_sync on, every launch is followed by a stream
+    synchronisation; the layer's outputs are the same bits as without it."""
+    w = workloads.get("gpt2-small")
+    lens = workloads.lengths(w, 3)
+    x = workloads.activations(w, 3, w.batch, w.pad_len, lens)
+    p = workloads.layer_params(w, 3, 0, variant="affine")
+    y0 = _run_layer(w, lens, x, p)
+    ee.ee_debug_sync(True)
+    try:
+        y1 = _run_layer(w, lens, x, p, layers_params=[p, p])
+        y2 = _run_layer(w, lens, x, p)
+    finally:
+        ee.ee_debug_sync(False)
+    assert torch.equal(y0, y2) and torch.isfinite(y1).all()

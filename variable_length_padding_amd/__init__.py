@@ -20,7 +20,7 @@ __all__ = [
     "ee_attention_varlen", "ee_attention_padded", "ee_transpose_padding_rebuild_heads",
     "ee_transpose_padding_remove_heads", "ee_add_bias_residual_layernorm",
     "BLOCK_GPT_PRELN", "BLOCK_BERT_POSTLN", "ATTN_VARLEN", "ATTN_PADDED",
-    "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_filter", "ee_profile_collect",
+    "Layer", "ee_stack_forward", "ee_profile_enable", "ee_profile_filter", "ee_profile_collect", "ee_debug_sync",
     "ee_kv_cache_bytes", "ee_extend_workspace_size", "ee_extend_max_positions", "ee_stack_extend",
     "ee_stack_extend_noalloc", "NOALLOC_SCRATCH_BYTES",
     "MAX_EXTEND_BATCH",
@@ -132,6 +132,7 @@ _SIGS = {
     "ee_add_bias_residual_layernorm": (C.c_int, [_VP, _VP, _VP, _VP, _VP, _I64, _I32, C.c_float, C.c_int, _VP,
                                                  _VP]),
     "ee_profile_enable": (C.c_int, [_I32]),
+    "ee_debug_sync": (C.c_int, [_I32]),
     "ee_profile_filter": (C.c_int, [C.c_char_p]),
     "ee_profile_collect": (C.c_int, [C.POINTER(KernelStat), _I32, _PI32]),
     "ee_kv_cache_bytes": (C.c_int, [_VP, _I32, _I64, C.POINTER(_SZ)]),
@@ -655,6 +656,12 @@ def ee_stack_forward(layers: List[Layer], x, lens: Sequence[int], y, workspace, 
 # ---------------------------------------------------------------- timing
 def ee_profile_enable(on: bool = True):
     _check(lib().ee_profile_enable(1 if on else 0), "ee_profile_enable")
+
+
+def ee_debug_sync(on: bool = True):
+    """Synchronise the stream after every launch (a launch that fails is then
+    reported by the call that made it, with its launch site)."""
+    _check(lib().ee_debug_sync(1 if on else 0), "ee_debug_sync")
 
 
 def ee_profile_filter(site: Optional[str] = None):

@@ -5,7 +5,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -123,11 +125,20 @@ Profiler& prof() {
   return *p;
 }
 
+// Debug mode (ee_debug_sync, or EE_DEBUG_SYNC=1 in the environment when the
+// library loads): every launch is followed by a synchronisation of its
+// stream, so an asynchronous failure surfaces at the launch site that caused
+// it instead of at some later call.
+std::atomic<bool> g_debug_sync{[] {
+  const char* v = std::getenv("EE_DEBUG_SYNC");
+  return v && v[0] && v[0] != '0';
+}()};
+
 // Runs `launch` (which returns the launch's hipError_t); while profiling is on,
 // brackets it with two events recorded on `s`.  `flops` and `kernel` are
 // recorded with the launch.
 template <class F>
-hipError_t timed(const char* site, hipStream_t s, F&& launch, double flops = 0.0, const char* kernel = nullptr) {
+hipError_t timed_launch(const char* site, hipStream_t s, F&& launch, double flops, const char* kernel) {
   Profiler& p = prof();
   if (!p.on) return launch();
   std::lock_guard<std::mutex> lk(p.mu);
@@ -150,6 +161,13 @@ hipError_t timed(const char* site, hipStream_t s, F&& launch, double flops = 0.0
   if (r != hipSuccess) return r;
   p.recs.push_back(Profiler::Rec{site, i, flops, kernel});
   return hipSuccess;
+}
+
+template <class F>
+hipError_t timed(const char* site, hipStream_t s, F&& launch, double flops = 0.0, const char* kernel = nullptr) {
+  hipError_t r = timed_launch(site, s, launch, flops, kernel);
+  if (r == hipSuccess && g_debug_sync.load(std::memory_order_relaxed)) r = hipStreamSynchronize(s);
+  return r;
 }
 
 #define EE_LAUNCH(site, stream, call)                                        \
@@ -1055,6 +1073,11 @@ ee_status ee_add_bias_residual_layernorm(const void* u, const void* bias, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   EE_LAUNCH("add_bias_residual_ln", s,
             launch_add_bias_residual_layernorm(dtype, u, bias, residual, gamma, beta, rows, hidden, eps, y, s));
+  return EE_OK;
+}
+
+ee_status ee_debug_sync(int32_t on) {
+  g_debug_sync.store(on != 0);
   return EE_OK;
 }
 
