@@ -56,7 +56,9 @@ PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROOFLINE_SITE = "gemm_fc1"
 PROFILES = os.path.join(ROOT, "profiles")
-GEMM_SOURCE = os.path.join(ROOT, "variable_length_padding_amd", "csrc", "gemm_f16.hip")
+# the GEMM kernel's source and the headers that shape its loads and tile order
+GEMM_SOURCES = [os.path.join(ROOT, "variable_length_padding_amd", "csrc", f)
+                for f in ("gemm_f16.hip", "gemm_tile_order.h", "lds_dma.h")]
 DEFAULT_WORKLOAD = "gpt3-48l-stream"
 
 
@@ -164,12 +166,15 @@ def kernel_symbol(label):
             "EEvPKDF16_iS3_iS3_S3_PDF16_iiiiiiiPf")
 
 
-def gemm_code_sha256(path=GEMM_SOURCE):
-    """sha256 of the GEMM source's code: // comments, trailing spaces and
-    blank lines removed (the file holds no // inside string literals), so an
-    edit of the comments keeps counters taken on the same code valid."""
-    with open(path) as f:
-        lines = [ln.split("//", 1)[0].rstrip() for ln in f]
+def gemm_code_sha256(paths=GEMM_SOURCES):
+    """sha256 of the GEMM sources' code, in order: // comments, trailing
+    spaces and blank lines removed (the files hold no // inside string
+    literals), so an edit of the comments keeps counters taken on the same
+    code valid."""
+    lines = []
+    for path in paths:
+        with open(path) as f:
+            lines += [ln.split("//", 1)[0].rstrip() for ln in f]
     return hashlib.sha256("\n".join(ln for ln in lines if ln).encode()).hexdigest()
 
 

@@ -193,6 +193,27 @@ def test_gemm_row_split_bit_identical(M, N, epi, gelu):
     assert not diff, f"rows {diff[:8]}... differ"
 
 
+@pytest.mark.parametrize("M,N", [(7317, 49152), (7889, 36864), (8731, 12288), (9036, 49152), (8192, 12288)])
+def test_gemm_integer_exact_request_stream_rows(M, N):
+    """Row counts of the request stream's batches at the layer's GEMM widths:
+    29, 31, 35 and 36 M-tiles of 256, whose tiles_m % 4 leftover M-tiles the
+    tile order shares out by N, some with a row split.  C starts as NaN; on
+    small-integer operands two rows of every 256-row tile (its first and last),
+    over all N, must be the fp16 rounding of the exact sum, bit for bit, so a
+    tile computed twice or never shows."""
+    K = 128
+    A, W = _small_ints((M, K)), _small_ints((N, K))
+    bias = _small_ints((N,))
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    ee.ee_linear(A.to(DEV), W.to(DEV), bias.to(DEV), None, ee.EPI_BIAS, C)
+    torch.cuda.synchronize()
+    rows = sorted({r for t in range(0, M, 256) for r in (t, min(M, t + 256) - 1)})
+    exact = A[rows].double().numpy() @ W.double().numpy().T + bias.double().numpy()
+    got = C[rows].cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16)), \
+        f"{np.count_nonzero(got != exact.astype(np.float16))} of {got.size} differ"
+
+
 @pytest.mark.parametrize("K", [32768, 49152 + 64])
 def test_gemm_integer_exact_long_k(K):
     """Long K ranges (>= 32768) take the three-W-stage ring of the 256 x 256 tile

@@ -13,38 +13,60 @@ namespace ee {
 // Tiles are numbered `tile` = 0 .. n_tiles-1 in launch order (a persistent
 // launch of a multiple of 8 workgroups walks tile = blockIdx.x + k*gridDim.x).
 // The hardware deals consecutive workgroup ids round-robin to the 8 XCDs, so
-// tile % 8 is the XCD that computes the tile, and each XCD's L2 is private.
+// tile % 8 is the XCD that computes the tile, tile / 8 its place in that XCD's
+// sequence, and each XCD's L2 is private.
 //
 // With tiles_n a multiple of 8, XCD x = 2p + h takes half h of the N tiles and
-// the p-th quarter of that half's tiles, walked in groups of 4 M-tiles (M
-// fastest inside a group).  Each round of 32 tiles on an XCD is then 4 M-tiles
-// by 8 N-tiles -- the split of 32 tiles that reads the fewest operand panels
-// through the XCD's L2 -- and the two XCDs of a pair share their A panels.  At
-// any time the 8 XCDs hold 4 groups of A panels, not 8: at 8192 rows and
-// K = 12288 that is 100 MB of A beside the W panels streaming through the
-// 256 MB Infinity Cache, instead of 200 MB (2-3% faster on the FC1 and QKV
-// shapes there; the same tiles at 4096 rows).  Otherwise, with n_tiles a
-// multiple of 8, each XCD takes a contiguous range of the group-major order;
-// else the group-major order itself.
+// the p-th quarter of the M tiles (tiles_m / 4 of them), walked in groups of 4
+// M-tiles (M fastest inside a group, then N); the tiles_m % 4 M-tiles left over
+// are shared out by N, a quarter of the half's N tiles to each XCD.  So:
+//   * each round of 32 tiles on an XCD is a 4 x 8 block of tiles, the split of
+//     32 tiles that reads the fewest operand panels through the XCD's L2;
+//   * the two XCDs of a pair work on the same M-tiles at the same time and
+//     share their A panels, so the 8 XCDs hold 4 groups of A panels;
+//   * the four XCDs of a half walk the same N-tiles at the same time, so each
+//     W panel is read from HBM about once per 4 XCDs, through the Infinity
+//     Cache.
+// The last point is what splitting each half's tiles into four contiguous
+// quarters of one group-major order lost when tiles_m is not a multiple of 16:
+// the XCDs then entered the N range at different points, each streamed W on
+// its own, and FC1 (N = 49152, K = 12288) ran 9-12% slower per round.
+// Otherwise, with n_tiles a multiple of 8, each XCD takes a contiguous range of
+// the group-major order; else the group-major order itself.
 EE_HOST_DEVICE inline void gemm_tile_origin(int tile, int n_tiles, int tiles_m, int tiles_n, int bm, int bn, int& m0,
                                             int& n0) {
   constexpr int GM = 4;  // M-tiles per group
-  int lin = tile, m_tiles = tiles_m, n_cols = tiles_n, n_base = 0;
   if ((tiles_n & 7) == 0) {
-    const int x = tile & 7, h = x & 1, p = x >> 1;
-    n_cols = tiles_n >> 1;
-    n_base = h * n_cols;
-    lin = p * ((tiles_m * n_cols) >> 2) + (tile >> 3);
-  } else if ((n_tiles & 7) == 0) {
-    lin = (tile & 7) * (n_tiles >> 3) + (tile >> 3);
+    const int x = tile & 7, h = x & 1, p = x >> 1, k = tile >> 3;
+    const int n_cols = tiles_n >> 1, mq = tiles_m >> 2;
+    const int main_tiles = mq * n_cols;
+    int m, n;
+    if (k < main_tiles) {
+      const int per_group = GM * n_cols;
+      const int group = k / per_group;
+      const int first_m = group * GM;
+      const int gm = mq - first_m < GM ? mq - first_m : GM;
+      const int ig = k - group * per_group;
+      m = p * mq + first_m + ig % gm;
+      n = ig / gm;
+    } else {  // the tiles_m % 4 leftover M-tiles, N-tiles [p*q, (p+1)*q) of the half
+      const int r = tiles_m & 3, q = n_cols >> 2, i = k - main_tiles;
+      m = 4 * mq + i % r;
+      n = p * q + i / r;
+    }
+    m0 = m * bm;
+    n0 = (h * n_cols + n) * bn;
+    return;
   }
-  const int per_group = GM * n_cols;
+  int lin = tile;
+  if ((n_tiles & 7) == 0) lin = (tile & 7) * (n_tiles >> 3) + (tile >> 3);
+  const int per_group = GM * tiles_n;
   const int group = lin / per_group;
   const int first_m = group * GM;
-  const int gm = m_tiles - first_m < GM ? m_tiles - first_m : GM;
+  const int gm = tiles_m - first_m < GM ? tiles_m - first_m : GM;
   const int ig = lin - group * per_group;
   m0 = (first_m + ig % gm) * bm;
-  n0 = (n_base + ig / gm) * bn;
+  n0 = (ig / gm) * bn;
 }
 
 }  // namespace ee
