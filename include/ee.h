@@ -264,6 +264,26 @@ EE_API ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, in
                                    const void* residual, int64_t M, int32_t N, int32_t K, ee_dtype dtype,
                                    ee_epilogue epi, ee_gelu gelu, void* C, int64_t ldc, void* stream);
 
+/* ee_linear_strided with a workspace of at least ee_linear_ws_workspace_size()
+ * bytes (device memory, not read before it is written; the caller keeps it).
+ * A large fp16 problem runs as one persistent launch of one workgroup per CU
+ * over 256 x 256 tiles.  When the tiles leave that launch's last round
+ * partial, its tiles are shared out as stream-K pieces (Osama et al., PPoPP
+ * 2023): equal contiguous ranges of (tile, K tile) steps, one per workgroup.
+ * A piece that starts inside a tile continues, in the same fp32 accumulators,
+ * from the sums its predecessor left in the workspace, so each element still
+ * adds its K tiles in one chain, in order: the result is bit for bit that of
+ * ee_linear_strided, which runs the remaining rows as a second launch on
+ * smaller tiles instead.  Calls that share a workspace must not overlap in
+ * time (one stream).  fp32 and small problems run as ee_linear_strided.
+ * Errors as ee_linear_strided, plus EE_ERR_WORKSPACE for a small workspace
+ * and EE_ERR_INVALID_ARG for a workspace overlapping an operand. */
+EE_API size_t ee_linear_ws_workspace_size(void);
+EE_API ee_status ee_linear_ws(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
+                              const void* residual, int64_t M, int32_t N, int32_t K, ee_dtype dtype,
+                              ee_epilogue epi, ee_gelu gelu, void* C, int64_t ldc, void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* The row pitch, in elements, that the library gives a matrix of `cols`
  * columns it stores itself (the FC1 output in the layer workspace), and the
  * one it suggests for weights: cols, plus 128 bytes when a row is a multiple
@@ -359,8 +379,8 @@ typedef struct {
   int64_t launches;
   double total_ms;    /* sum of event-measured durations */
   double flops;       /* sum of the launches' algorithmic flops (GEMM sites: 2*rows*N*K; else 0) */
-  char kernel[96];    /* the kernel the site launched, e.g. "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 2>"
-                         (template arguments in declaration order), "several kernels", or "" if not recorded */
+  char kernel[96];    /* the kernel these launches ran, e.g. "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 2, false>"
+                         (template arguments in declaration order), or "" if not recorded */
 } ee_kernel_stat;
 
 EE_API ee_status ee_profile_enable(int32_t on);
@@ -379,8 +399,10 @@ EE_API ee_status ee_debug_sync(int32_t on);
  * at full speed.  The name is copied.  EE_ERR_INVALID_ARG for a name of 32 or
  * more characters. */
 EE_API ee_status ee_profile_filter(const char* site);
-/* Waits for the recorded events, writes up to `capacity` per-site totals into
- * `out` (host), sets *count, and clears the record. */
+/* Waits for the recorded events, writes up to `capacity` totals into `out`
+ * (host), one per (site, kernel) pair in the order first seen -- a site whose
+ * launches ran different kernels (a GEMM with and without an in-order split)
+ * has one row per kernel -- sets *count, and clears the record. */
 EE_API ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* count);
 
 /* ---- Incremental decoding with a packed KV cache ----

@@ -127,6 +127,16 @@ def test_op_entry_points_validate():
                          None) == 1
     # M = 0 is a valid no-op
     assert lib.ee_linear(None, 1 << 31, None, None, 0, 64, 64, ee.F16, ee.EPI_NONE, 0, None, None) == 0
+    # linear with a workspace: its size, then a small, a NULL and an overlapping workspace
+    need = lib.ee_linear_ws_workspace_size()
+    assert need == 4096 + 256 * 256 * 256 * 4
+    a, w, c, ws = 1 << 30, 1 << 31, 1 << 33, 1 << 34
+    assert lib.ee_linear_ws(a, 64, w, 64, None, None, 8, 64, 64, ee.F16, ee.EPI_NONE, 0, c, 64, ws, need - 1,
+                            None) == 3
+    assert lib.ee_linear_ws(a, 64, w, 64, None, None, 8, 64, 64, ee.F16, ee.EPI_NONE, 0, c, 64, None, need,
+                            None) == 1
+    assert lib.ee_linear_ws(a, 64, w, 64, None, None, 8, 64, 64, ee.F16, ee.EPI_NONE, 0, c, 64, c - 4096, need,
+                            None) == 1
     # attention: unsupported head_dim
     assert lib.ee_attention_varlen(1 << 30, 1 << 31, 2, 8, 4, 48, 10, 1, ee.F16, 1 << 32, None) == 2
     assert lib.ee_attention_padded(1 << 30, 1 << 31, 1 << 32, 1 << 33, 2, 8, 4, 24, 1, ee.F16, 1 << 34, None) == 2

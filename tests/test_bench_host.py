@@ -20,8 +20,9 @@ def test_kernel_labels_map_to_library_symbols():
     names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
     for cfg, depth in CONFIGS:
         for epi in range(4):
-            label = f"gemm_f16_mfma_kernel<{cfg}, {epi}, {depth}>"
-            assert bench.kernel_symbol(label) in names, label
+            for ordered in ("false", "true") if cfg.startswith("16, 256") else ("false",):
+                label = f"gemm_f16_mfma_kernel<{cfg}, {epi}, {depth}, {ordered}>"
+                assert bench.kernel_symbol(label) in names, label
     assert bench.kernel_symbol("gemm_streamk_kernel + streamk_reduce_kernel") is None
 
 

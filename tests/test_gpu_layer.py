@@ -174,7 +174,7 @@ def test_profile_records_every_launch_site():
     for site, (K, N, epi) in {"gemm_qkv": (768, 3 * 768, 1), "gemm_out": (768, 768, 2), "gemm_fc1": (768, 3072, 3),
                               "gemm_fc2": (3072, 768, 2)}.items():
         assert stats[site]["flops"] == 2.0 * T * K * N
-        assert stats[site]["kernel"] == f"gemm_f16_mfma_kernel<32, 128, 128, 2, 2, {epi}, 2>"
+        assert stats[site]["kernel"] == f"gemm_f16_mfma_kernel<32, 128, 128, 2, 2, {epi}, 2, false>"
     assert stats["attention"]["flops"] == 0 and not any(s.endswith("_rest") for s in stats)
 
 

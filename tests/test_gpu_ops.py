@@ -214,6 +214,86 @@ def test_gemm_integer_exact_request_stream_rows(M, N):
         f"{np.count_nonzero(got != exact.astype(np.float16))} of {got.size} differ"
 
 
+# (M, N, K, epi): 256 x 256 tile counts that leave the persistent launch's last
+# round partial, with whole rounds R and extra tiles E of 256 workgroups, split
+# over P of them: R 23 / E 64 / P 128 (pieces of 32 K tiles), R 2 / E 100 /
+# P 200 (the TP-shard QKV), R 3 / E 48 / P 96 and P 128 (the TP-shard out
+# projection and FC2 widths, K = 4096 and 49152), R 6 / E 48 / P 96 with the
+# residual, and R 1 / E 16 (too few rounds: the row split instead)
+ORDERED = [(7889, 49152, 4096, ee.EPI_BIAS_GELU), (4205, 9216, 4096, ee.EPI_BIAS),
+           (4205, 12288, 4096, ee.EPI_BIAS_RESIDUAL), (8436, 12288, 4096, ee.EPI_BIAS_RESIDUAL),
+           (4205, 12288, 49152, ee.EPI_BIAS_RESIDUAL), (4300, 4096, 512, ee.EPI_NONE)]
+
+
+@pytest.fixture(scope="module")
+def linear_ws():
+    return torch.empty(ee.ee_linear_ws_workspace_size(), dtype=torch.uint8, device=DEV)
+
+
+@pytest.mark.parametrize("M,N,K,epi", ORDERED)
+def test_gemm_ordered_split_bit_identical(M, N, K, epi, linear_ws):
+    """The partial last round as in-order stream-K pieces (ee_linear_ws) gives
+    ee_linear's bits on random data, twice in a row with the workspace's
+    flags from the first call in place (each launch has its own tag), and
+    after the workspace is filled with random bytes."""
+    gen = torch.Generator(device="cpu").manual_seed(M + N + K)
+    A = torch.randn(M, K, generator=gen).half().to(DEV)
+    W = (0.05 * torch.randn(N, K, generator=gen)).half().to(DEV)
+    bias = (0.1 * torch.randn(N, generator=gen)).half().to(DEV) if epi != ee.EPI_NONE else None
+    R = torch.randn(M, N, generator=gen).half().to(DEV) if epi == ee.EPI_BIAS_RESIDUAL else None
+    ref = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    ee.ee_linear(A, W, bias, R, epi, ref)
+    for rep in range(3):
+        if rep == 2:
+            linear_ws.copy_(torch.randint(0, 256, linear_ws.shape, dtype=torch.uint8, generator=gen).to(DEV))
+        C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        ee.ee_linear_ws(A, W, bias, R, epi, C, linear_ws)
+        torch.cuda.synchronize()
+        diff = (C.view(torch.int16) != ref.view(torch.int16)).any(dim=1).nonzero().flatten().tolist()
+        say(f"ordered split {M}x{N}x{K} epi={epi} call {rep}: {len(diff)} rows differ from ee_linear")
+        assert not diff, f"rows {diff[:8]}... differ"
+
+
+def test_profile_splits_a_site_by_kernel(linear_ws):
+    """A GEMM site whose launches ran the plain and the in-order split form of
+    the large kernel (8192 rows: whole rounds; 7889 rows: 64 extra tiles) is
+    reported per kernel: by_kernel holds both labels with their launches and
+    flops, and the site's kernel reads "several kernels"."""
+    N, K = 49152, 4096
+    W = (0.05 * torch.randn(N, K, generator=GEN)).half().to(DEV)
+    bias = torch.zeros(N, dtype=torch.float16, device=DEV)
+    ee.ee_profile_enable(True)
+    try:
+        for M in (8192, 7889):
+            A = torch.randn(M, K, generator=GEN).half().to(DEV)
+            C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+            ee.ee_linear_ws(A, W, bias, None, ee.EPI_BIAS_GELU, C, linear_ws)
+        st = ee.ee_profile_collect()["linear"]
+    finally:
+        ee.ee_profile_enable(False)
+    plain = "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 2, false>"
+    split = "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 2, true>"
+    assert st["launches"] == 2 and st["kernel"] == "several kernels"
+    assert set(st["by_kernel"]) == {plain, split}
+    assert st["by_kernel"][plain]["flops"] == 2.0 * 8192 * N * K
+    assert st["by_kernel"][split]["flops"] == 2.0 * 7889 * N * K
+
+
+@pytest.mark.parametrize("M,N,K", [(7889, 49152, 4096), (4205, 12288, 4096)])
+def test_gemm_ordered_split_integer_exact(M, N, K, linear_ws):
+    """Small-integer operands through ee_linear_ws: two rows of every 256-row
+    tile, over all N, are the fp16 rounding of the exact sum, bit for bit."""
+    A, W = _small_ints((M, K)), _small_ints((N, K))
+    bias = _small_ints((N,))
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    ee.ee_linear_ws(A.to(DEV), W.to(DEV), bias.to(DEV), None, ee.EPI_BIAS, C, linear_ws)
+    torch.cuda.synchronize()
+    rows = sorted({r for t in range(0, M, 256) for r in (t, min(M, t + 256) - 1)})
+    exact = A[rows].double().numpy() @ W.double().numpy().T + bias.double().numpy()
+    got = C[rows].cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
+
+
 @pytest.mark.parametrize("K", [32768, 49152 + 64])
 def test_gemm_integer_exact_long_k(K):
     """Long K ranges (>= 32768) take the three-W-stage ring of the 256 x 256 tile
@@ -232,8 +312,8 @@ def test_gemm_integer_exact_long_k(K):
     assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
 
 
-@pytest.mark.parametrize("M,rest_kernel", [(4205, "gemm_f16_mfma_kernel<32, 128, 64, 2, 2, 2, 2>"),
-                                           (8457, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 2, 2>")])
+@pytest.mark.parametrize("M,rest_kernel", [(4205, "gemm_f16_mfma_kernel<32, 128, 64, 2, 2, 2, 2, false>"),
+                                           (8457, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 2, 2, false>")])
 def test_gemm_integer_exact_row_split_long_k(M, rest_kernel):
     """The FC2 shape of the layer (N = 12288, K = 49152, A and W rows at the
     preferred 49216-element pitch) at row counts whose 256 x 256 tile count is
@@ -260,7 +340,7 @@ def test_gemm_integer_exact_row_split_long_k(M, rest_kernel):
         ee.ee_profile_enable(False)
     torch.cuda.synchronize()
     m_big = M // 256 * 256 if M == 4205 else 8192
-    assert st["linear"]["kernel"] == "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3>"
+    assert st["linear"]["kernel"] == "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3, false>"
     assert st["linear_rest"]["kernel"] == rest_kernel
     assert st["linear"]["flops"] == 2.0 * m_big * N * K and st["linear_rest"]["flops"] == 2.0 * (M - m_big) * N * K
     rows = [0, 1, 255, m_big - 1, m_big, m_big + 1, (m_big + M) // 2, M - 1]

@@ -15,7 +15,8 @@ __all__ = [
     "EEError", "lib", "F32", "F16", "GELU_TANH", "GELU_ERF",
     "EPI_NONE", "EPI_BIAS", "EPI_BIAS_RESIDUAL", "EPI_BIAS_GELU",
     "ee_compute_offsets", "ee_compute_offsets_mask", "ee_padding_workspace_size",
-    "ee_remove_padding", "ee_rebuild_padding", "ee_layernorm", "ee_linear", "ee_bias_gelu",
+    "ee_remove_padding", "ee_rebuild_padding", "ee_layernorm", "ee_linear", "ee_linear_ws",
+    "ee_linear_ws_workspace_size", "ee_bias_gelu",
     "ee_linear_splitk", "ee_linear_splitk_workspace_size", "ee_linear_streamk", "ee_linear_streamk_workspace_size",
     "ee_attention_varlen", "ee_attention_padded", "ee_transpose_padding_rebuild_heads",
     "ee_transpose_padding_remove_heads", "ee_add_bias_residual_layernorm",
@@ -115,6 +116,9 @@ _SIGS = {
     "ee_linear": (C.c_int, [_VP, _VP, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP, _VP]),
     "ee_linear_strided": (C.c_int, [_VP, _I64, _VP, _I64, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP,
                                     _I64, _VP]),
+    "ee_linear_ws_workspace_size": (_SZ, []),
+    "ee_linear_ws": (C.c_int, [_VP, _I64, _VP, _I64, _VP, _VP, _I64, _I32, _I32, C.c_int, C.c_int, C.c_int, _VP,
+                               _I64, _VP, _SZ, _VP]),
     "ee_preferred_row_pitch": (_I64, [_I64, C.c_int]),
     "ee_bias_gelu": (C.c_int, [_VP, _VP, _I64, _I32, C.c_int, C.c_int, _VP, _VP]),
     "ee_linear_splitk_workspace_size": (C.c_int, [_I64, _I32, _I32, C.POINTER(_SZ)]),
@@ -366,6 +370,25 @@ def ee_linear(A, W, bias, residual, epi: int, C_out, gelu: int = GELU_TANH, stre
     _check(lib().ee_linear_strided(_ptr(A), _row_pitch(A, dense=True), _ptr(W), _row_pitch(W, dense=True), _ptr(bias),
                                    _ptr(residual), M, N, K, _dtype_code(A), epi, gelu, _ptr(C_out), ldc,
                                    _stream(stream)), "ee_linear_strided")
+
+
+def ee_linear_ws_workspace_size() -> int:
+    """Bytes of workspace ee_linear_ws needs."""
+    return int(lib().ee_linear_ws_workspace_size())
+
+
+def ee_linear_ws(A, W, bias, residual, epi: int, C_out, workspace, gelu: int = GELU_TANH, stream=None):
+    """ee_linear with a workspace: a large fp16 problem runs its partial last
+    round of tiles as in-order stream-K pieces (the same bits as ee_linear)."""
+    M, N, K = _linear_args(A, W, bias, residual, epi, C_out, strided=True)
+    _need_workspace(workspace)
+    _need_gpu(workspace=workspace)
+    ldc = _row_pitch(C_out, dense=True)
+    if residual is not None and _row_pitch(residual, dense=True) != ldc:
+        raise ValueError("residual and C_out must share a row pitch")
+    _check(lib().ee_linear_ws(_ptr(A), _row_pitch(A, dense=True), _ptr(W), _row_pitch(W, dense=True), _ptr(bias),
+                              _ptr(residual), M, N, K, _dtype_code(A), epi, gelu, _ptr(C_out), ldc, _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream)), "ee_linear_ws")
 
 
 def ee_preferred_row_pitch(cols: int, dtype: int = F16) -> int:
@@ -670,13 +693,24 @@ def ee_profile_filter(site: Optional[str] = None):
 
 
 def ee_profile_collect() -> Dict[str, Dict[str, float]]:
-    cap = 64
+    """Per launch site: launches, total_ms, flops, the kernel label ("several
+    kernels" if its launches ran more than one) and by_kernel, the same
+    totals for each kernel label."""
+    cap = 128
     arr = (KernelStat * cap)()
     n = C.c_int32(0)
     _check(lib().ee_profile_collect(arr, cap, C.byref(n)), "ee_profile_collect")
-    return {arr[i].name.decode(): {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms),
-                                   "flops": float(arr[i].flops), "kernel": arr[i].kernel.decode()}
-            for i in range(n.value)}
+    out: Dict[str, Dict] = {}
+    for i in range(n.value):
+        name, kern = arr[i].name.decode(), arr[i].kernel.decode()
+        row = {"launches": int(arr[i].launches), "total_ms": float(arr[i].total_ms), "flops": float(arr[i].flops)}
+        site = out.setdefault(name, {"launches": 0, "total_ms": 0.0, "flops": 0.0, "kernel": kern, "by_kernel": {}})
+        for k in ("launches", "total_ms", "flops"):
+            site[k] += row[k]
+        if site["kernel"] != kern:
+            site["kernel"] = "several kernels"
+        site["by_kernel"][kern] = row
+    return out
 
 
 # ---------------------------------------------------------------- batch planning (host only)

@@ -233,7 +233,8 @@ bool desc_equal(const ee_layer_desc& a, const ee_layer_desc& b) {
 
 // ---------------------------------------------------------------- workspace
 struct Plan {
-  size_t cu, token_src, pad2pack, x, ln, big, o, h, heads, o_heads, splitk, splitk_bytes, total;
+  size_t cu, token_src, pad2pack, x, ln, big, o, h, heads, o_heads, splitk, splitk_bytes, ordered, ordered_bytes,
+      total;
 };
 
 // Whether the pre-LN residuals are added in a separate pass (EE_RESIDUAL_AUTO: in the epilogue).
@@ -278,6 +279,10 @@ Plan plan_layer(const ee_layer_desc& d, int32_t B, int32_t P, int64_t T) {
     p.heads = take(3 * pad_rows * Hp * s);
     p.o_heads = take(pad_rows * Hp * s);
   }
+  if (d.dtype == EE_F16) {  // the large GEMMs' in-order stream-K pieces
+    p.ordered_bytes = gemm_f16_ordered_bytes();
+    p.ordered = take(p.ordered_bytes);
+  }
   p.total = off;
   return p;
 }
@@ -288,11 +293,14 @@ char* at(void* ws, size_t off) { return static_cast<char*>(ws) + off; }
 // One GEMM launch site.  With a scratch buffer (extend steps), small-M
 // problems run stream-K or split-K (two kernels, timed as one launch of
 // `site`).  The dense fp16 path runs as one or two parts (gemm_f16_parts):
-// the first is timed as `site`, a remainder of rows as `rest_site`.  Each
-// launch records its algorithmic flops, 2*rows*N*K.
+// the first is timed as `site`, a remainder of rows as `rest_site`; with
+// `ordered` scratch a large problem is one part whose partial last round
+// runs as in-order stream-K pieces (the same bits).  Each launch records its
+// algorithmic flops, 2*rows*N*K.
 ee_status gemm_site(const char* site, const char* rest_site, ee_dtype dt, const void* A, const void* W,
                     const void* bias, const void* R, int64_t M, int N, int K, const GemmPitch& ld, ee_epilogue epi,
-                    ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr, size_t scratch_bytes = 0) {
+                    ee_gelu g, void* C, hipStream_t s, void* scratch = nullptr, size_t scratch_bytes = 0,
+                    void* ordered = nullptr, size_t ordered_bytes = 0) {
   const double flops = 2.0 * (double)M * N * K;
   if (dt == EE_F16 && gemm_f16_mfma_ok(M, N, K, ld, A, W)) {
     if (scratch) {
@@ -308,16 +316,19 @@ ee_status gemm_site(const char* site, const char* rest_site, ee_dtype dt, const 
     if (splits > 1) {
       const hipError_t e = timed(
           site, s, [&]() { return launch_gemm_f16_splitk(A, W, bias, R, M, N, K, ld, epi, g, C, splits, scratch, s); },
-          flops, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 4, 2> + splitk_reduce_kernel");
+          flops, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 4, 2, false> + splitk_reduce_kernel");
       return e == hipSuccess ? EE_OK : hip_fail(e, site);
     }
     GemmPart parts[2];
-    const int n = gemm_f16_parts(M, N, K, parts);
+    const bool vec_stores = N % 8 == 0 && ld.c % 8 == 0 && aligned16(C) && (!R || aligned16(R));
+    const int n = gemm_f16_parts(M, N, K, parts, ordered ? ordered_bytes : 0, vec_stores);
     for (int i = 0; i < n; ++i) {
       const char* at_site = i == 0 ? site : rest_site;
       const hipError_t e = timed(
-          at_site, s, [&]() { return launch_gemm_f16_part(parts[i], A, W, bias, R, N, K, ld, epi, g, C, s); },
-          2.0 * (double)parts[i].rows * N * K, gemm_f16_kernel_label(parts[i].cfg, epi));
+          at_site, s,
+          [&]() { return launch_gemm_f16_part(parts[i], A, W, bias, R, N, K, ld, epi, g, C, s, ordered, ordered_bytes); },
+          2.0 * (double)parts[i].rows * N * K,
+          gemm_f16_kernel_label(parts[i].cfg, epi, parts[i].ordered));
       if (e != hipSuccess) return hip_fail(e, at_site);
     }
     return EE_OK;
@@ -374,45 +385,49 @@ ee_status packed_layer(const ee_layer* L, void* ws, const Plan& p, int64_t T, hi
   void* h = at(ws, p.h);
   void* sk = p.splitk_bytes ? at(ws, p.splitk) : nullptr;
   const size_t skb = p.splitk_bytes;
+  // in-order stream-K scratch: its own region in a forward, the (sequentially
+  // reused) partial-sum region in an extend step
+  void* ord = p.ordered_bytes ? at(ws, p.ordered) : sk;
+  const size_t ordb = p.ordered_bytes ? p.ordered_bytes : skb;
   // A [T, .] . W^T: activations dense except the FC1 output (pitch ld_big)
   const GemmPitch ld_qkv{H, (int)w.ld_qkv, 3 * Hp}, ld_out{Hp, (int)w.ld_out, H};
   const GemmPitch ld_fc1{H, (int)w.ld_fc1, L->ld_big}, ld_fc2{L->ld_big, (int)w.ld_fc2, H};
   auto fc1 = [&](const void* in) -> ee_status {
     if (d.fuse_gelu) {
-      EE_GEMM("gemm_fc1", d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, ld_fc1, EE_EPI_BIAS_GELU, d.gelu, big, s, sk, skb);
+      EE_GEMM("gemm_fc1", d.dtype, in, w.w_fc1, w.b_fc1, nullptr, T, F, H, ld_fc1, EE_EPI_BIAS_GELU, d.gelu, big, s, sk, skb, ord, ordb);
     } else {
-      EE_GEMM("gemm_fc1", d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, ld_fc1, EE_EPI_NONE, d.gelu, big, s, sk, skb);
+      EE_GEMM("gemm_fc1", d.dtype, in, w.w_fc1, nullptr, nullptr, T, F, H, ld_fc1, EE_EPI_NONE, d.gelu, big, s, sk, skb, ord, ordb);
       EE_LAUNCH("bias_gelu", s, launch_bias_gelu(d.dtype, big, w.b_fc1, T, F, L->ld_big, d.gelu, big, s));
     }
     return EE_OK;
   };
   if (d.block == EE_BLOCK_GPT_PRELN) {
     EE_LAUNCH("ln1", s, launch_layernorm(d.dtype, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, ln, s));
-    EE_GEMM("gemm_qkv", d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb);
+    EE_GEMM("gemm_qkv", d.dtype, ln, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb, ord, ordb);
     EE_TRY(attn(big, o, true));
     if (residual_pass(d)) {
       // h = (o W_out^T + b_out) + x and ln = LN2(h); x = (g W_fc2^T + b_fc2) + h
-      EE_GEMM("gemm_out", d.dtype, o, w.w_out, w.b_out, nullptr, T, H, Hp, ld_out, EE_EPI_BIAS, d.gelu, h, s, sk, skb);
+      EE_GEMM("gemm_out", d.dtype, o, w.w_out, w.b_out, nullptr, T, H, Hp, ld_out, EE_EPI_BIAS, d.gelu, h, s, sk, skb, ord, ordb);
       EE_LAUNCH("res_ln2", s, launch_residual_add_layernorm(d.dtype, h, x, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
       EE_TRY(fc1(ln));
-      EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, w.b_fc2, nullptr, T, H, F, ld_fc2, EE_EPI_BIAS, d.gelu, x, s, sk, skb);
+      EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, w.b_fc2, nullptr, T, H, F, ld_fc2, EE_EPI_BIAS, d.gelu, x, s, sk, skb, ord, ordb);
       EE_LAUNCH("res_add", s, launch_residual_add_layernorm(d.dtype, x, h, x, nullptr, nullptr, T, H, 0.f, nullptr, s));
       return EE_OK;
     }
-    EE_GEMM("gemm_out", d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, ld_out, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb);
+    EE_GEMM("gemm_out", d.dtype, o, w.w_out, w.b_out, x, T, H, Hp, ld_out, EE_EPI_BIAS_RESIDUAL, d.gelu, h, s, sk, skb, ord, ordb);
     EE_LAUNCH("ln2", s, launch_layernorm(d.dtype, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, ln, s));
     EE_TRY(fc1(ln));
-    EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, ld_fc2, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s, sk, skb);
+    EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, w.b_fc2, h, T, H, F, ld_fc2, EE_EPI_BIAS_RESIDUAL, d.gelu, x, s, sk, skb, ord, ordb);
     return EE_OK;
   }
   // post-LN encoder: GEMM, then bias + residual + LayerNorm in one pass
-  EE_GEMM("gemm_qkv", d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb);
+  EE_GEMM("gemm_qkv", d.dtype, x, w.w_qkv, w.b_qkv, nullptr, T, 3 * Hp, H, ld_qkv, EE_EPI_BIAS, d.gelu, big, s, sk, skb, ord, ordb);
   EE_TRY(attn(big, o, false));
-  EE_GEMM("gemm_out", d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, ld_out, EE_EPI_NONE, d.gelu, ln, s, sk, skb);
+  EE_GEMM("gemm_out", d.dtype, o, w.w_out, nullptr, nullptr, T, H, Hp, ld_out, EE_EPI_NONE, d.gelu, ln, s, sk, skb, ord, ordb);
   EE_LAUNCH("add_ln1", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_out, x, w.ln1_g, w.ln1_b, T, H, d.ln_eps, h, s));
   EE_TRY(fc1(h));
-  EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, ld_fc2, EE_EPI_NONE, d.gelu, ln, s, sk, skb);
+  EE_GEMM("gemm_fc2", d.dtype, big, w.w_fc2, nullptr, nullptr, T, H, F, ld_fc2, EE_EPI_NONE, d.gelu, ln, s, sk, skb, ord, ordb);
   EE_LAUNCH("add_ln2", s,
             launch_add_bias_residual_layernorm(d.dtype, ln, w.b_fc2, h, w.ln2_g, w.ln2_b, T, H, d.ln_eps, x, s));
   return EE_OK;
@@ -815,7 +830,8 @@ ee_status ee_layernorm(const void* x, const void* gamma, const void* beta, int64
 // ee_linear_strided with the enum arguments as the ints the caller passed
 static ee_status linear_strided(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
                                 const void* residual, int64_t M, int32_t N, int32_t K, int dtype_i, int epi_i,
-                                int gelu_i, void* C, int64_t ldc, void* stream) {
+                                int gelu_i, void* C, int64_t ldc, void* stream, void* ws = nullptr,
+                                size_t ws_bytes = 0) {
   if (!dtype_ok(dtype_i)) return fail(EE_ERR_INVALID_ARG, "unknown dtype %d", dtype_i);
   if (!epilogue_ok(epi_i)) return fail(EE_ERR_INVALID_ARG, "unknown epilogue %d", epi_i);
   if (!gelu_ok(gelu_i)) return fail(EE_ERR_INVALID_ARG, "unknown gelu %d", gelu_i);
@@ -839,10 +855,30 @@ static ee_status linear_strided(const void* A, int64_t lda, const void* W, int64
       (epi != EE_EPI_NONE && overlap(C, nc, bias, (size_t)N * s)) ||
       (epi == EE_EPI_BIAS_RESIDUAL && overlap(C, nc, residual, nc)))
     return fail(EE_ERR_INVALID_ARG, "C overlaps an input");
+  if (ws) {
+    const size_t na = span(M, K, lda, s), nw = span(N, K, ldw, s);
+    if (overlap(ws, ws_bytes, A, na) || overlap(ws, ws_bytes, W, nw) || overlap(ws, ws_bytes, C, nc) ||
+        (epi != EE_EPI_NONE && overlap(ws, ws_bytes, bias, (size_t)N * s)) ||
+        (epi == EE_EPI_BIAS_RESIDUAL && overlap(ws, ws_bytes, residual, nc)))
+      return fail(EE_ERR_INVALID_ARG, "the workspace overlaps an operand");
+  }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const GemmPitch ld{(int)lda, (int)ldw, (int)ldc};
-  EE_GEMM("linear", dtype, A, W, bias, residual, M, N, K, ld, epi, gelu, C, st);
+  EE_TRY(gemm_site("linear", "linear_rest", dtype, A, W, bias, residual, M, N, K, ld, epi, gelu, C, st, nullptr, 0,
+                   ws, ws_bytes));
   return EE_OK;
+}
+
+size_t ee_linear_ws_workspace_size(void) { return gemm_f16_ordered_bytes(); }
+
+ee_status ee_linear_ws(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
+                       const void* residual, int64_t M, int32_t N, int32_t K, ee_dtype dtype, ee_epilogue epi,
+                       ee_gelu gelu, void* C, int64_t ldc, void* ws, size_t ws_bytes, void* stream) {
+  EE_TRY(check_ptr(ws, "workspace"));
+  if (ws_bytes < gemm_f16_ordered_bytes())
+    return fail(EE_ERR_WORKSPACE, "workspace of %zu bytes, need %zu", ws_bytes, gemm_f16_ordered_bytes());
+  return linear_strided(A, lda, W, ldw, bias, residual, M, N, K, ev(dtype), ev(epi), ev(gelu), C, ldc, stream, ws,
+                        ws_bytes);
 }
 
 ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, int64_t ldw, const void* bias,
@@ -1101,14 +1137,15 @@ ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* cou
   if (!count || (capacity > 0 && !out)) return fail(EE_ERR_INVALID_ARG, "out/count must be non-NULL");
   Profiler& p = prof();
   std::lock_guard<std::mutex> lk(p.mu);
+  // one row per (site, kernel) pair, in the order first seen
   struct Agg {
+    std::string site;
+    const char* kernel = nullptr;
     int64_t launches = 0;
     double ms = 0.0, flops = 0.0;
-    const char* kernel = nullptr;
-    bool several = false;
   };
-  std::vector<std::string> order;
-  std::map<std::string, Agg> agg;
+  std::vector<Agg> rows;
+  std::map<std::pair<std::string, std::string>, size_t> index;
   for (const auto& r : p.recs) {
     const auto& ev = p.pool[r.event];
     hipError_t e = hipEventSynchronize(ev.second);
@@ -1119,30 +1156,27 @@ ee_status ee_profile_collect(ee_kernel_stat* out, int32_t capacity, int32_t* cou
       p.used = 0;
       return hip_fail(e, "profile event");
     }
-    if (!agg.count(r.site)) order.push_back(r.site);
-    Agg& a = agg[r.site];
+    const auto key = std::make_pair(r.site, std::string(r.kernel ? r.kernel : ""));
+    auto it = index.find(key);
+    if (it == index.end()) {
+      it = index.emplace(key, rows.size()).first;
+      rows.push_back(Agg{r.site, r.kernel});
+    }
+    Agg& a = rows[it->second];
     a.launches += 1;
     a.ms += ms;
     a.flops += r.flops;
-    if (r.kernel) {
-      if (a.kernel && std::strcmp(a.kernel, r.kernel) != 0) a.several = true;
-      if (!a.kernel) a.kernel = r.kernel;
-    }
   }
   int32_t n = 0;
-  for (const auto& name : order) {
+  for (const Agg& a : rows) {
     if (n < capacity) {
       ee_kernel_stat& k = out[n];
-      const Agg& a = agg[name];
       std::memset(&k, 0, sizeof k);
-      std::strncpy(k.name, name.c_str(), sizeof k.name - 1);
+      std::strncpy(k.name, a.site.c_str(), sizeof k.name - 1);
       k.launches = a.launches;
       k.total_ms = a.ms;
       k.flops = a.flops;
-      if (a.several)
-        std::strncpy(k.kernel, "several kernels", sizeof k.kernel - 1);
-      else if (a.kernel)
-        std::strncpy(k.kernel, a.kernel, sizeof k.kernel - 1);
+      if (a.kernel) std::strncpy(k.kernel, a.kernel, sizeof k.kernel - 1);
     }
     ++n;
   }

@@ -47,9 +47,13 @@
 //     the same few HBM channels: at K = 49152 (96 KiB rows) this kernel ran
 //     7% slower than with 128 bytes of padding per row of A and W.
 #include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <random>
 #include <type_traits>
 
 #include "device_common.h"
+#include "gemm_ordered_split.h"
 #include "gemm_tile_order.h"
 #include "internal.h"
 #include "lds_dma.h"
@@ -78,6 +82,10 @@ namespace {
 #endif
 
 constexpr int kBK = 64;
+// Cache policy bit (sc1) of a buffer access: device scope, so a store is
+// written through to memory and a load is served from it, not from a line
+// this XCD's L2 may hold.
+constexpr int kCacheDevice = 16;
 // Split-K partial store (internal): fp32 sums of one K range, no epilogue.
 constexpr int kEpiPartial = 4;
 template <int EPI>
@@ -126,11 +134,21 @@ struct StagedEpilogue {
   static constexpr int kRowsPerPass = 64 / kLanesPerRow;
 };
 
-template <int MF, int FM, int FN, int EPI>
+//
+// With RAW and a `raw` target, the same path stores the tile's plain fp32
+// sums instead (no bias, GeLU or residual): row-major at a pitch of raw_ld
+// elements from the tile origin (rm0, rn0) over raw_rows rows, written through to memory
+// (device-scope stores) for a workgroup on another XCD.  One consumer of the
+// accumulators for both results: a second store path beside this one made the
+// register allocator spill in the persistent kernel.
+template <int MF, int FM, int FN, int EPI, bool RAW = false>
 __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t (&acc)[FM][FN], float* __restrict__ stage,
                                                   int row0, int col0, int lane, const f16* __restrict__ bias,
                                                   const f16* __restrict__ R, f16* __restrict__ C, int M, int N,
-                                                  int ldc, int gelu_form, float* __restrict__ Pp) {
+                                                  int ldc, int gelu_form, float* __restrict__ Pp,
+                                                  float* __restrict__ raw = nullptr, int raw_rows = 0,
+                                                  int raw_ld = 0, int rm0 = 0, int rn0 = 0) {
+  const bool to_raw = RAW && raw != nullptr;
   using SE = StagedEpilogue<MF, FN>;
   constexpr int FPB = 1;  // fragment rows per band
   constexpr int PASSES = SE::kBandRows / SE::kRowsPerPass;
@@ -149,7 +167,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
       const int row = row0 + band * SE::kBandRows + it * SE::kRowsPerPass + rsub;
-      if (EPI == EE_EPI_BIAS_RESIDUAL && row < M && col < N)
+      if (EPI == EE_EPI_BIAS_RESIDUAL && !to_raw && row < M && col < N)
         rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * ldc + col);
     }
 #pragma unroll
@@ -158,9 +176,10 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int e = 0; e < Frag<MF>::kElems; ++e) {
-          float v = acc[band * FPB + ii][j][e] + bcol[j];
+          const float a = acc[band * FPB + ii][j][e];
+          float v = a + bcol[j];
           if (EPI == EE_EPI_BIAS_GELU) v = gelu_f(v, gelu_form);
-          stage[(ii * MF + Frag<MF>::row(lane, e)) * SE::kLd + j * MF + lane % MF] = v;
+          stage[(ii * MF + Frag<MF>::row(lane, e)) * SE::kLd + j * MF + lane % MF] = to_raw ? a : v;
         }
     __syncthreads();
 #pragma unroll
@@ -169,7 +188,14 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
       const int row = row0 + band * SE::kBandRows + r;
       const float4 lo = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8);
       const float4 hi = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8 + 4);
-      if (EPI == kEpiPartial) {
+      if (to_raw) {
+        // bounded by the tile: a store outside it is dropped
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc(raw, (short)0, raw_rows * raw_ld * 4, kBufferFlags);
+        const int off = ((row - rm0) * raw_ld + (col - rn0)) * 4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), rs, off, 0, kCacheDevice);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), rs, off + 16, 0, kCacheDevice);
+      } else if (EPI == kEpiPartial) {
         if (row < M && col < N) {
           *reinterpret_cast<float4*>(Pp + (int64_t)row * N + col) = lo;
           *reinterpret_cast<float4*>(Pp + (int64_t)row * N + col + 4) = hi;
@@ -216,13 +242,36 @@ __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)
   }
 }
 
-template <int MF, int BM, int BN, int WGM, int WGN, int EPI, int WDEPTH>
+// In-order stream-K of a persistent launch's partial last round.  After
+// `rounds` whole rounds of tiles (tile = blockIdx.x + r * gridDim.x), the
+// `extra` tiles left are cut into `wgs` equal contiguous ranges of their
+// (tile, K tile) steps, one range per workgroup.  A piece that starts inside
+// a tile continues from the fp32 sums that the previous workgroup (whose range
+// ends there) stored in its slot of `partial`, once that workgroup's flag
+// holds this launch's `tag`: every element still adds its K tiles in one
+// chain, in order, so the bits are those of the tile computed whole.  A piece
+// runs after about as many of its workgroup's whole tiles as its first K tile
+// is far into the tile, so its predecessor (an earlier slot) is done by then.
+// extra == 0: whole tiles only (the last round partial).
+struct OrderedSplit {
+  unsigned long long* flags;  // [wgs]; then, kOrderedFlagBytes on, [wgs][BM * BN] fp32 partial tiles
+  unsigned long long tag;     // unique per launch
+  int rounds, extra, wgs;
+};
+constexpr size_t kOrderedFlagBytes = 4096;
+// Polls of a predecessor's flag (about 0.25 us apart) before a piece gives up
+// and recomputes its tile from K tile 0: only if the predecessor never ran,
+// which a launch of at most one workgroup per CU, alone on the device, rules out.
+constexpr int kOrderedSpin = 1 << 16;
+
+template <int MF, int BM, int BN, int WGM, int WGN, int EPI, int WDEPTH, bool ORD>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16* __restrict__ A, int lda,
                                                                  const f16* __restrict__ W, int ldw,
                                                                  const f16* __restrict__ bias,
                                                                  const f16* __restrict__ R, f16* __restrict__ C,
                                                                  int ldc, int M, int N, int K, int gelu_form,
-                                                                 int tiles_m, int tiles_n, float* __restrict__ P) {
+                                                                 int tiles_m, int tiles_n, float* __restrict__ P,
+                                                                 OrderedSplit os) {
   using FR = Frag<MF>;
   using acc_t = typename FR::acc_t;
   constexpr int NW = WGM * WGN;                // waves: WGM x WGN grid over the tile
@@ -244,6 +293,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
 
   // split-K: workgroup row y of the grid sums the y-th of gridDim.y equal K ranges
   const int k_len = K / (int)gridDim.y, kbeg = (int)blockIdx.y * k_len;
+  int kb = kbeg;  // K offset of the current work item's first K tile
   const int n_tiles = tiles_m * tiles_n;
 
   const int t = threadIdx.x;
@@ -282,10 +332,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   auto dma_one = [&](int as, int ka, int ws, int kw, int q) {
     if (q < AJ) {
       f16* sa = smem + a_off(as) + (wave * (BM / NW) + 8 * q) * kBK;
-      buffer_load_lds16(arsrc, sa, aoff[q], (kbeg + ka) * 2);
+      buffer_load_lds16(arsrc, sa, aoff[q], (kb + ka) * 2);
     } else {
       f16* sb = smem + w_off(ws) + (wave * (BN / NW) + 8 * (q - AJ)) * kBK;
-      buffer_load_lds16(wrsrc, sb, boff[q - AJ], (kbeg + kw) * 2);
+      buffer_load_lds16(wrsrc, sb, boff[q - AJ], (kb + kw) * 2);
     }
   };
   auto dma_a = [&](int as, int ka) {
@@ -368,7 +418,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  const int nk = k_len / kBK;
   half8 fa0[FM], fb0[FN], fa1[FM], fb1[FN];
   const std::integral_constant<bool, false> no_dma;
   const std::integral_constant<bool, true> with_dma;
@@ -400,18 +449,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     dma_a(0, 0);
     dma_w(0, 0);
   };
-  int tile = blockIdx.x;
-  if (tile >= n_tiles) return;
-  set_tile(tile);
-  early_loads();
-  for (;;) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int e = 0; e < FR::kElems; ++e) acc[i][j][e] = 0.f;
-    // A0 and W0 are in flight (issued above, or during the previous epilogue)
+  // ---- one tile's (or piece's) K loop over nk K tiles from K offset kb,
+  // after its first K tile's loads (A0, W0) were issued
+  auto k_loop = [&](int nk) {
+    // A0 and W0 are in flight (issued before, or during the previous epilogue)
     dma_a(1, min(1, nk - 1) * kBK);
     if constexpr (WD == 3) dma_w(1, min(1, nk - 1) * kBK);
     dma_w(WD - 1, min(WD - 1, nk - 1) * kBK);
@@ -437,26 +478,159 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     steps_before_barrier(ca, cw);
     mfmas(fa1, fb1);
     wait_dma();  // no load may still be writing LDS when it is reused or the workgroup retires
-
-    const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
-    const int next = tile + (int)gridDim.x;
-    __syncthreads();  // every wave is done reading the ring
-    if (kOverlap && next < n_tiles) {
-      set_tile(next);
-      early_loads();
-    }
+  };
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int e = 0; e < FR::kElems; ++e) acc[i][j][e] = 0.f;
+  };
+  auto epilogue = [&](int row0, int col0) {
     float* const Pp = P + (int64_t)blockIdx.y * M * N;
     if (vec_ok)
       store_tile_staged<MF, FM, FN, EPI>(acc, stage_base + wave * SE::kFloats, row0, col0, lane, bias, R, C, M, N,
                                          ldc, gelu_form, Pp);
     else
       store_tile<MF, FM, FN, EPI>(acc, row0, col0, lane, bias, R, C, M, N, ldc, gelu_form, Pp);
-    if (next >= n_tiles) break;
-    tile = next;
-    __syncthreads();  // every wave's staging is done before the ring is loaded again
-    if (!kOverlap) {
-      set_tile(tile);
-      early_loads();
+  };
+
+  if constexpr (!ORD) {
+    // ---- whole tiles: blockIdx.x, then every gridDim.x-th
+    int tile = blockIdx.x;
+    if (tile >= n_tiles) return;
+    set_tile(tile);
+    early_loads();
+    for (;;) {
+      zero_acc();
+      k_loop(k_len / kBK);
+      const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
+      const int next = tile + (int)gridDim.x;
+      __syncthreads();  // every wave is done reading the ring
+      if (kOverlap && next < n_tiles) {
+        set_tile(next);
+        early_loads();
+      }
+      epilogue(row0, col0);
+      if (next >= n_tiles) break;
+      tile = next;
+      __syncthreads();  // every wave's staging is done before the ring is loaded again
+      if (!kOverlap) {
+        set_tile(tile);
+        early_loads();
+      }
+    }
+  } else {
+    // ---- in-order stream-K (gemm_ordered_split.h): whole tiles, and up to
+    // two pieces of this workgroup's K range over the extra tiles.  The sums
+    // a piece leaves, and the flag that publishes them, move by device-scope
+    // coherent accesses (sc1: written through to memory, read past this XCD's
+    // L2) ordered by waiting for the stores' completion, instead of fences,
+    // which write back or invalidate the whole L2 of the XCD.
+    const int b = blockIdx.x, G = gridDim.x, KT = k_len / kBK;
+    // Item c, and the item count, recomputed where needed from the split's
+    // three numbers: the register allocator is at its limit here, and values
+    // kept live across the K loop would spill.  The empty asm hides the
+    // inputs' provenance, so the computation stays where it is written.
+    struct ItemAt {
+      OrderedItem it;
+      int n;
+    };
+    auto item_at = [&](int c) {
+      int rounds = os.rounds, extra = os.extra, wgs = os.wgs;
+      asm volatile("" : "+s"(rounds), "+s"(extra), "+s"(wgs));
+      const OrderedWork w = ordered_work(b, G, n_tiles, KT, rounds, extra, wgs);
+      return ItemAt{ordered_item(w, b, G, KT, c), ordered_items(w)};
+    };
+    const ItemAt first = item_at(0);
+    if (first.n == 0) return;
+    int c = 0;
+    OrderedItem it = first.it;
+    set_tile(it.tile);
+    kb = kbeg + it.k0 * kBK;
+    early_loads();
+    for (;;) {
+      zero_acc();
+      if (it.pred >= 0) {
+        // thread 0 polls the predecessor's flag; then every wave reads its sums
+        int* const note = reinterpret_cast<int*>(smem + a_off(1));  // stage 1: not loaded yet
+        if (t == 0) {
+          int ok = 0;
+          for (int n = 0; n < kOrderedSpin; ++n) {
+            if (__hip_atomic_load(os.flags + it.pred, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == os.tag) {
+              ok = 1;
+              break;
+            }
+            __builtin_amdgcn_s_sleep(8);
+          }
+          *note = ok;
+        }
+        __syncthreads();
+        const int ok = __builtin_amdgcn_readfirstlane(*note);
+        __syncthreads();  // every wave has read `note` before stage 1 is loaded
+        if (ok) {
+          // the predecessor's sums, row-major in the tile (store_tile_staged's raw form)
+          const __amdgpu_buffer_rsrc_t src = __builtin_amdgcn_make_buffer_rsrc(
+              reinterpret_cast<char*>(os.flags) + kOrderedFlagBytes + (size_t)it.pred * BM * BN * 4, (short)0,
+              BM * BN * 4, kBufferFlags);
+          const int voff = ((wm * WTM + FR::row(lane, 0)) * BN + wn * WTN + lane % MF) * 4;
+#pragma unroll
+          for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+#pragma unroll
+              for (int e = 0; e < FR::kElems; ++e)
+                acc[i][j][e] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                               src, voff, ((i * MF + FR::row(0, e) - FR::row(0, 0)) * BN + j * MF) * 4, kCacheDevice));
+        } else {
+          // never published: compute the tile from its first K tile instead
+          wait_dma();
+          __syncthreads();
+          it.k0 = 0;
+          kb = kbeg;
+          early_loads();
+        }
+      }
+      k_loop(it.k1 - it.k0);
+      const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
+      const int tile_m0 = m0, tile_n0 = n0;  // set_tile below moves m0, n0 to the next item
+      const ItemAt nxa = item_at(c + 1);
+      const bool more = c + 1 < nxa.n;
+      const OrderedItem nx = nxa.it;
+      __syncthreads();  // every wave is done reading the ring
+      if (kOverlap && more) {
+        set_tile(nx.tile);
+        kb = kbeg + nx.k0 * kBK;
+        early_loads();
+      }
+      // a piece that ends inside its tile leaves its sums for workgroup b + 1
+      // (raw fp32, row-major in the tile), through the same staged store
+      float* const raw = it.partial ? reinterpret_cast<float*>(reinterpret_cast<char*>(os.flags) + kOrderedFlagBytes) +
+                                          (size_t)b * BM * BN
+                                    : nullptr;
+      if (vec_ok) {
+        float* const Pp = P + (int64_t)blockIdx.y * M * N;
+        store_tile_staged<MF, FM, FN, EPI, true>(acc, stage_base + wave * SE::kFloats, row0, col0, lane, bias, R, C,
+                                                 M, N, ldc, gelu_form, Pp, raw, BM, BN, tile_m0, tile_n0);
+      } else {
+        epilogue(row0, col0);  // never with a partial piece: the host splits only where vec_ok holds
+      }
+      if (it.partial) {
+        wait_dma();       // this wave's written-through stores have completed
+        __syncthreads();  // ... and every other wave's
+        if (t == 0) __hip_atomic_store(os.flags + b, os.tag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      if (!more) break;
+      it = nx;
+      ++c;
+      __syncthreads();  // every wave's staging is done before the ring is loaded again
+      if (!kOverlap) {
+        set_tile(it.tile);
+        kb = kbeg + it.k0 * kBK;
+        early_loads();
+      }
     }
   }
 }
@@ -465,7 +639,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
 template <int MF, int BM, int BN, int WGM, int WGN, int WDEPTH = 2>
 hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void* R, int M, int N, int K,
                       const GemmPitch& ld, int epi, ee_gelu form, void* C, int splits, float* P, hipStream_t s,
-                      int max_wgs = 0) {
+                      int max_wgs = 0, const OrderedSplit& os = OrderedSplit{}) {
   const int tm = (M + BM - 1) / BM, tn = (N + BN - 1) / BN;
   const int wgs = max_wgs > 0 ? std::min(tm * tn, max_wgs) : tm * tn;
   const dim3 grid((unsigned)wgs, (unsigned)splits), block(64 * WGM * WGN);
@@ -474,15 +648,24 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
   const f16* b = static_cast<const f16*>(bias);
   const f16* r = static_cast<const f16*>(R);
   f16* c = static_cast<f16*>(C);
-#define EE_GEMM_LAUNCH(E)                                                                                        \
-  hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E, WDEPTH>), grid, block, 0, s, a, ld.a, w, ld.w, b, r, \
-                     c, ld.c, M, N, K, (int)form, tm, tn, P)
+  // the in-order stream-K form exists for the persistent 256 x 256 tiles only
+  constexpr bool kCanOrder = BM == 256 && BN == 256;
+#define EE_GEMM_LAUNCH(E)                                                                                       \
+  if (kCanOrder && os.extra > 0)                                                                                \
+    hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E, WDEPTH, kCanOrder>), grid, block, 0, s, a, \
+                       ld.a, w, ld.w, b, r, c, ld.c, M, N, K, (int)form, tm, tn, P, os);                         \
+  else                                                                                                          \
+    hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E, WDEPTH, false>), grid, block, 0, s, a, ld.a, w, \
+                       ld.w, b, r, c, ld.c, M, N, K, (int)form, tm, tn, P, os)
   switch (epi) {
     case EE_EPI_NONE: EE_GEMM_LAUNCH(EE_EPI_NONE); break;
     case EE_EPI_BIAS: EE_GEMM_LAUNCH(EE_EPI_BIAS); break;
     case EE_EPI_BIAS_RESIDUAL: EE_GEMM_LAUNCH(EE_EPI_BIAS_RESIDUAL); break;
     case EE_EPI_BIAS_GELU: EE_GEMM_LAUNCH(EE_EPI_BIAS_GELU); break;
-    case kEpiPartial: EE_GEMM_LAUNCH(kEpiPartial); break;
+    case kEpiPartial:  // split-K partial sums: never with an ordered split
+      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, kEpiPartial, WDEPTH, false>), grid, block, 0, s, a,
+                         ld.a, w, ld.w, b, r, c, ld.c, M, N, K, (int)form, tm, tn, P, os);
+      break;
   }
 #undef EE_GEMM_LAUNCH
   return hipGetLastError();
@@ -578,28 +761,87 @@ int64_t gemm_big_rows(int64_t M, int N, int cus) {
   return t_split < t_plain ? m_tiles * 256 : M;
 }
 
-int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[2]) {
+namespace {
+// In-order stream-K scratch: the flags, then one partial 256 x 256 tile per
+// workgroup that takes part.
+constexpr int kOrderedMaxWgs = 256;
+constexpr size_t kOrderedTileBytes = (size_t)256 * 256 * 4;
+// The fewest K tiles in a piece (2048 of K): a shorter one spends much of its
+// time on its prologue and on storing or loading partial sums (the TP-shard
+// out projection, K = 3072, ran 5% slower split into pieces of 18 K tiles).
+constexpr int kOrderedMinPiece = 32;
+
+// A tag no earlier launch of this process used, nor (but with probability
+// 2^-64) one of another process that left flags in the same memory.
+unsigned long long next_ordered_tag() {
+  static std::atomic<unsigned long long> ctr{[] {
+    std::random_device rd;
+    const unsigned long long t = (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count();
+    return (((unsigned long long)rd() << 32) ^ rd() ^ (t * 0x9e3779b97f4a7c15ull));
+  }()};
+  unsigned long long v;
+  do v = ++ctr;
+  while (v == 0);
+  return v;
+}
+
+// The in-order stream-K split of a persistent 256 x 256 launch of `wgs`
+// workgroups, or none (extra == 0) without scratch or where it gains nothing.
+// Its pieces each cover at least 1/rounds of a tile, so two pieces of one
+// tile never share a slot; a workgroup with more than one tile's worth of
+// extra steps would end later than the plain last round.
+int64_t ordered_wgs(int64_t M, int N, int K, int wgs, size_t bytes) {
+  if (bytes < kOrderedFlagBytes + 2 * kOrderedTileBytes || wgs > kOrderedMaxWgs) return 0;
+  const int64_t n_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int slots = (int)std::min<size_t>((bytes - kOrderedFlagBytes) / kOrderedTileBytes, kOrderedMaxWgs);
+  return ordered_split_wgs(n_tiles, wgs, K / kBK, slots, kOrderedMinPiece);
+}
+
+OrderedSplit ordered_split(int64_t M, int N, int K, int wgs, void* scratch, size_t bytes) {
+  OrderedSplit os{};
+  const int64_t p = scratch ? ordered_wgs(M, N, K, wgs, bytes) : 0;
+  if (p == 0) return os;
+  const int64_t n_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t rounds = n_tiles / wgs, extra = n_tiles - rounds * wgs;
+  os.flags = static_cast<unsigned long long*>(scratch);
+  os.tag = next_ordered_tag();
+  os.rounds = (int)rounds;
+  os.extra = (int)extra;
+  os.wgs = (int)p;
+  return os;
+}
+}  // namespace
+
+size_t gemm_f16_ordered_bytes() { return kOrderedFlagBytes + (size_t)kOrderedMaxWgs * kOrderedTileBytes; }
+
+int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[2], size_t ordered_bytes, bool vec_stores) {
   if (M <= 0) return 0;
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
   if (tiles_big < 256) {
-    parts[0] = GemmPart{0, M, kGemm128x128};
+    parts[0] = GemmPart{0, M, kGemm128x128, false};
     return 1;
   }
   const int cus = device_cu_count();
+  const int big = K >= EE_GEMM_DEEP_W_K ? kGemmBig3 : kGemmBig2;
+  if (EE_GEMM_PERSIST && vec_stores &&
+      ordered_wgs(M, N, K, (int)std::min<int64_t>(tiles_big, cus), ordered_bytes) > 0) {
+    parts[0] = GemmPart{0, M, big, true};  // the launch splits its partial last round itself
+    return 1;
+  }
   const int64_t m_big = gemm_big_rows(M, N, cus);
-  parts[0] = GemmPart{0, m_big, K >= EE_GEMM_DEEP_W_K ? kGemmBig3 : kGemmBig2};
+  parts[0] = GemmPart{0, m_big, big, false};
   if (m_big == M) return 1;
   // Few remaining rows stream all of W through few tiles: 128 x 64 tiles
   // (the same MFMA shape) put twice as many CUs on it.
   const int64_t rest = M - m_big;
   const bool narrow = ((rest + 127) / 128) * ((N + 127) / 128) * 2 <= cus;
-  parts[1] = GemmPart{m_big, rest, narrow ? kGemm128x64 : kGemm128x128};
+  parts[1] = GemmPart{m_big, rest, narrow ? kGemm128x64 : kGemm128x128, false};
   return 2;
 }
 
 hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W, const void* bias, const void* R,
                                 int N, int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C,
-                                hipStream_t s) {
+                                hipStream_t s, void* ordered, size_t ordered_bytes) {
   if (p.rows <= 0) return hipSuccess;
   // the part's rows of A, C and the residual
   const f16* a = static_cast<const f16*>(A) + p.row0 * ld.a;
@@ -607,42 +849,53 @@ hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W,
   f16* c = static_cast<f16*>(C) + p.row0 * ld.c;
   const int M = (int)p.rows;
   const int wgs = EE_GEMM_PERSIST ? device_cu_count() : 0;
+  const int64_t tiles = ((int64_t)(M + 255) / 256) * ((N + 255) / 256);
+  const OrderedSplit os = p.ordered && wgs > 0
+                              ? ordered_split(M, N, K, (int)std::min<int64_t>(tiles, wgs), ordered, ordered_bytes)
+                              : OrderedSplit{};
   switch (p.cfg) {
     case kGemmBig2:
       return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1,
-                                                                          nullptr, s, wgs);
+                                                                          nullptr, s, wgs, os);
     case kGemmBig3:
       return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(a, W, bias, r, M, N, K, ld, epi, form, c, 1,
-                                                                          nullptr, s, wgs);
+                                                                          nullptr, s, wgs, os);
     case kGemm128x64: return launch_cfg<32, 128, 64, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
     case kGemm128x128: return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
   }
   return hipErrorInvalidValue;
 }
 
-const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi) {
-  // gemm_f16_mfma_kernel's template arguments <MF, BM, BN, WGM, WGN, EPI, WDEPTH>
+const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi, bool ordered) {
+  // gemm_f16_mfma_kernel's template arguments <MF, BM, BN, WGM, WGN, EPI, WDEPTH, ORD>
   static const char* const labels[4][4] = {
-#define EE_L(cfg) {"gemm_f16_mfma_kernel<" cfg ", 0, 2>", "gemm_f16_mfma_kernel<" cfg ", 1, 2>", \
-                   "gemm_f16_mfma_kernel<" cfg ", 2, 2>", "gemm_f16_mfma_kernel<" cfg ", 3, 2>"}
+#define EE_L(cfg) {"gemm_f16_mfma_kernel<" cfg ", 0, 2, false>", "gemm_f16_mfma_kernel<" cfg ", 1, 2, false>", \
+                   "gemm_f16_mfma_kernel<" cfg ", 2, 2, false>", "gemm_f16_mfma_kernel<" cfg ", 3, 2, false>"}
       EE_L("16, 256, 256, 2, 2"),
-      {"gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 0, 3>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 1, 3>",
-       "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 3>"},
+      {"gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 0, 3, false>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 1, 3, false>",
+       "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3, false>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 3, false>"},
       EE_L("32, 128, 128, 2, 2"),
       EE_L("32, 128, 64, 2, 2"),
 #undef EE_L
   };
+  static const char* const ordered_labels[2][4] = {
+      {"gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 0, 2, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 1, 2, true>",
+       "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 2, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 2, true>"},
+      {"gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 0, 3, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 1, 3, true>",
+       "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 3, true>"},
+  };
   const int e = (int)epi;
   if (cfg < 0 || cfg > 3 || e < 0 || e > 3) return "gemm_f16_mfma_kernel";
-  return labels[cfg][e];
+  return ordered && cfg <= kGemmBig3 ? ordered_labels[cfg][e] : labels[cfg][e];
 }
+
 
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
                                 int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
   GemmPart parts[2];
-  const int n = gemm_f16_parts(M, N, K, parts);
+  const int n = gemm_f16_parts(M, N, K, parts, 0, false);
   for (int i = 0; i < n; ++i) {
-    const hipError_t e = launch_gemm_f16_part(parts[i], A, W, bias, R, N, K, ld, epi, form, C, s);
+    const hipError_t e = launch_gemm_f16_part(parts[i], A, W, bias, R, N, K, ld, epi, form, C, s, nullptr, 0);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

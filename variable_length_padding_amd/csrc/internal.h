@@ -103,19 +103,26 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
 // The launches launch_gemm_f16_mfma makes, for callers that time them one by
 // one: rows [row0, row0 + rows) of the problem on one kernel configuration.
 // A large problem whose 256 x 256 tile count is just past a multiple of the
-// CU count runs whole rounds of 256-row tiles and the remaining rows as a
-// second part on smaller tiles.
+// CU count runs its partial last round as in-order stream-K pieces of the one
+// persistent launch when given `ordered` scratch of gemm_f16_ordered_bytes()
+// (bit-identical to whole tiles); without it, whole rounds of 256-row tiles
+// and the remaining rows as a second part on smaller tiles.
 enum { kGemmBig2 = 0, kGemmBig3 = 1, kGemm128x128 = 2, kGemm128x64 = 3 };
 struct GemmPart {
   int64_t row0, rows;
   int cfg;
+  bool ordered;  // its partial last round as in-order stream-K pieces
 };
-int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[2]);  // number of parts (0 for M <= 0)
+size_t gemm_f16_ordered_bytes();
+// Number of parts (0 for M <= 0).  vec_stores: N and C's pitch are multiples
+// of 8 and C and the residual 16-byte aligned (the ordered form needs it).
+int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[2], size_t ordered_bytes, bool vec_stores);
 hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W, const void* bias, const void* R,
                                 int N, int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C,
-                                hipStream_t s);
-// The kernel template a part runs, as gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EPI, WDEPTH>.
-const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi);
+                                hipStream_t s, void* ordered, size_t ordered_bytes);
+// The kernel template a part runs, as
+// gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, EPI, WDEPTH, ORD>.
+const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi, bool ordered);
 // Split-K for small M: `splits` equal K ranges (K % (64 * splits) == 0) summed
 // into fp32 partials in scratch (gemm_f16_splitk_bytes), then reduced with the
 // epilogue.  gemm_f16_splitk_choice picks the split count (1 = do not split)
