@@ -89,6 +89,37 @@ def test_prefill_decode_and_mixed_steps(name, tol, ctol):
     assert torch.all(tail.view(torch.uint8) == 0xFF)
 
 
+def test_chunked_extend_steps():
+    """Extend steps with many new tokens per sequence after cached ones (a
+    chunked prefill): from 16 new tokens in some sequence on, the attention
+    runs on the MFMA kernel over the cached keys.  Steps of up to 200 new
+    tokens (two 128-query tiles), a sequence with no cache yet beside cached
+    ones, an empty one, and one new token beside 16 and 20; then a decode
+    step on the cache-attention kernel.  Each step against the oracle, and the
+    cache after them."""
+    w = workloads.get("gpt2-small")
+    prompts = [40, 130, 0, 129, 17]
+    plan = [prompts, [17, 200, 33, 130, 0], [1, 16, 0, 3, 20], [1] * 5]
+    extra = [sum(st[b] for st in plan[1:]) for b in range(len(prompts))]
+    dec = Decoder(w, 44, 2, prompts, max_new=max(extra))
+    rows_all = [_token_rows(w, 500 + b, prompts[b] + extra[b]) for b in range(len(prompts))]
+    pos = [0] * len(prompts)
+    for k, new_len in enumerate(plan):
+        rows = torch.cat([rows_all[b][pos[b]:pos[b] + n] for b, n in enumerate(new_len)])
+        got, ref = dec.step(rows, new_len)
+        err = normwise_rel(got, ref)
+        say(f"chunked step {k} new={new_len} after {pos}: rel {err:.3e}")
+        assert np.all(np.isfinite(got)) and err <= 2e-2
+        pos = [p + n for p, n in zip(pos, new_len)]
+    cv = dec.cache_view()
+    for b in range(len(prompts)):
+        n, s0 = dec.ctx[b], dec.slot_base[b]
+        for l in range(2):
+            k = cv[l, 0, :, s0:s0 + n].double().cpu().numpy()
+            v = cv[l, 1, :, s0:s0 + n].double().cpu().numpy()
+            assert normwise_rel(k, dec.ocaches[b].k[l]) <= 2e-3 and normwise_rel(v, dec.ocaches[b].v[l]) <= 2e-3
+
+
 @pytest.mark.parametrize("residual", [ee.RESIDUAL_EPILOGUE, ee.RESIDUAL_PASS])
 def test_prefill_equals_padded_forward_bit_exact(residual):
     w = workloads.get("gpt2-small")

@@ -62,11 +62,15 @@ def test_extend_at_max_batch(name, tol):
     B = ee.MAX_EXTEND_BATCH
     g = torch.Generator().manual_seed(256)
     prompts = torch.randint(1, 9, (B,), generator=g).tolist()
-    dec = Decoder(w, 88, 1, prompts, max_new=1)
-    rows_all = [_token_rows(w, 700 + b, prompts[b] + 1) for b in range(B)]
-    for k, new_len in enumerate([prompts, [1] * B]):
-        start = [0] * B if k == 0 else prompts
-        rows = torch.cat([rows_all[b][start[b]:start[b] + n] for b, n in enumerate(new_len)])
+    # a prefill, a decode step, then 0-3 new tokens per sequence: with 256
+    # sequences that last step fills the GPU on the MFMA kernel
+    third = [b % 4 for b in range(B)]
+    dec = Decoder(w, 88, 1, prompts, max_new=4)
+    rows_all = [_token_rows(w, 700 + b, prompts[b] + 4) for b in range(B)]
+    pos = [0] * B
+    for k, new_len in enumerate([prompts, [1] * B, third]):
+        rows = torch.cat([rows_all[b][pos[b]:pos[b] + n] for b, n in enumerate(new_len)])
+        pos = [p + n for p, n in zip(pos, new_len)]
         got, ref = dec.step(rows, new_len)
         err = normwise_rel(got, ref)
         say(f"{name} extend at B={B}, step {k} (T={sum(new_len)}): rel {err:.3e}")
@@ -106,13 +110,18 @@ def test_attention_rows_past_2gib():
 
 
 @pytest.mark.parametrize("name,prompts,steps", [
-    ("gpt2-small", [40000, 5], [[1, 1], [3, 2]]),     # past 32768 positions: 79 key chunks, then a mixed step
-    ("gpt3-12l", [2000, 1, 700], [[1, 1, 1]]),         # GPT-3 width (96 heads of 128): 4 key chunks
+    # past 32768 positions: 79 key chunks, a mixed step, then 200 and 17 new
+    # tokens on the MFMA kernel over the 40k cached keys
+    ("gpt2-small", [40000, 5], [[1, 1], [3, 2], [200, 17]]),
+    # GPT-3 width (96 heads of 128): 4 key chunks, then 130, 20 and 0 new
+    # tokens on the MFMA kernel
+    ("gpt3-12l", [2000, 1, 700], [[1, 1, 1], [130, 20, 0]]),
 ])
 def test_decode_long_context(name, prompts, steps):
     """One layer: long prompts prefilled on the GPU, then extend steps over the
     long cache.  The cache attention splits the keys into chunks whose softmax
-    states a second kernel merges.  The oracle's cache of a long prompt is its
+    states a second kernel merges; steps with 16 or more new tokens in a
+    sequence run on the MFMA kernel instead.  The oracle's cache of a long prompt is its
     first layer's keys and values (no attention over the prompt is needed for
     them); every step's outputs and both caches are checked against it."""
     w = workloads.get(name)

@@ -22,6 +22,8 @@
 // accumulator layout produced.
 //
 // Any other case (fp32, head_dim 16): a vector-ALU kernel, one query per lane.
+#include <type_traits>
+
 #include "device_common.h"
 #include "attention_limits.h"
 #include "internal.h"
@@ -207,9 +209,23 @@ __device__ __forceinline__ half4 tr_read(const f16* p) {
 #define EE_ATTN_WAVES_PER_SIMD 2
 #endif
 
-template <int HD, bool CAUSAL>
+// The keys and values of an extend step (new tokens after cached ones) come
+// from the packed KV cache: sequence b's keys 0 .. ctx_len[b] + new_len[b] - 1
+// sit at slots slot_base[b] + j of each head's [capacity, hd] block, the new
+// tokens' own keys already appended; its new queries are the packed q rows
+// cu[b] .. cu[b+1] - 1, query i at position ctx_len[b] + i.
+struct NoCache {};
+struct CacheKV {
+  ExtendArg arg;
+  const f16* kc;
+  const f16* vc;
+  int64_t capacity;
+};
+
+template <int HD, bool CAUSAL, class KV = NoCache>
 __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(AttnAddr ad, const int32_t* __restrict__ cu,
-                                                       float scale_log2) {
+                                                       float scale_log2, KV kv = KV{}) {
+  constexpr bool EXT = !std::is_same<KV, NoCache>::value;
   constexpr int KCH = HD / 8;          // 16-byte chunks per key row
   constexpr int RPL = 64 / KCH;        // rows one wave covers per 16-byte access
   constexpr int NLQ = kKB / 4 / RPL;   // accesses per wave per matrix per tile (8 rows per wave)
@@ -221,23 +237,36 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
 
   const int b = blockIdx.y, head = blockIdx.z;
   const int s0 = cu[b];
-  const int L = cu[b + 1] - s0;
+  const int L = cu[b + 1] - s0;  // queries (all the sequence's rows, or its new tokens)
   const int q_start = blockIdx.x * kQB;
   if (q_start >= L) return;  // uniform over the workgroup
   const int64_t in_base = (ad.seq ? (int64_t)s0 * ad.in_row_stride : 0) + b * ad.in_batch_stride + head * ad.in_head_stride;
-  const int ld = (int)ad.in_row_stride;
+  const int ldq = (int)ad.in_row_stride;
   const f16* qb = static_cast<const f16*>(ad.q) + in_base;
+  // keys: the same rows as the queries, or the cached context and then the new tokens
+  int ctx = 0, Lk = L, ld = ldq;
+  const f16* kbase = static_cast<const f16*>(ad.k) + in_base;
+  const f16* vbase = static_cast<const f16*>(ad.v) + in_base;
+  if constexpr (EXT) {
+    ctx = kv.arg.ctx_len[b];
+    Lk = ctx + L;
+    ld = HD;
+    const int64_t kv_off = ((int64_t)head * kv.capacity + kv.arg.slot_base[b]) * HD;
+    kbase = kv.kc + kv_off;
+    vbase = kv.vc + kv_off;
+  }
   const int t = threadIdx.x, lane = t & 63, hk = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int q0 = q_start + wave * 32;
   const int qi = q0 + (lane & 31);
   const int qc = min(qi, L - 1);
+  const int qpos = ctx + qi;  // the query's position: it sees keys 0 .. qpos
 
-  // descriptors over this sequence's rows of k and v (head slice), ending at row L
-  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const f16*>(ad.k) + in_base), (short)0, L * ld * 2, kBufferFlags);
-  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(static_cast<const f16*>(ad.v) + in_base), (short)0, L * ld * 2, kBufferFlags);
+  // descriptors over this sequence's rows of k and v (head slice), ending at row Lk
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, Lk * ld * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, Lk * ld * 2, kBufferFlags);
   // this lane's 16 bytes of each access: tile row r, physical chunk lp, which
   // holds the row's logical chunk lp ^ k_swizzle(r)
   const int lr = lane / KCH, lp = lane % KCH;
@@ -268,7 +297,7 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
 
   half8 qf[NKK];
   {
-    const f16* qrow = qb + (int64_t)qc * ld + hk * 8;
+    const f16* qrow = qb + (int64_t)qc * ldq + hk * 8;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) qf[kk] = *reinterpret_cast<const half8*>(qrow + kk * 16);
   }
@@ -279,8 +308,8 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
     for (int e = 0; e < 16; ++e) oacc[d][e] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int kend = CAUSAL ? min(L, q_start + kQB) : L;
-  const int wave_last_key = CAUSAL ? min(q0 + 31, L - 1) : L - 1;
+  const int kend = CAUSAL ? min(Lk, ctx + q_start + kQB) : Lk;
+  const int wave_last_key = CAUSAL ? min(ctx + q0 + 31, Lk - 1) : Lk - 1;
   const bool wave_active = q0 < L;
   const int kswz = k_swizzle<HD>(lane & 31);
   // transposing-read address of this lane within a V tile, for key slice
@@ -317,7 +346,7 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int key = k0 + (e >> 2) * 8 + hk * 4 + (e & 3);
-        const bool keep = CAUSAL ? key <= qi : key < L;
+        const bool keep = CAUSAL ? key <= qpos : key < Lk;
         const float v = keep ? sacc[e] * scale_log2 : -INFINITY;
         sacc[e] = v;
         mloc = fmaxf(mloc, v);
@@ -493,6 +522,28 @@ hipError_t launch_attention(ee_dtype dt, const void* qkv, const int32_t* cu, int
   const char* base = static_cast<const char*>(qkv);
   const AttnAddr ad{base, base + Hp * es, base + 2 * Hp * es, o, 0, hd, 3 * Hp, 0, hd, Hp, 1};
   return launch_attn(dt, ad, cu, B, max_len, nh, hd, causal, s);
+}
+
+bool cache_attention_mfma_ok(ee_dtype dt, int hd, int64_t max_pos) {
+  // the kernel addresses a sequence's cached rows with 32-bit byte offsets
+  return dt == EE_F16 && (hd == 64 || hd == 128) && attn_tr_offsets_fit(max_pos, hd);
+}
+
+hipError_t launch_cache_attention_mfma(ee_dtype dt, const void* qkv, const ExtendArg& arg, const int32_t* cu, int B,
+                                       int max_new, int nh, int hd, int64_t max_pos, int64_t capacity,
+                                       const void* kc, const void* vc, void* o, hipStream_t s) {
+  if (!cache_attention_mfma_ok(dt, hd, max_pos)) return hipErrorInvalidValue;
+  if (B <= 0 || max_new <= 0) return hipSuccess;
+  const int64_t Hp = (int64_t)nh * hd;
+  const AttnAddr ad{qkv, nullptr, nullptr, o, 0, hd, 3 * Hp, 0, hd, Hp, 1};
+  const CacheKV kv{arg, static_cast<const f16*>(kc), static_cast<const f16*>(vc), capacity};
+  const dim3 grid((unsigned)((max_new + kQB - 1) / kQB), (unsigned)B, (unsigned)nh), block(256);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
+  if (hd == 64)
+    hipLaunchKernelGGL((attn_tr_kernel<64, true, CacheKV>), grid, block, 0, s, ad, cu, scale_log2, kv);
+  else
+    hipLaunchKernelGGL((attn_tr_kernel<128, true, CacheKV>), grid, block, 0, s, ad, cu, scale_log2, kv);
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_padded(ee_dtype dt, const void* q, const void* k, const void* v, const int32_t* cu,

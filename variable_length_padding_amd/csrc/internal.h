@@ -50,6 +50,14 @@ struct ExtendArg {
   int32_t slot_base[EE_MAX_EXTEND_BATCH];
 };
 bool cache_attention_ok(int head_dim);
+// Extend steps with many new tokens per sequence: the MFMA attention kernel
+// (attention.hip) over the cached keys, one workgroup per 128 new queries of a
+// (sequence, head).  fp16, head_dim 64 or 128, positions below the 32-bit
+// offset limit.
+bool cache_attention_mfma_ok(ee_dtype dt, int hd, int64_t max_pos);
+hipError_t launch_cache_attention_mfma(ee_dtype dt, const void* qkv, const ExtendArg& arg, const int32_t* cu, int B,
+                                       int max_new, int nh, int hd, int64_t max_pos, int64_t capacity,
+                                       const void* kc, const void* vc, void* o, hipStream_t s);
 int cache_attention_max_positions();
 hipError_t launch_extend_cu(const ExtendArg& arg, int B, int32_t* cu, hipStream_t s);
 hipError_t launch_append_kv(const void* qkv, const ExtendArg& arg, const int32_t* cu, int B, int64_t T, int nh,
