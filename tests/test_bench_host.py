@@ -11,7 +11,8 @@ import bench
 import variable_length_padding_amd as ee
 
 # every kernel configuration gemm_f16_kernel_label can name: <MF, BM, BN, WGM, WGN> and W depth
-CONFIGS = [("16, 256, 256, 2, 2", 2), ("16, 256, 256, 2, 2", 3), ("32, 128, 128, 2, 2", 2), ("32, 128, 64, 2, 2", 2)]
+CONFIGS = [("16, 256, 256, 2, 2", 2), ("16, 256, 256, 2, 2", 3), ("32, 128, 128, 2, 2", 2), ("32, 128, 64, 2, 2", 2),
+           ("16, 256, 384, 2, 2", 2)]
 
 
 @pytest.mark.skipif(shutil.which("nm") is None, reason="needs nm")
@@ -20,7 +21,7 @@ def test_kernel_labels_map_to_library_symbols():
     names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
     for cfg, depth in CONFIGS:
         for epi in range(4):
-            for ordered in ("false", "true") if cfg.startswith("16, 256") else ("false",):
+            for ordered in ("false", "true") if cfg.startswith("16, 256, 256") else ("false",):
                 label = f"gemm_f16_mfma_kernel<{cfg}, {epi}, {depth}, {ordered}>"
                 assert bench.kernel_symbol(label) in names, label
     assert bench.kernel_symbol("gemm_streamk_kernel + streamk_reduce_kernel") is None

@@ -216,12 +216,13 @@ def test_gemm_integer_exact_request_stream_rows(M, N):
 
 # (M, N, K, epi): 256 x 256 tile counts that leave the persistent launch's last
 # round partial, with whole rounds R and extra tiles E of 256 workgroups, split
-# over P of them: R 23 / E 64 / P 128 (pieces of 32 K tiles), R 2 / E 100 /
+# over P of them: R 23 / E 95 / P 190 (pieces of 32 K tiles), R 2 / E 100 /
 # P 200 (the TP-shard QKV), R 3 / E 48 / P 96 and P 128 (the TP-shard out
-# projection and FC2 widths, K = 4096 and 49152), R 6 / E 48 / P 96 with the
-# residual, and R 1 / E 16 (too few rounds: the row split instead)
-ORDERED = [(7889, 49152, 4096, ee.EPI_BIAS_GELU), (4205, 9216, 4096, ee.EPI_BIAS),
-           (4205, 12288, 4096, ee.EPI_BIAS_RESIDUAL), (8436, 12288, 4096, ee.EPI_BIAS_RESIDUAL),
+# projection and FC2 widths, K = 4096 and 49152), R 6 / E 81 / P 162 with the
+# residual, and R 1 / E 16 (too few rounds: the row split instead).  N is not
+# a multiple of 384 where 256 x 384 tiles would be planned instead.
+ORDERED = [(7889, 49408, 4096, ee.EPI_BIAS_GELU), (4205, 9216, 4096, ee.EPI_BIAS),
+           (4205, 12288, 4096, ee.EPI_BIAS_RESIDUAL), (8436, 12544, 4096, ee.EPI_BIAS_RESIDUAL),
            (4205, 12288, 49152, ee.EPI_BIAS_RESIDUAL), (4300, 4096, 512, ee.EPI_NONE)]
 
 
@@ -256,15 +257,16 @@ def test_gemm_ordered_split_bit_identical(M, N, K, epi, linear_ws):
 
 def test_profile_splits_a_site_by_kernel(linear_ws):
     """A GEMM site whose launches ran the plain and the in-order split form of
-    the large kernel (8192 rows: whole rounds; 7889 rows: 64 extra tiles) is
-    reported per kernel: by_kernel holds both labels with their launches and
-    flops, and the site's kernel reads "several kernels"."""
-    N, K = 49152, 4096
+    the large kernel (N = 16384, 64 tile columns; 8192 rows: whole rounds;
+    8500 rows: 128 extra tiles) is reported per kernel: by_kernel holds both
+    labels with their launches and flops, and the site's kernel reads
+    "several kernels"."""
+    N, K = 16384, 4096
     W = (0.05 * torch.randn(N, K, generator=GEN)).half().to(DEV)
     bias = torch.zeros(N, dtype=torch.float16, device=DEV)
     ee.ee_profile_enable(True)
     try:
-        for M in (8192, 7889):
+        for M in (8192, 8500):
             A = torch.randn(M, K, generator=GEN).half().to(DEV)
             C = torch.empty(M, N, dtype=torch.float16, device=DEV)
             ee.ee_linear_ws(A, W, bias, None, ee.EPI_BIAS_GELU, C, linear_ws)
@@ -276,10 +278,10 @@ def test_profile_splits_a_site_by_kernel(linear_ws):
     assert st["launches"] == 2 and st["kernel"] == "several kernels"
     assert set(st["by_kernel"]) == {plain, split}
     assert st["by_kernel"][plain]["flops"] == 2.0 * 8192 * N * K
-    assert st["by_kernel"][split]["flops"] == 2.0 * 7889 * N * K
+    assert st["by_kernel"][split]["flops"] == 2.0 * 8500 * N * K
 
 
-@pytest.mark.parametrize("M,N,K", [(7889, 49152, 4096), (4205, 12288, 4096)])
+@pytest.mark.parametrize("M,N,K", [(7889, 49408, 4096), (4205, 12288, 4096)])
 def test_gemm_ordered_split_integer_exact(M, N, K, linear_ws):
     """Small-integer operands through ee_linear_ws: two rows of every 256-row
     tile, over all N, are the fp16 rounding of the exact sum, bit for bit."""
@@ -312,13 +314,92 @@ def test_gemm_integer_exact_long_k(K):
     assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
 
 
+# (M, N, K, epi) planned on 256 x 384 tiles (N a multiple of 384): whole
+# rounds of them (16 rounds at 8192 x 49152; 6 at 4096 x 36864), and rows
+# past the whole rounds on the 256 x 256 plan's smaller tiles (7889 rows: 209
+# rows on 128 x 128 tiles; 4205 rows: 109 rows on 128 x 64 tiles)
+WIDE = [(8192, 49152, 4096, ee.EPI_BIAS_GELU), (7889, 49152, 4096, ee.EPI_BIAS),
+        (4096, 36864, 1024, ee.EPI_BIAS_RESIDUAL), (4205, 12288, 512, ee.EPI_NONE)]
+WIDE_LABEL = "gemm_f16_mfma_kernel<16, 256, 384, 2, 2, {}, 2, false>"
+
+
+@pytest.mark.parametrize("M,N,K,epi", WIDE)
+def test_gemm_wide_tile_matches_square_tile(M, N, K, epi):
+    """The 256 x 384 tile against the 256 x 256 one on random data: the same
+    problem with 256 more W rows (N + 256 columns, which no 256 x 384 plan
+    covers) gives the same bits in the first N columns, since every output
+    element adds its K tiles in the same order with the same MFMA shape."""
+    gen = torch.Generator().manual_seed(M + N + K + epi)
+    A = torch.randn(M, K, generator=gen).half().to(DEV)
+    W = (0.05 * torch.randn(N + 256, K, generator=gen)).half().to(DEV)
+    bias = (0.1 * torch.randn(N + 256, generator=gen)).half().to(DEV)
+    R = torch.randn(M, N + 256, generator=gen).half().to(DEV) if epi == ee.EPI_BIAS_RESIDUAL else None
+    wide = Guarded((M, N), torch.float16, fill=float("nan"))
+    ee.ee_profile_enable(True)
+    try:
+        ee.ee_linear(A, W[:N], None if epi == ee.EPI_NONE else bias[:N],
+                     None if R is None else R[:, :N].contiguous(), epi, wide.t)
+        st = ee.ee_profile_collect()
+    finally:
+        ee.ee_profile_enable(False)
+    square = torch.full((M, N + 256), float("nan"), dtype=torch.float16, device=DEV)
+    ee.ee_linear(A, W, None if epi == ee.EPI_NONE else bias, R, epi, square)
+    torch.cuda.synchronize()
+    wide.check("C")
+    assert st["linear"]["kernel"] == WIDE_LABEL.format(epi)
+    rows_w = st["linear"]["flops"] / (2.0 * N * K)
+    say(f"wide {M}x{N}x{K} epi={epi}: {rows_w:.0f} rows on 256 x 384 tiles, rest {st.get('linear_rest', {}).get('kernel')}")
+    diff = (wide.t.view(torch.int16) != square[:, :N].view(torch.int16)).any(dim=1).nonzero().flatten().tolist()
+    assert not diff, f"{len(diff)} rows differ, first {diff[:8]}"
+
+
+@pytest.mark.parametrize("M,N,K", [(8192, 49152, 4096), (7889, 36864, 1024)])
+def test_gemm_wide_tile_integer_exact(M, N, K):
+    """Small-integer operands on 256 x 384 tiles (and the rows after their
+    whole rounds): two rows of every 256-row tile, over all N, are the fp16
+    rounding of the exact sum, bit for bit."""
+    A, W = _small_ints((M, K)), _small_ints((N, K))
+    bias = _small_ints((N,))
+    C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    ee.ee_profile_enable(True)
+    try:
+        ee.ee_linear(A.to(DEV), W.to(DEV), bias.to(DEV), None, ee.EPI_BIAS, C)
+        st = ee.ee_profile_collect()
+    finally:
+        ee.ee_profile_enable(False)
+    torch.cuda.synchronize()
+    assert st["linear"]["kernel"] == WIDE_LABEL.format(ee.EPI_BIAS)
+    rows = sorted({r for t in range(0, M, 256) for r in (t, min(M, t + 256) - 1)})
+    exact = A[rows].double().numpy() @ W.double().numpy().T + bias.double().numpy()
+    got = C[rows].cpu().numpy()
+    assert np.array_equal(got.view(np.uint16), exact.astype(np.float16).view(np.uint16))
+
+
+def test_profile_reports_wide_tiles_and_rest():
+    """7889 x 49152: 30 M-tiles of 256 x 384 tiles fill 15 whole rounds (site
+    "linear"); the last 209 rows run on 128 x 128 tiles (site "linear_rest")."""
+    M, N, K = 7889, 49152, 1024
+    A = torch.randn(M, K, generator=GEN).half().to(DEV)
+    W = (0.05 * torch.randn(N, K, generator=GEN)).half().to(DEV)
+    C = torch.empty(M, N, dtype=torch.float16, device=DEV)
+    ee.ee_profile_enable(True)
+    try:
+        ee.ee_linear(A, W, None, None, ee.EPI_NONE, C)
+        st = ee.ee_profile_collect()
+    finally:
+        ee.ee_profile_enable(False)
+    assert st["linear"]["kernel"] == WIDE_LABEL.format(ee.EPI_NONE)
+    assert st["linear"]["flops"] == 2.0 * 7680 * N * K
+    assert st["linear_rest"]["kernel"] == "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 0, 2, false>"
+    assert st["linear_rest"]["flops"] == 2.0 * 209 * N * K
+
+
 @pytest.mark.parametrize("M,rest_kernel", [(4205, "gemm_f16_mfma_kernel<32, 128, 64, 2, 2, 2, 2, false>"),
                                            (8457, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 2, 2, false>")])
 def test_gemm_integer_exact_row_split_long_k(M, rest_kernel):
     """The FC2 shape of the layer (N = 12288, K = 49152, A and W rows at the
-    preferred 49216-element pitch) at row counts whose 256 x 256 tile count is
-    just past a multiple of the CU count: whole rounds of 256-row tiles on the
-    three-W-stage kernel (timed as site "linear"), the remaining rows on
+    preferred 49216-element pitch) at row counts past whole rounds of 256 x
+    384 tiles: those rounds (timed as site "linear"), the remaining rows on
     smaller tiles (site "linear_rest").  Small-integer operands, so the result
     is the fp16 rounding of the exact sum, bit for bit, on sampled rows of
     both parts."""
@@ -340,7 +421,7 @@ def test_gemm_integer_exact_row_split_long_k(M, rest_kernel):
         ee.ee_profile_enable(False)
     torch.cuda.synchronize()
     m_big = M // 256 * 256 if M == 4205 else 8192
-    assert st["linear"]["kernel"] == "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3, false>"
+    assert st["linear"]["kernel"] == "gemm_f16_mfma_kernel<16, 256, 384, 2, 2, 2, 2, false>"
     assert st["linear_rest"]["kernel"] == rest_kernel
     assert st["linear"]["flops"] == 2.0 * m_big * N * K and st["linear_rest"]["flops"] == 2.0 * (M - m_big) * N * K
     rows = [0, 1, 255, m_big - 1, m_big, m_big + 1, (m_big + M) // 2, M - 1]

@@ -319,7 +319,7 @@ ee_status gemm_site(const char* site, const char* rest_site, ee_dtype dt, const 
           flops, "gemm_f16_mfma_kernel<32, 128, 128, 2, 2, 4, 2, false> + splitk_reduce_kernel");
       return e == hipSuccess ? EE_OK : hip_fail(e, site);
     }
-    GemmPart parts[2];
+    GemmPart parts[kGemmMaxParts];
     const bool vec_stores = N % 8 == 0 && ld.c % 8 == 0 && aligned16(C) && (!R || aligned16(R));
     const int n = gemm_f16_parts(M, N, K, parts, ordered ? ordered_bytes : 0, vec_stores);
     for (int i = 0; i < n; ++i) {

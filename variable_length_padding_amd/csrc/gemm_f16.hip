@@ -49,6 +49,7 @@
 #include <algorithm>
 #include <atomic>
 #include <chrono>
+#include <numeric>
 #include <random>
 #include <type_traits>
 
@@ -77,6 +78,21 @@ namespace {
 // ring (W requested two K tiles ahead, A one), shorter ones two (both one
 // ahead).  Three measured 1.7% faster on FC2 (K = 49152, where both operands
 // stream from HBM) and 1.6% slower on the QKV GEMM (K = 12288).
+#ifndef EE_GEMM_WIDE
+#define EE_GEMM_WIDE 1
+#endif
+#ifndef EE_GEMM_WIDE_LB
+#define EE_GEMM_WIDE_LB 5
+#endif
+#ifndef EE_GEMM_WIDE_Q1
+#define EE_GEMM_WIDE_Q1 6
+#endif
+#ifndef EE_GEMM_WIDE_FOLD
+#define EE_GEMM_WIDE_FOLD 0
+#endif
+#ifndef EE_GEMM_WIDE_GAP1
+#define EE_GEMM_WIDE_GAP1 5
+#endif
 #ifndef EE_GEMM_DEEP_W_K
 #define EE_GEMM_DEEP_W_K 32768
 #endif
@@ -113,6 +129,16 @@ struct Frag<16> {
   __device__ static int row(int lane, int e) { return (lane >> 4) * 4 + e; }
   __device__ static acc_t mfma(half8 a, half8 b, acc_t c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 };
+
+// f(std::integral_constant<int, I>) for I = I0 .. N - 1, unrolled by the
+// compiler's front end (a loop of inline asm blocks is not always unrolled).
+template <int I0, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, N>(f);
+  }
+}
 
 // Row-major epilogue through LDS: the MFMA result layout gives a lane one
 // column of several rows, so storing from it writes 2 bytes per lane and
@@ -153,6 +179,8 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
   constexpr int FPB = 1;  // fragment rows per band
   constexpr int PASSES = SE::kBandRows / SE::kRowsPerPass;
   const int c8 = lane % SE::kLanesPerRow, rsub = lane / SE::kLanesPerRow;
+  // a 192-column wave tile has 24 lanes per row: lanes 48-63 stay idle
+  const bool lane_on = SE::kRowsPerPass * SE::kLanesPerRow == 64 || rsub < SE::kRowsPerPass;
   const int col = col0 + c8 * 8;
   float bcol[FN];
 #pragma unroll
@@ -160,14 +188,16 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
     const int cj = col0 + j * MF + lane % MF;
     bcol[j] = (kHasBias<EPI> && cj < N) ? (float)bias[cj] : 0.f;
   }
-#pragma unroll
-  for (int band = 0; band < FM / FPB; ++band) {
+  // bands unrolled by the front end: with GeLU a 12-fragment band is too long
+  // for the loop unroller, and an indexed band would put acc in memory
+  static_for<0, FM / FPB>([&](auto BAND) __attribute__((always_inline)) {
+    constexpr int band = decltype(BAND)::value;
     // the residual of this band is requested before the band goes through LDS
     half8 rv[PASSES];
 #pragma unroll
     for (int it = 0; it < PASSES; ++it) {
       const int row = row0 + band * SE::kBandRows + it * SE::kRowsPerPass + rsub;
-      if (EPI == EE_EPI_BIAS_RESIDUAL && !to_raw && row < M && col < N)
+      if (EPI == EE_EPI_BIAS_RESIDUAL && !to_raw && lane_on && row < M && col < N)
         rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * ldc + col);
     }
 #pragma unroll
@@ -186,6 +216,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
     for (int it = 0; it < PASSES; ++it) {
       const int r = it * SE::kRowsPerPass + rsub;
       const int row = row0 + band * SE::kBandRows + r;
+      if (!lane_on) continue;
       const float4 lo = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8);
       const float4 hi = *reinterpret_cast<const float4*>(stage + r * SE::kLd + c8 * 8 + 4);
       if (to_raw) {
@@ -209,7 +240,7 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
       }
     }
     __syncthreads();  // the next band overwrites this wave's slice
-  }
+  });
 }
 
 // Direct per-element epilogue of a wave's FM x FN block of fragments whose
@@ -219,10 +250,10 @@ __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)
                                            const f16* __restrict__ bias, const f16* __restrict__ R,
                                            f16* __restrict__ C, int M, int N, int ldc, int gelu_form,
                                            float* __restrict__ Pp) {
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
+  static_for<0, FN>([&](auto J) __attribute__((always_inline)) {
+    constexpr int j = decltype(J)::value;
     const int col = col0 + j * MF + lane % MF;
-    if (col >= N) continue;
+    if (col >= N) return;
     const float bcol = kHasBias<EPI> ? (float)bias[col] : 0.f;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
@@ -239,7 +270,7 @@ __device__ __forceinline__ void store_tile(const typename Frag<MF>::acc_t (&acc)
         }
       }
     }
-  }
+  });
 }
 
 // In-order stream-K of a persistent launch's partial last round.  After
@@ -329,13 +360,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   };
   // load q of a tile's A rows (q < AJ, K offset ka into A stage as) or of its
   // W rows (K offset kw into W stage ws); A loads are issued before W loads
+  // Rows 16 apart have the same swizzle, so a 256 x 384 tile (whose register
+  // file has no room for an offset per load) keeps the offsets of loads 0
+  // and 1 and adds 16 rows per further pair in the loop itself; the row
+  // offset stays in the lane offset, which the descriptor's range check sees.
+  auto lane_off = [&](const int* off, int q, int ld) {
+    if constexpr (BN == 384 && EE_GEMM_WIDE_FOLD) {
+      int o = off[q & 1];
+      asm volatile("" : "+v"(o));
+      return o + (q >> 1) * 32 * ld;
+    } else {
+      return off[q];
+    }
+  };
   auto dma_one = [&](int as, int ka, int ws, int kw, int q) {
     if (q < AJ) {
       f16* sa = smem + a_off(as) + (wave * (BM / NW) + 8 * q) * kBK;
-      buffer_load_lds16(arsrc, sa, aoff[q], (kb + ka) * 2);
+      buffer_load_lds16(arsrc, sa, lane_off(aoff, q, lda), (kb + ka) * 2);
     } else {
       f16* sb = smem + w_off(ws) + (wave * (BN / NW) + 8 * (q - AJ)) * kBK;
-      buffer_load_lds16(wrsrc, sb, boff[q - AJ], (kb + kw) * 2);
+      buffer_load_lds16(wrsrc, sb, lane_off(boff, q - AJ, ldw), (kb + kw) * 2);
     }
   };
   auto dma_a = [&](int as, int ka) {
@@ -479,6 +523,123 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     mfmas(fa1, fb1);
     wait_dma();  // no load may still be writing LDS when it is reused or the workgroup retires
   };
+  // ---- the K loop of a 256 x 384 tile (wave tile 128 x 192: 384 accumulators
+  // per lane).  Both operands' fragments for a whole K step, double-buffered
+  // as above, would not fit beside them, so the A fragments alone are
+  // double-buffered and the W (B) fragments stream through a ring of NBR
+  // registers: the MFMAs go column by column (column j's FM MFMAs take B
+  // fragment j and the resident A fragments) and B fragment j + LB is read at
+  // the start of column j.  Step 1 of K tile kt reads its last B fragment
+  // (column FN - 1) at column PB - 1; the tile's one barrier sits before
+  // column PB.  It waits for this wave's loads of tile kt + 1 and for its LDS
+  // reads, so after it the next tile's A fragments and first B fragments are
+  // read from the other stage, and the loads of tile kt + 2 go into this one:
+  // loads [0, Q1) after the barrier, the rest in step 0 of tile kt + 1.
+  //
+  // The compiler gives every MFMA accumulator the AGPR class, and 384 do not
+  // fit in the 256 AGPRs: columns [0, kWideA) use the builtin (AGPRs), the
+  // rest inline asm with VGPR accumulators.  The compiler knows nothing of
+  // the asm MFMAs' latency, which matters only for their results (an MFMA
+  // reads its A and B operands at issue, so a ring slot may be refilled right
+  // after): each accumulator's MFMAs are a K step apart, and the s_nops after
+  // the last step wait out the last ones before anything reads them.
+  constexpr bool kWide = BN == 384;
+  constexpr int LB = EE_GEMM_WIDE_LB, NBR = LB + 1, PB = FN - LB, Q1 = EE_GEMM_WIDE_Q1, kWideA = 8;
+  constexpr int kPostSlots = (FN - PB) * FM;            // MFMA slots after the barrier
+  constexpr int kAPer = (FM + (FN - PB) - 1) / (FN - PB);  // next-tile A reads per column there
+  constexpr int kDmaGap2 = kPostSlots / (Q1 > 0 ? Q1 : 1);  // slots between loads there
+  constexpr int kDmaGap1 = EE_GEMM_WIDE_GAP1;               // slots between step 0's loads
+  static_assert(!kWide || (MF == 16 && NSTEP == 2 && WD == 2 && FN % NBR == 0 && PB > 0 && kAPer < FM &&
+                           kDmaGap1 * (NL - Q1) <= FN * FM && kDmaGap2 >= 2 && FM * kWideA * 4 == 256),
+                "the wide K loop's schedule");
+  auto read_a = [&](int st, int kk, int i) {
+    const int ch = ((kk * (FR::kK / 8) + kg) ^ rsw) * 8;
+    return *reinterpret_cast<const half8*>(smem + a_off(st) + abase + i * MF * kBK + ch);
+  };
+  auto read_b = [&](int st, int kk, int j) {
+    const int ch = ((kk * (FR::kK / 8) + kg) ^ rsw) * 8;
+    return *reinterpret_cast<const half8*>(smem + w_off(st) + bbase + j * MF * kBK + ch);
+  };
+  half8 br[NBR];
+  // One K step of a wide tile from stage c: S is the step (0 or 1); NX (step
+  // 1) whether a next K tile follows; DM which loads go out: 1 = loads
+  // [Q1, NL) of the tile at K offset dk into stage c ^ 1 (step 0), 2 = loads
+  // [0, Q1) of it into stage c, after the barrier (step 1).
+  auto wide_step = [&](auto S, auto NX, auto DM, auto Z, const half8 (&xa)[FM], half8 (&ya)[FM], int c,
+                       int dk) __attribute__((always_inline)) {
+    constexpr int s = decltype(S)::value, dm = decltype(DM)::value;
+    constexpr bool nx = decltype(NX)::value, z = decltype(Z)::value;
+    static_for<0, FN * FM>([&](auto M) __attribute__((always_inline)) {
+      constexpr int m = decltype(M)::value, j = m / FM, i = m % FM;
+      if constexpr (s == 1 && nx && m == PB * FM) barrier_after_loads<0>();
+      if constexpr (i == 0) {
+        constexpr int jb = j + LB;
+        if constexpr (jb < FN)
+          br[jb % NBR] = read_b(c, s, jb);
+        else if constexpr (s == 0)
+          br[jb % NBR] = read_b(c, 1, jb - FN);
+        else if constexpr (nx)
+          br[jb % NBR] = read_b(c ^ 1, 0, jb - FN);
+      }
+      if constexpr (s == 0 && i == FM / 2 && j < FM) ya[j] = read_a(c, 1, j);
+      if constexpr (s == 1 && nx && j >= PB && i % (FM / kAPer) == 1) {
+        constexpr int ia = (j - PB) * kAPer + i / (FM / kAPer);
+        if constexpr (ia < FM) ya[ia] = read_a(c ^ 1, 0, ia);
+      }
+      if constexpr (dm == 1 && m >= 2 && (m - 2) % kDmaGap1 == 0 && (m - 2) / kDmaGap1 < NL - Q1)
+        dma_one(c ^ 1, dk, c ^ 1, dk, Q1 + (m - 2) / kDmaGap1);
+      if constexpr (dm == 2 && m > PB * FM && (m - PB * FM - 1) % kDmaGap2 == 0 && (m - PB * FM - 1) / kDmaGap2 < Q1)
+        dma_one(c, dk, c, dk, (m - PB * FM - 1) / kDmaGap2);
+      if constexpr (z && j < kWideA)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=a"(acc[i][j]) : "v"(xa[i]), "v"(br[j % NBR]));
+      else if constexpr (z)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "=v"(acc[i][j]) : "v"(xa[i]), "v"(br[j % NBR]));
+      else if constexpr (j < kWideA)
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+a"(acc[i][j]) : "v"(xa[i]), "v"(br[j % NBR]));
+      else
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0" : "+v"(acc[i][j]) : "v"(xa[i]), "v"(br[j % NBR]));
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+  // nk >= 2 (the host gives this tile K >= 2 * kBK)
+  auto k_loop_wide = [&](int nk) __attribute__((always_inline)) {
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    // K tile 0 (stage 0) is in flight; loads [0, Q1) of K tile 1 go into
+    // stage 1 now, the rest in step 0 below, as for every later K tile
+#pragma unroll
+    for (int q = 0; q < Q1; ++q) dma_one(1, kBK, 1, kBK, q);
+    barrier_after_loads<Q1>();
+    br[0] = read_b(0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa0[i] = read_a(0, 0, i);
+#pragma unroll
+    for (int j = 1; j < LB; ++j) br[j] = read_b(0, 0, j);
+    // step 0 of K tile 0 starts the sums from 0 (an inline constant: the
+    // accumulators are never written by VALU instructions, whose results
+    // the asm MFMAs would not wait for); then step 1 of K tile kt and step 0
+    // of K tile kt + 1 per iteration
+    wide_step(I0{}, F{}, I1{}, T{}, fa0, fa1, 0, kBK);
+    int kt = 0;
+    for (; kt + 1 < nk; ++kt) {
+      wide_step(I1{}, T{}, I2{}, F{}, fa1, fa0, kt & 1, min(kt + 2, nk - 1) * kBK);
+      wide_step(I0{}, F{}, I1{}, F{}, fa0, fa1, (kt + 1) & 1, min(kt + 2, nk - 1) * kBK);
+    }
+    wide_step(I1{}, F{}, I0{}, F{}, fa1, fa0, kt & 1, 0);
+    // the last MFMAs' results are written before anything reads them (24
+    // wait states: more than a 16-pass MFMA needs)
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    wait_dma();  // no load may still be writing LDS when it is reused or the workgroup retires
+  };
+  auto run_k_loop = [&](int nk) {
+    if constexpr (kWide)
+      k_loop_wide(nk);
+    else
+      k_loop(nk);
+  };
   auto zero_acc = [&]() {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -504,7 +665,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     early_loads();
     for (;;) {
       zero_acc();
-      k_loop(k_len / kBK);
+      run_k_loop(k_len / kBK);
       const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
       const int next = tile + (int)gridDim.x;
       __syncthreads();  // every wave is done reading the ring
@@ -593,7 +754,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
           early_loads();
         }
       }
-      k_loop(it.k1 - it.k0);
+      run_k_loop(it.k1 - it.k0);
       const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
       const int tile_m0 = m0, tile_n0 = n0;  // set_tile below moves m0, n0 to the next item
       const ItemAt nxa = item_at(c + 1);
@@ -662,9 +823,12 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
     case EE_EPI_BIAS: EE_GEMM_LAUNCH(EE_EPI_BIAS); break;
     case EE_EPI_BIAS_RESIDUAL: EE_GEMM_LAUNCH(EE_EPI_BIAS_RESIDUAL); break;
     case EE_EPI_BIAS_GELU: EE_GEMM_LAUNCH(EE_EPI_BIAS_GELU); break;
-    case kEpiPartial:  // split-K partial sums: never with an ordered split
-      hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, kEpiPartial, WDEPTH, false>), grid, block, 0, s, a,
-                         ld.a, w, ld.w, b, r, c, ld.c, M, N, K, (int)form, tm, tn, P, os);
+    case kEpiPartial:  // split-K partial sums (128 x 128 tiles only): never with an ordered split
+      if constexpr (BN != 384)
+        hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, kEpiPartial, WDEPTH, false>), grid, block, 0, s,
+                           a, ld.a, w, ld.w, b, r, c, ld.c, M, N, K, (int)form, tm, tn, P, os);
+      else
+        return hipErrorInvalidValue;
       break;
   }
 #undef EE_GEMM_LAUNCH
@@ -814,29 +978,88 @@ OrderedSplit ordered_split(int64_t M, int N, int K, int wgs, void* scratch, size
 
 size_t gemm_f16_ordered_bytes() { return kOrderedFlagBytes + (size_t)kOrderedMaxWgs * kOrderedTileBytes; }
 
-int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[2], size_t ordered_bytes, bool vec_stores) {
-  if (M <= 0) return 0;
+namespace {
+// Time of a 256 x 384 round in 256 x 256 rounds: 1.5 times the work at 4.5%
+// less time per flop (FC1, QKV and out GEMMs at 8192 rows, same process); at
+// K >= EE_GEMM_DEEP_W_K, against the three-W-stage 256 x 256 kernel, 10% less
+// (FC2 at 4096, 8125 and 8192 rows).
+constexpr double kWideRoundCost = 1.43;
+constexpr double kWideRoundCostLongK = 1.35;
+// What a second launch costs beyond its rounds: its first and last tiles'
+// loads and stores are not overlapped with another tile's MFMAs.
+constexpr double kLaunchCost = 0.05;
+
+// The 256 x 256 plan of rows [row0, row0 + M): one or two parts; *rounds
+// gets its estimated time in 256 x 256 rounds.
+int plan_square(int64_t row0, int64_t M, int N, int K, GemmPart* parts, size_t ordered_bytes, bool vec_stores,
+                int cus, double* rounds) {
   const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles_big < 256) {
-    parts[0] = GemmPart{0, M, kGemm128x128, false};
+  if (tiles_big < cus) {
+    // the rows after another part's whole rounds stream all of W through few
+    // tiles: 128 x 64 tiles (the same MFMA shape) put twice as many CUs on it
+    const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
+    const bool narrow = row0 > 0 && small * 2 <= cus;
+    *rounds = kSmallTileCost * (double)((small + cus - 1) / cus);
+    parts[0] = GemmPart{row0, M, narrow ? kGemm128x64 : kGemm128x128, false};
     return 1;
   }
-  const int cus = device_cu_count();
   const int big = K >= EE_GEMM_DEEP_W_K ? kGemmBig3 : kGemmBig2;
   if (EE_GEMM_PERSIST && vec_stores &&
       ordered_wgs(M, N, K, (int)std::min<int64_t>(tiles_big, cus), ordered_bytes) > 0) {
-    parts[0] = GemmPart{0, M, big, true};  // the launch splits its partial last round itself
+    *rounds = (double)tiles_big / cus + kLaunchCost;
+    parts[0] = GemmPart{row0, M, big, true};  // the launch splits its partial last round itself
     return 1;
   }
   const int64_t m_big = gemm_big_rows(M, N, cus);
-  parts[0] = GemmPart{0, m_big, big, false};
+  parts[0] = GemmPart{row0, m_big, big, false};
+  const int64_t tn = (N + 255) / 256;
+  *rounds = (double)((((m_big + 255) / 256) * tn + cus - 1) / cus);
   if (m_big == M) return 1;
   // Few remaining rows stream all of W through few tiles: 128 x 64 tiles
   // (the same MFMA shape) put twice as many CUs on it.
   const int64_t rest = M - m_big;
-  const bool narrow = ((rest + 127) / 128) * ((N + 127) / 128) * 2 <= cus;
-  parts[1] = GemmPart{m_big, rest, narrow ? kGemm128x64 : kGemm128x128, false};
+  const int64_t small = ((rest + 127) / 128) * ((N + 127) / 128);
+  const bool narrow = small * 2 <= cus;
+  *rounds += kSmallTileCost * (double)((small + cus - 1) / cus);
+  parts[1] = GemmPart{row0 + m_big, rest, narrow ? kGemm128x64 : kGemm128x128, false};
   return 2;
+}
+}  // namespace
+
+int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[kGemmMaxParts], size_t ordered_bytes,
+                   bool vec_stores) {
+  if (M <= 0) return 0;
+  const int cus = device_cu_count();
+  double t_square = 0.0;
+  const int n_square = plan_square(0, M, N, K, parts, ordered_bytes, vec_stores, cus, &t_square);
+  if (!(EE_GEMM_WIDE && EE_GEMM_PERSIST && N % 384 == 0 && K >= 2 * kBK)) return n_square;
+  const double wide_cost = K >= EE_GEMM_DEEP_W_K ? kWideRoundCostLongK : kWideRoundCost;
+  // 256 x 384 tiles on the rows that fill whole rounds of them (M tiles in
+  // groups of `step`), the rest on the 256 x 256 plan; or on every row, the
+  // last round partial.  Taken where the estimate ends sooner.
+  const int64_t tn = N / 384, mt = (M + 255) / 256;
+  const int64_t step = cus / std::gcd<int64_t>(cus, tn);
+  const int64_t m_tiles = mt / step * step;
+  const int64_t rows_w = std::min<int64_t>(M, m_tiles * 256);
+  GemmPart rest[kGemmMaxParts - 1];
+  double t_rest = 0.0;
+  const int n_rest = rows_w < M && rows_w > 0
+                         ? plan_square(rows_w, M - rows_w, N, K, rest, ordered_bytes, vec_stores, cus, &t_rest)
+                         : 0;
+  const double t_split = rows_w > 0 ? (double)(m_tiles * tn / cus) * wide_cost + t_rest +
+                                          (n_rest > 0 ? kLaunchCost : 0.0)
+                                    : 1e30;
+  const double t_all = mt * tn >= cus ? (double)((mt * tn + cus - 1) / cus) * wide_cost : 1e30;
+  if (t_all <= t_split && t_all < t_square) {
+    parts[0] = GemmPart{0, M, kGemmWide, false};
+    return 1;
+  }
+  if (t_split < t_square) {
+    parts[0] = GemmPart{0, rows_w, kGemmWide, false};
+    for (int i = 0; i < n_rest; ++i) parts[1 + i] = rest[i];
+    return 1 + n_rest;
+  }
+  return n_square;
 }
 
 hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W, const void* bias, const void* R,
@@ -860,6 +1083,8 @@ hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W,
     case kGemmBig3:
       return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(a, W, bias, r, M, N, K, ld, epi, form, c, 1,
                                                                           nullptr, s, wgs, os);
+    case kGemmWide:
+      return launch_cfg<16, 256, 384, 2, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s, wgs);
     case kGemm128x64: return launch_cfg<32, 128, 64, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
     case kGemm128x128: return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
   }
@@ -868,7 +1093,7 @@ hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W,
 
 const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi, bool ordered) {
   // gemm_f16_mfma_kernel's template arguments <MF, BM, BN, WGM, WGN, EPI, WDEPTH, ORD>
-  static const char* const labels[4][4] = {
+  static const char* const labels[5][4] = {
 #define EE_L(cfg) {"gemm_f16_mfma_kernel<" cfg ", 0, 2, false>", "gemm_f16_mfma_kernel<" cfg ", 1, 2, false>", \
                    "gemm_f16_mfma_kernel<" cfg ", 2, 2, false>", "gemm_f16_mfma_kernel<" cfg ", 3, 2, false>"}
       EE_L("16, 256, 256, 2, 2"),
@@ -876,6 +1101,7 @@ const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi, bool ordered) {
        "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3, false>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 3, false>"},
       EE_L("32, 128, 128, 2, 2"),
       EE_L("32, 128, 64, 2, 2"),
+      EE_L("16, 256, 384, 2, 2"),
 #undef EE_L
   };
   static const char* const ordered_labels[2][4] = {
@@ -885,14 +1111,14 @@ const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi, bool ordered) {
        "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 3, true>"},
   };
   const int e = (int)epi;
-  if (cfg < 0 || cfg > 3 || e < 0 || e > 3) return "gemm_f16_mfma_kernel";
+  if (cfg < 0 || cfg > kGemmWide || e < 0 || e > 3) return "gemm_f16_mfma_kernel";
   return ordered && cfg <= kGemmBig3 ? ordered_labels[cfg][e] : labels[cfg][e];
 }
 
 
 hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, const void* R, int64_t M, int N,
                                 int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C, hipStream_t s) {
-  GemmPart parts[2];
+  GemmPart parts[kGemmMaxParts];
   const int n = gemm_f16_parts(M, N, K, parts, 0, false);
   for (int i = 0; i < n; ++i) {
     const hipError_t e = launch_gemm_f16_part(parts[i], A, W, bias, R, N, K, ld, epi, form, C, s, nullptr, 0);
