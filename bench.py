@@ -185,15 +185,17 @@ def pmc_summary_path(workload):
 
 def _traffic(workload, symbol):
     """HBM bytes per launch of the roofline kernel from the committed counter
-    summary, if it was taken on this workload, this kernel and the current
-    GEMM code."""
+    summary, if it was taken on this workload and the current GEMM code and
+    covers this kernel (its "kernel", or an entry of its "kernels")."""
     try:
         with open(pmc_summary_path(workload)) as f:
             s = json.load(f)
-        if s.get("gemm_code_sha256") != gemm_code_sha256() or s.get("kernel") != symbol:
+        if s.get("gemm_code_sha256") != gemm_code_sha256():
             return None
-        return s["hbm_bytes_per_launch"]
-    except (OSError, KeyError, ValueError):
+        if symbol in s.get("kernels", {}):
+            return s["kernels"][symbol]["hbm_bytes_per_launch"]
+        return s["hbm_bytes_per_launch"] if s.get("kernel") == symbol else None
+    except (OSError, KeyError, ValueError, TypeError):
         return None
 
 
@@ -221,7 +223,8 @@ def _kernel_table(w, stats, steps, ms_total, rows_of_site, B, P, attn_flops, res
             k["kernel"] = st["kernel"]
         if len(st.get("by_kernel", {})) > 1:   # e.g. a GEMM with and without the in-order split
             k["kernels"] = {lb: {"launches": v["launches"],
-                                 "tflops": round(v["flops"] / v["total_ms"] / 1e9, 1) if v["flops"] else None}
+                                 "tflops": round(v["flops"] / v["total_ms"] / 1e9, 1) if v["flops"] else None,
+                                 "flops_per_launch": v["flops"] / v["launches"]}
                             for lb, v in st["by_kernel"].items()}
         if fl:
             k["tflops"] = round(fl / (avg_ms * 1e-3) / 1e12, 1)

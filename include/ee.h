@@ -267,14 +267,18 @@ EE_API ee_status ee_linear_strided(const void* A, int64_t lda, const void* W, in
 /* ee_linear_strided with a workspace of at least ee_linear_ws_workspace_size()
  * bytes (device memory, not read before it is written; the caller keeps it).
  * A large fp16 problem runs as one persistent launch of one workgroup per CU
- * over 256 x 256 tiles.  When the tiles leave that launch's last round
+ * over 256 x 256 tiles, or 256 x 384 where N is a multiple of 384 and that
+ * is estimated to end sooner.  When the tiles leave that launch's last round
  * partial, its tiles are shared out as stream-K pieces (Osama et al., PPoPP
  * 2023): equal contiguous ranges of (tile, K tile) steps, one per workgroup.
  * A piece that starts inside a tile continues, in the same fp32 accumulators,
  * from the sums its predecessor left in the workspace, so each element still
  * adds its K tiles in one chain, in order: the result is bit for bit that of
  * ee_linear_strided, which runs the remaining rows as a second launch on
- * smaller tiles instead.  Calls that share a workspace must not overlap in
+ * other tiles instead (every tile shape adds an element's K tiles in the
+ * same order; the MFMA shapes' equal sums are measured on gfx950, see
+ * ee_linear).  The workspace holds 4 KiB of flags and one 256 x 384 fp32
+ * tile per CU (96 MiB + 4 KiB).  Calls that share a workspace must not overlap in
  * time (one stream).  fp32 and small problems run as ee_linear_strided.
  * Errors as ee_linear_strided, plus EE_ERR_WORKSPACE for a small workspace
  * and EE_ERR_INVALID_ARG for a workspace overlapping an operand. */

@@ -129,7 +129,7 @@ def test_op_entry_points_validate():
     assert lib.ee_linear(None, 1 << 31, None, None, 0, 64, 64, ee.F16, ee.EPI_NONE, 0, None, None) == 0
     # linear with a workspace: its size, then a small, a NULL and an overlapping workspace
     need = lib.ee_linear_ws_workspace_size()
-    assert need == 4096 + 256 * 256 * 256 * 4
+    assert need == 4096 + 256 * 256 * 384 * 4
     a, w, c, ws = 1 << 30, 1 << 31, 1 << 33, 1 << 34
     assert lib.ee_linear_ws(a, 64, w, 64, None, None, 8, 64, 64, ee.F16, ee.EPI_NONE, 0, c, 64, ws, need - 1,
                             None) == 3

@@ -21,7 +21,7 @@ def test_kernel_labels_map_to_library_symbols():
     names = {ln.split()[-1] for ln in out.splitlines() if ln.strip()}
     for cfg, depth in CONFIGS:
         for epi in range(4):
-            for ordered in ("false", "true") if cfg.startswith("16, 256, 256") else ("false",):
+            for ordered in ("false", "true") if cfg.startswith("16, 256") else ("false",):
                 label = f"gemm_f16_mfma_kernel<{cfg}, {epi}, {depth}, {ordered}>"
                 assert bench.kernel_symbol(label) in names, label
     assert bench.kernel_symbol("gemm_streamk_kernel + streamk_reduce_kernel") is None
@@ -43,3 +43,20 @@ def test_site_bytes():
     assert bench._site_bytes(w, 4096, 32, 256, "gemm_fc1") == (4096 * H + F * H + 4096 * F) * 2
     assert bench._site_bytes(w, 96, 32, 256, "gemm_fc2_rest") == (96 * F + H * F + 2 * 96 * H) * 2
     assert bench._site_bytes(w, 4096, 32, 256, "rebuild") == (4096 + 32 * 256) * H * 2
+
+
+def test_traffic_reads_the_summary_per_kernel(tmp_path, monkeypatch):
+    """The roofline's traffic comes from the counter summary's entry for its
+    kernel (or its top-level kernel), and only for the current GEMM code."""
+    import json
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    summary = {"kernel": "plain", "hbm_bytes_per_launch": 1.0, "gemm_code_sha256": bench.gemm_code_sha256(),
+               "kernels": {"plain": {"hbm_bytes_per_launch": 1.0}, "split": {"hbm_bytes_per_launch": 2.0}}}
+    with open(bench.pmc_summary_path("w"), "w") as f:
+        json.dump(summary, f)
+    assert bench._traffic("w", "plain") == 1.0 and bench._traffic("w", "split") == 2.0
+    assert bench._traffic("w", "other") is None and bench._traffic("x", "plain") is None
+    summary["gemm_code_sha256"] = "0" * 64
+    with open(bench.pmc_summary_path("w"), "w") as f:
+        json.dump(summary, f)
+    assert bench._traffic("w", "split") is None

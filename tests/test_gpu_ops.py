@@ -255,6 +255,44 @@ def test_gemm_ordered_split_bit_identical(M, N, K, epi, linear_ws):
         assert not diff, f"rows {diff[:8]}... differ"
 
 
+# (M, N, K, epi) whose 256 x 384 tiles leave a partial last round that
+# ee_linear_ws runs as in-order stream-K pieces of the same launch: R 15 / E
+# 128 / P 256 (FC1 width), R 12 / E 96 / P 256 (QKV width), R 4 / E 32 / P 128
+# (FC2: K = 49152, with the residual)
+WIDE_ORDERED = [(7889, 49152, 4096, ee.EPI_BIAS_GELU), (8436, 36864, 4096, ee.EPI_BIAS),
+                (8436, 12288, 49152, ee.EPI_BIAS_RESIDUAL)]
+
+
+@pytest.mark.parametrize("M,N,K,epi", WIDE_ORDERED)
+def test_gemm_wide_ordered_split_bit_identical(M, N, K, epi, linear_ws):
+    """The in-order split of a 256 x 384 launch (ee_linear_ws) gives
+    ee_linear's bits on random data, three calls in a row, the third on a
+    workspace filled with random bytes first."""
+    gen = torch.Generator().manual_seed(M + N + K)
+    A = torch.randn(M, K, generator=gen).half().to(DEV)
+    W = (0.05 * torch.randn(N, K, generator=gen)).half().to(DEV)
+    bias = (0.1 * torch.randn(N, generator=gen)).half().to(DEV)
+    R = torch.randn(M, N, generator=gen).half().to(DEV) if epi == ee.EPI_BIAS_RESIDUAL else None
+    ref = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+    ee.ee_linear(A, W, bias, R, epi, ref)
+    for rep in range(3):
+        if rep == 2:
+            linear_ws.copy_(torch.randint(0, 256, linear_ws.shape, dtype=torch.uint8, generator=gen).to(DEV))
+        C = torch.full((M, N), float("nan"), dtype=torch.float16, device=DEV)
+        ee.ee_profile_enable(True)
+        try:
+            ee.ee_linear_ws(A, W, bias, R, epi, C, linear_ws)
+            st = ee.ee_profile_collect()
+        finally:
+            ee.ee_profile_enable(False)
+        torch.cuda.synchronize()
+        assert st["linear"]["kernel"] == f"gemm_f16_mfma_kernel<16, 256, 384, 2, 2, {epi}, 2, true>"
+        assert st["linear"]["launches"] == 1 and "linear_rest" not in st
+        diff = (C.view(torch.int16) != ref.view(torch.int16)).any(dim=1).nonzero().flatten().tolist()
+        say(f"wide ordered split {M}x{N}x{K} epi={epi} call {rep}: {len(diff)} rows differ from ee_linear")
+        assert not diff, f"rows {diff[:8]}... differ"
+
+
 def test_profile_splits_a_site_by_kernel(linear_ws):
     """A GEMM site whose launches ran the plain and the in-order split form of
     the large kernel (N = 16384, 64 tile columns; 8192 rows: whole rounds;

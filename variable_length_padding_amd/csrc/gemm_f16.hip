@@ -602,7 +602,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     });
   };
   // nk >= 2 (the host gives this tile K >= 2 * kBK)
-  auto k_loop_wide = [&](int nk) __attribute__((always_inline)) {
+  auto k_loop_wide = [&](int nk, auto Z0) __attribute__((always_inline)) {
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
@@ -611,18 +611,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
     // K tile 0 (stage 0) is in flight; loads [0, Q1) of K tile 1 go into
     // stage 1 now, the rest in step 0 below, as for every later K tile
 #pragma unroll
-    for (int q = 0; q < Q1; ++q) dma_one(1, kBK, 1, kBK, q);
+    for (int q = 0; q < Q1; ++q) dma_one(1, min(1, nk - 1) * kBK, 1, min(1, nk - 1) * kBK, q);
     barrier_after_loads<Q1>();
     br[0] = read_b(0, 0, 0);
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa0[i] = read_a(0, 0, i);
 #pragma unroll
     for (int j = 1; j < LB; ++j) br[j] = read_b(0, 0, j);
-    // step 0 of K tile 0 starts the sums from 0 (an inline constant: the
-    // accumulators are never written by VALU instructions, whose results
-    // the asm MFMAs would not wait for); then step 1 of K tile kt and step 0
-    // of K tile kt + 1 per iteration
-    wide_step(I0{}, F{}, I1{}, T{}, fa0, fa1, 0, kBK);
+    // step 0 of K tile 0 starts the sums from 0 (Z0: an inline constant, so
+    // the accumulators are never written by VALU instructions, whose results
+    // the asm MFMAs would not wait for) or from acc as prepared; then step 1
+    // of K tile kt and step 0 of K tile kt + 1 per iteration
+    wide_step(I0{}, F{}, I1{}, Z0, fa0, fa1, 0, min(1, nk - 1) * kBK);
     int kt = 0;
     for (; kt + 1 < nk; ++kt) {
       wide_step(I1{}, T{}, I2{}, F{}, fa1, fa0, kt & 1, min(kt + 2, nk - 1) * kBK);
@@ -636,7 +636,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
   };
   auto run_k_loop = [&](int nk) {
     if constexpr (kWide)
-      k_loop_wide(nk);
+      k_loop_wide(nk, std::integral_constant<bool, !ORD>{});
     else
       k_loop(nk);
   };
@@ -736,15 +736,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
               reinterpret_cast<char*>(os.flags) + kOrderedFlagBytes + (size_t)it.pred * BM * BN * 4, (short)0,
               BM * BN * 4, kBufferFlags);
           const int voff = ((wm * WTM + FR::row(lane, 0)) * BN + wn * WTN + lane % MF) * 4;
+          static_for<0, FM * FN>([&](auto IJ) __attribute__((always_inline)) {
+            constexpr int i = decltype(IJ)::value / FN, j = decltype(IJ)::value % FN;
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-              for (int e = 0; e < FR::kElems; ++e)
-                acc[i][j][e] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(
-                               src, voff, ((i * MF + FR::row(0, e) - FR::row(0, 0)) * BN + j * MF) * 4, kCacheDevice));
+            for (int e = 0; e < FR::kElems; ++e)
+              acc[i][j][e] = __builtin_bit_cast(
+                  float, __builtin_amdgcn_raw_buffer_load_b32(
+                             src, voff, ((i * MF + FR::row(0, e) - FR::row(0, 0)) * BN + j * MF) * 4, kCacheDevice));
+          });
         } else {
           // never published: compute the tile from its first K tile instead
           wait_dma();
@@ -753,6 +752,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
           kb = kbeg;
           early_loads();
         }
+      }
+      if constexpr (kWide) {
+        // the wide K loop's asm MFMAs take acc as it stands (zeros or a
+        // predecessor's sums): each value is placed in its MFMA's register
+        // class here, and the s_nops let those writes complete first
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int j = 0; j < kWideA; ++j) asm volatile("" : "+a"(acc[i][j]));
+#pragma unroll
+          for (int j = kWideA; j < FN; ++j) asm volatile("" : "+v"(acc[i][j]));
+        }
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
       }
       run_k_loop(it.k1 - it.k0);
       const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
@@ -809,8 +821,8 @@ hipError_t launch_cfg(const void* A, const void* W, const void* bias, const void
   const f16* b = static_cast<const f16*>(bias);
   const f16* r = static_cast<const f16*>(R);
   f16* c = static_cast<f16*>(C);
-  // the in-order stream-K form exists for the persistent 256 x 256 tiles only
-  constexpr bool kCanOrder = BM == 256 && BN == 256;
+  // the in-order stream-K form exists for the persistent 256 x 256 and 256 x 384 tiles only
+  constexpr bool kCanOrder = BM == 256 && (BN == 256 || BN == 384);
 #define EE_GEMM_LAUNCH(E)                                                                                       \
   if (kCanOrder && os.extra > 0)                                                                                \
     hipLaunchKernelGGL((gemm_f16_mfma_kernel<MF, BM, BN, WGM, WGN, E, WDEPTH, kCanOrder>), grid, block, 0, s, a, \
@@ -929,7 +941,9 @@ namespace {
 // In-order stream-K scratch: the flags, then one partial 256 x 256 tile per
 // workgroup that takes part.
 constexpr int kOrderedMaxWgs = 256;
-constexpr size_t kOrderedTileBytes = (size_t)256 * 256 * 4;
+// one partial tile: 256 rows of bn fp32 sums; the scratch holds the widest
+constexpr size_t ordered_tile_bytes(int bn) { return (size_t)256 * bn * 4; }
+constexpr size_t kOrderedTileBytes = ordered_tile_bytes(384);
 // The fewest K tiles in a piece (2048 of K): a shorter one spends much of its
 // time on its prologue and on storing or loading partial sums (the TP-shard
 // out projection, K = 3072, ran 5% slower split into pieces of 18 K tiles).
@@ -954,18 +968,18 @@ unsigned long long next_ordered_tag() {
 // Its pieces each cover at least 1/rounds of a tile, so two pieces of one
 // tile never share a slot; a workgroup with more than one tile's worth of
 // extra steps would end later than the plain last round.
-int64_t ordered_wgs(int64_t M, int N, int K, int wgs, size_t bytes) {
-  if (bytes < kOrderedFlagBytes + 2 * kOrderedTileBytes || wgs > kOrderedMaxWgs) return 0;
-  const int64_t n_tiles = ((M + 255) / 256) * ((N + 255) / 256);
-  const int slots = (int)std::min<size_t>((bytes - kOrderedFlagBytes) / kOrderedTileBytes, kOrderedMaxWgs);
+int64_t ordered_wgs(int64_t M, int N, int K, int wgs, size_t bytes, int bn = 256) {
+  if (bytes < kOrderedFlagBytes + 2 * ordered_tile_bytes(bn) || wgs > kOrderedMaxWgs) return 0;
+  const int64_t n_tiles = ((M + 255) / 256) * ((N + bn - 1) / bn);
+  const int slots = (int)std::min<size_t>((bytes - kOrderedFlagBytes) / ordered_tile_bytes(bn), kOrderedMaxWgs);
   return ordered_split_wgs(n_tiles, wgs, K / kBK, slots, kOrderedMinPiece);
 }
 
-OrderedSplit ordered_split(int64_t M, int N, int K, int wgs, void* scratch, size_t bytes) {
+OrderedSplit ordered_split(int64_t M, int N, int K, int wgs, void* scratch, size_t bytes, int bn) {
   OrderedSplit os{};
-  const int64_t p = scratch ? ordered_wgs(M, N, K, wgs, bytes) : 0;
+  const int64_t p = scratch ? ordered_wgs(M, N, K, wgs, bytes, bn) : 0;
   if (p == 0) return os;
-  const int64_t n_tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  const int64_t n_tiles = ((M + 255) / 256) * ((N + bn - 1) / bn);
   const int64_t rounds = n_tiles / wgs, extra = n_tiles - rounds * wgs;
   os.flags = static_cast<unsigned long long*>(scratch);
   os.tag = next_ordered_tag();
@@ -1049,7 +1063,17 @@ int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[kGemmMaxParts], si
   const double t_split = rows_w > 0 ? (double)(m_tiles * tn / cus) * wide_cost + t_rest +
                                           (n_rest > 0 ? kLaunchCost : 0.0)
                                     : 1e30;
-  const double t_all = mt * tn >= cus ? (double)((mt * tn + cus - 1) / cus) * wide_cost : 1e30;
+  const int64_t tiles_w = mt * tn;
+  const double t_all = tiles_w >= cus ? (double)((tiles_w + cus - 1) / cus) * wide_cost : 1e30;
+  // every row on 256 x 384 tiles, the partial last round as in-order
+  // stream-K pieces of the same launch
+  const bool ord = vec_stores && tiles_w >= cus && tiles_w % cus != 0 &&
+                   ordered_wgs(M, N, K, cus, ordered_bytes, 384) > 0;
+  const double t_ord = ord ? (double)tiles_w / cus * wide_cost + kLaunchCost : 1e30;
+  if (t_ord < t_all && t_ord <= t_split && t_ord < t_square) {
+    parts[0] = GemmPart{0, M, kGemmWide, true};
+    return 1;
+  }
   if (t_all <= t_split && t_all < t_square) {
     parts[0] = GemmPart{0, M, kGemmWide, false};
     return 1;
@@ -1072,9 +1096,10 @@ hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W,
   f16* c = static_cast<f16*>(C) + p.row0 * ld.c;
   const int M = (int)p.rows;
   const int wgs = EE_GEMM_PERSIST ? device_cu_count() : 0;
-  const int64_t tiles = ((int64_t)(M + 255) / 256) * ((N + 255) / 256);
+  const int bn = p.cfg == kGemmWide ? 384 : 256;
+  const int64_t tiles = ((int64_t)(M + 255) / 256) * ((N + bn - 1) / bn);
   const OrderedSplit os = p.ordered && wgs > 0
-                              ? ordered_split(M, N, K, (int)std::min<int64_t>(tiles, wgs), ordered, ordered_bytes)
+                              ? ordered_split(M, N, K, (int)std::min<int64_t>(tiles, wgs), ordered, ordered_bytes, bn)
                               : OrderedSplit{};
   switch (p.cfg) {
     case kGemmBig2:
@@ -1084,7 +1109,7 @@ hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W,
       return launch_cfg<EE_GEMM_MF, 256, 256, EE_GEMM_WGM, EE_GEMM_WGN, 3>(a, W, bias, r, M, N, K, ld, epi, form, c, 1,
                                                                           nullptr, s, wgs, os);
     case kGemmWide:
-      return launch_cfg<16, 256, 384, 2, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s, wgs);
+      return launch_cfg<16, 256, 384, 2, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s, wgs, os);
     case kGemm128x64: return launch_cfg<32, 128, 64, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
     case kGemm128x128: return launch_cfg<32, 128, 128, 2, 2>(a, W, bias, r, M, N, K, ld, epi, form, c, 1, nullptr, s);
   }
@@ -1104,15 +1129,18 @@ const char* gemm_f16_kernel_label(int cfg, ee_epilogue epi, bool ordered) {
       EE_L("16, 256, 384, 2, 2"),
 #undef EE_L
   };
-  static const char* const ordered_labels[2][4] = {
+  static const char* const ordered_labels[3][4] = {
       {"gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 0, 2, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 1, 2, true>",
        "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 2, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 2, true>"},
       {"gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 0, 3, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 1, 3, true>",
        "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 2, 3, true>", "gemm_f16_mfma_kernel<16, 256, 256, 2, 2, 3, 3, true>"},
+      {"gemm_f16_mfma_kernel<16, 256, 384, 2, 2, 0, 2, true>", "gemm_f16_mfma_kernel<16, 256, 384, 2, 2, 1, 2, true>",
+       "gemm_f16_mfma_kernel<16, 256, 384, 2, 2, 2, 2, true>", "gemm_f16_mfma_kernel<16, 256, 384, 2, 2, 3, 2, true>"},
   };
   const int e = (int)epi;
   if (cfg < 0 || cfg > kGemmWide || e < 0 || e > 3) return "gemm_f16_mfma_kernel";
-  return ordered && cfg <= kGemmBig3 ? ordered_labels[cfg][e] : labels[cfg][e];
+  if (ordered && cfg <= kGemmBig3) return ordered_labels[cfg][e];
+  return ordered && cfg == kGemmWide ? ordered_labels[2][e] : labels[cfg][e];
 }
 
 
