@@ -217,13 +217,14 @@ def test_gemm_integer_exact_request_stream_rows(M, N):
 # (M, N, K, epi): 256 x 256 tile counts that leave the persistent launch's last
 # round partial, with whole rounds R and extra tiles E of 256 workgroups, split
 # over P of them: R 23 / E 95 / P 190 (pieces of 32 K tiles), R 2 / E 100 /
-# P 200 (the TP-shard QKV), R 3 / E 48 / P 96 and P 128 (the TP-shard out
-# projection and FC2 widths, K = 4096 and 49152), R 6 / E 81 / P 162 with the
-# residual, and R 1 / E 16 (too few rounds: the row split instead).  N is not
-# a multiple of 384 where 256 x 384 tiles would be planned instead.
+# P 200 (the TP-shard QKV), R 3 / E 48 / P 96 (the TP-shard out projection
+# width, K = 4096), R 3 / E 65 / P 130 (three W stages, K = 49152), R 6 / E
+# 81 / P 162 with the residual, and R 1 / E 16 (too few rounds: the row split
+# instead).  N is not a multiple of 384 where 256 x 384 tiles would be planned
+# instead (the plans: tests/test_gemm_plan.py).
 ORDERED = [(7889, 49408, 4096, ee.EPI_BIAS_GELU), (4205, 9216, 4096, ee.EPI_BIAS),
            (4205, 12288, 4096, ee.EPI_BIAS_RESIDUAL), (8436, 12544, 4096, ee.EPI_BIAS_RESIDUAL),
-           (4205, 12288, 49152, ee.EPI_BIAS_RESIDUAL), (4300, 4096, 512, ee.EPI_NONE)]
+           (4205, 12544, 49152, ee.EPI_BIAS_RESIDUAL), (4300, 4096, 512, ee.EPI_NONE)]
 
 
 @pytest.fixture(scope="module")
@@ -356,8 +357,8 @@ def test_gemm_integer_exact_long_k(K):
 # rounds of them (16 rounds at 8192 x 49152; 6 at 4096 x 36864), and rows
 # past the whole rounds on the 256 x 256 plan's smaller tiles (7889 rows: 209
 # rows on 128 x 128 tiles; 4205 rows: 109 rows on 128 x 64 tiles)
-WIDE = [(8192, 49152, 4096, ee.EPI_BIAS_GELU), (7889, 49152, 4096, ee.EPI_BIAS),
-        (4096, 36864, 1024, ee.EPI_BIAS_RESIDUAL), (4205, 12288, 512, ee.EPI_NONE)]
+WIDE = [(8192, 49152, 8192, ee.EPI_BIAS_GELU), (7889, 49152, 4096, ee.EPI_BIAS),
+        (4096, 36864, 8192, ee.EPI_BIAS_RESIDUAL), (4205, 12288, 12288, ee.EPI_NONE)]
 WIDE_LABEL = "gemm_f16_mfma_kernel<16, 256, 384, 2, 2, {}, 2, false>"
 
 
@@ -391,7 +392,7 @@ def test_gemm_wide_tile_matches_square_tile(M, N, K, epi):
     assert not diff, f"{len(diff)} rows differ, first {diff[:8]}"
 
 
-@pytest.mark.parametrize("M,N,K", [(8192, 49152, 4096), (7889, 36864, 1024)])
+@pytest.mark.parametrize("M,N,K", [(8192, 49152, 8192), (7889, 36864, 1024)])
 def test_gemm_wide_tile_integer_exact(M, N, K):
     """Small-integer operands on 256 x 384 tiles (and the rows after their
     whole rounds): two rows of every 256-row tile, over all N, are the fp16

@@ -55,6 +55,7 @@
 
 #include "device_common.h"
 #include "gemm_ordered_split.h"
+#include "gemm_plan.h"
 #include "gemm_tile_order.h"
 #include "internal.h"
 #include "lds_dma.h"
@@ -289,7 +290,6 @@ struct OrderedSplit {
   unsigned long long tag;     // unique per launch
   int rounds, extra, wgs;
 };
-constexpr size_t kOrderedFlagBytes = 4096;
 // Polls of a predecessor's flag (about 0.25 us apart) before a piece gives up
 // and recomputes its tile from K tile 0: only if the predecessor never ran,
 // which a launch of at most one workgroup per CU, alone on the device, rules out.
@@ -601,7 +601,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f16_mfma_kernel(const f16
       __builtin_amdgcn_sched_barrier(0);
     });
   };
-  // nk >= 2 (the host gives this tile K >= 2 * kBK)
+  // nk >= 1: a K loop of one K tile loads tile 0 twice (stage 1 is read by no step)
   auto k_loop_wide = [&](int nk, auto Z0) __attribute__((always_inline)) {
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -912,43 +912,7 @@ bool gemm_f16_mfma_ok(int64_t M, int N, int K, const GemmPitch& ld, const void* 
   return M >= 1 && M <= (1 << 30) && N >= 1 && K >= kBK && K % kBK == 0 && pitches && aligned;
 }
 
-// Time of a 128 x 128 tile relative to a 256 x 256 tile of the same K (a
-// quarter of the work at a lower MFMA rate).
-constexpr double kSmallTileCost = 0.36;
-
-// Rows [0, m_big) of a large problem go to the 256 x 256 kernel and the rest
-// to 128 x 128 tiles.  A tile count just past a multiple of the CU count
-// leaves most CUs idle in the last round of 256 x 256 tiles; running only
-// whole rounds of 256-row tiles there and the remaining rows as 128 x 128
-// tiles ends sooner.  Both kernels add an element's K tiles in the same order;
-// their MFMA shapes differ (16x16x32 and 32x32x16), and on gfx950 they give
-// the same bits for every element (tested on random data against GEMMs run
-// on each 256-row block alone), so the split changes no results.
-int64_t gemm_big_rows(int64_t M, int N, int cus) {
-  const int64_t tn = (N + 255) / 256, tiles = ((M + 255) / 256) * tn;
-  const int64_t whole = tiles / cus * cus;
-  if (whole == tiles) return M;
-  const int64_t m_tiles = whole / tn;  // 256-row tiles that fit in the whole rounds
-  const int64_t rest = M - m_tiles * 256;
-  if (m_tiles <= 0 || rest <= 0) return M;
-  const int64_t small = ((rest + 127) / 128) * ((N + 127) / 128);
-  const double t_plain = (double)((tiles + cus - 1) / cus);
-  const double t_split = (double)((m_tiles * tn + cus - 1) / cus) + kSmallTileCost * (double)((small + cus - 1) / cus);
-  return t_split < t_plain ? m_tiles * 256 : M;
-}
-
 namespace {
-// In-order stream-K scratch: the flags, then one partial 256 x 256 tile per
-// workgroup that takes part.
-constexpr int kOrderedMaxWgs = 256;
-// one partial tile: 256 rows of bn fp32 sums; the scratch holds the widest
-constexpr size_t ordered_tile_bytes(int bn) { return (size_t)256 * bn * 4; }
-constexpr size_t kOrderedTileBytes = ordered_tile_bytes(384);
-// The fewest K tiles in a piece (2048 of K): a shorter one spends much of its
-// time on its prologue and on storing or loading partial sums (the TP-shard
-// out projection, K = 3072, ran 5% slower split into pieces of 18 K tiles).
-constexpr int kOrderedMinPiece = 32;
-
 // A tag no earlier launch of this process used, nor (but with probability
 // 2^-64) one of another process that left flags in the same memory.
 unsigned long long next_ordered_tag() {
@@ -961,18 +925,6 @@ unsigned long long next_ordered_tag() {
   do v = ++ctr;
   while (v == 0);
   return v;
-}
-
-// The in-order stream-K split of a persistent 256 x 256 launch of `wgs`
-// workgroups, or none (extra == 0) without scratch or where it gains nothing.
-// Its pieces each cover at least 1/rounds of a tile, so two pieces of one
-// tile never share a slot; a workgroup with more than one tile's worth of
-// extra steps would end later than the plain last round.
-int64_t ordered_wgs(int64_t M, int N, int K, int wgs, size_t bytes, int bn = 256) {
-  if (bytes < kOrderedFlagBytes + 2 * ordered_tile_bytes(bn) || wgs > kOrderedMaxWgs) return 0;
-  const int64_t n_tiles = ((M + 255) / 256) * ((N + bn - 1) / bn);
-  const int slots = (int)std::min<size_t>((bytes - kOrderedFlagBytes) / ordered_tile_bytes(bn), kOrderedMaxWgs);
-  return ordered_split_wgs(n_tiles, wgs, K / kBK, slots, kOrderedMinPiece);
 }
 
 OrderedSplit ordered_split(int64_t M, int N, int K, int wgs, void* scratch, size_t bytes, int bn) {
@@ -992,98 +944,10 @@ OrderedSplit ordered_split(int64_t M, int N, int K, int wgs, void* scratch, size
 
 size_t gemm_f16_ordered_bytes() { return kOrderedFlagBytes + (size_t)kOrderedMaxWgs * kOrderedTileBytes; }
 
-namespace {
-// Time of a 256 x 384 round in 256 x 256 rounds: 1.5 times the work at 4.5%
-// less time per flop (FC1, QKV and out GEMMs at 8192 rows, same process); at
-// K >= EE_GEMM_DEEP_W_K, against the three-W-stage 256 x 256 kernel, 10% less
-// (FC2 at 4096, 8125 and 8192 rows).
-constexpr double kWideRoundCost = 1.43;
-constexpr double kWideRoundCostLongK = 1.35;
-// What a second launch costs beyond its rounds: its first and last tiles'
-// loads and stores are not overlapped with another tile's MFMAs.
-constexpr double kLaunchCost = 0.05;
-
-// The 256 x 256 plan of rows [row0, row0 + M): one or two parts; *rounds
-// gets its estimated time in 256 x 256 rounds.
-int plan_square(int64_t row0, int64_t M, int N, int K, GemmPart* parts, size_t ordered_bytes, bool vec_stores,
-                int cus, double* rounds) {
-  const int64_t tiles_big = ((M + 255) / 256) * ((N + 255) / 256);
-  if (tiles_big < cus) {
-    // the rows after another part's whole rounds stream all of W through few
-    // tiles: 128 x 64 tiles (the same MFMA shape) put twice as many CUs on it
-    const int64_t small = ((M + 127) / 128) * ((N + 127) / 128);
-    const bool narrow = row0 > 0 && small * 2 <= cus;
-    *rounds = kSmallTileCost * (double)((small + cus - 1) / cus);
-    parts[0] = GemmPart{row0, M, narrow ? kGemm128x64 : kGemm128x128, false};
-    return 1;
-  }
-  const int big = K >= EE_GEMM_DEEP_W_K ? kGemmBig3 : kGemmBig2;
-  if (EE_GEMM_PERSIST && vec_stores &&
-      ordered_wgs(M, N, K, (int)std::min<int64_t>(tiles_big, cus), ordered_bytes) > 0) {
-    *rounds = (double)tiles_big / cus + kLaunchCost;
-    parts[0] = GemmPart{row0, M, big, true};  // the launch splits its partial last round itself
-    return 1;
-  }
-  const int64_t m_big = gemm_big_rows(M, N, cus);
-  parts[0] = GemmPart{row0, m_big, big, false};
-  const int64_t tn = (N + 255) / 256;
-  *rounds = (double)((((m_big + 255) / 256) * tn + cus - 1) / cus);
-  if (m_big == M) return 1;
-  // Few remaining rows stream all of W through few tiles: 128 x 64 tiles
-  // (the same MFMA shape) put twice as many CUs on it.
-  const int64_t rest = M - m_big;
-  const int64_t small = ((rest + 127) / 128) * ((N + 127) / 128);
-  const bool narrow = small * 2 <= cus;
-  *rounds += kSmallTileCost * (double)((small + cus - 1) / cus);
-  parts[1] = GemmPart{row0 + m_big, rest, narrow ? kGemm128x64 : kGemm128x128, false};
-  return 2;
-}
-}  // namespace
-
 int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[kGemmMaxParts], size_t ordered_bytes,
                    bool vec_stores) {
-  if (M <= 0) return 0;
-  const int cus = device_cu_count();
-  double t_square = 0.0;
-  const int n_square = plan_square(0, M, N, K, parts, ordered_bytes, vec_stores, cus, &t_square);
-  if (!(EE_GEMM_WIDE && EE_GEMM_PERSIST && N % 384 == 0 && K >= 2 * kBK)) return n_square;
-  const double wide_cost = K >= EE_GEMM_DEEP_W_K ? kWideRoundCostLongK : kWideRoundCost;
-  // 256 x 384 tiles on the rows that fill whole rounds of them (M tiles in
-  // groups of `step`), the rest on the 256 x 256 plan; or on every row, the
-  // last round partial.  Taken where the estimate ends sooner.
-  const int64_t tn = N / 384, mt = (M + 255) / 256;
-  const int64_t step = cus / std::gcd<int64_t>(cus, tn);
-  const int64_t m_tiles = mt / step * step;
-  const int64_t rows_w = std::min<int64_t>(M, m_tiles * 256);
-  GemmPart rest[kGemmMaxParts - 1];
-  double t_rest = 0.0;
-  const int n_rest = rows_w < M && rows_w > 0
-                         ? plan_square(rows_w, M - rows_w, N, K, rest, ordered_bytes, vec_stores, cus, &t_rest)
-                         : 0;
-  const double t_split = rows_w > 0 ? (double)(m_tiles * tn / cus) * wide_cost + t_rest +
-                                          (n_rest > 0 ? kLaunchCost : 0.0)
-                                    : 1e30;
-  const int64_t tiles_w = mt * tn;
-  const double t_all = tiles_w >= cus ? (double)((tiles_w + cus - 1) / cus) * wide_cost : 1e30;
-  // every row on 256 x 384 tiles, the partial last round as in-order
-  // stream-K pieces of the same launch
-  const bool ord = vec_stores && tiles_w >= cus && tiles_w % cus != 0 &&
-                   ordered_wgs(M, N, K, cus, ordered_bytes, 384) > 0;
-  const double t_ord = ord ? (double)tiles_w / cus * wide_cost + kLaunchCost : 1e30;
-  if (t_ord < t_all && t_ord <= t_split && t_ord < t_square) {
-    parts[0] = GemmPart{0, M, kGemmWide, true};
-    return 1;
-  }
-  if (t_all <= t_split && t_all < t_square) {
-    parts[0] = GemmPart{0, M, kGemmWide, false};
-    return 1;
-  }
-  if (t_split < t_square) {
-    parts[0] = GemmPart{0, rows_w, kGemmWide, false};
-    for (int i = 0; i < n_rest; ++i) parts[1 + i] = rest[i];
-    return 1 + n_rest;
-  }
-  return n_square;
+  return gemm_plan_parts(M, N, K, parts, ordered_bytes, vec_stores,
+                         GemmPlanOpts{device_cu_count(), EE_GEMM_PERSIST != 0, EE_GEMM_WIDE != 0, EE_GEMM_DEEP_W_K});
 }
 
 hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W, const void* bias, const void* R,

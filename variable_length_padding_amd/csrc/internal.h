@@ -7,6 +7,7 @@
 #include <cstdint>
 
 #include "ee.h"
+#include "gemm_plan.h"
 
 namespace ee {
 
@@ -115,16 +116,10 @@ hipError_t launch_gemm_f16_mfma(const void* A, const void* W, const void* bias, 
 // persistent launch when given `ordered` scratch of gemm_f16_ordered_bytes()
 // (bit-identical to whole tiles); without it, whole rounds of 256-row tiles
 // and the remaining rows as a second part on smaller tiles.
-enum { kGemmBig2 = 0, kGemmBig3 = 1, kGemm128x128 = 2, kGemm128x64 = 3, kGemmWide = 4 };
-struct GemmPart {
-  int64_t row0, rows;
-  int cfg;
-  bool ordered;  // its partial last round as in-order stream-K pieces
-};
+// (The parts, GemmPart and the plan itself: gemm_plan.h.)
 size_t gemm_f16_ordered_bytes();
 // Number of parts (0 for M <= 0).  vec_stores: N and C's pitch are multiples
 // of 8 and C and the residual 16-byte aligned (the ordered form needs it).
-constexpr int kGemmMaxParts = 3;
 int gemm_f16_parts(int64_t M, int N, int K, GemmPart (&parts)[kGemmMaxParts], size_t ordered_bytes, bool vec_stores);
 hipError_t launch_gemm_f16_part(const GemmPart& p, const void* A, const void* W, const void* bias, const void* R,
                                 int N, int K, const GemmPitch& ld, ee_epilogue epi, ee_gelu form, void* C,
