@@ -56,9 +56,9 @@ PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 ROOFLINE_SITE = "gemm_fc1"
 PROFILES = os.path.join(ROOT, "profiles")
-# the GEMM kernel's source and the headers that shape its loads and tile order
+# the GEMM kernel's source and the headers that shape its loads, tile order and epilogue arithmetic
 GEMM_SOURCES = [os.path.join(ROOT, "variable_length_padding_amd", "csrc", f)
-                for f in ("gemm_f16.hip", "gemm_tile_order.h", "lds_dma.h")]
+                for f in ("gemm_f16.hip", "gemm_tile_order.h", "lds_dma.h", "device_common.h")]
 DEFAULT_WORKLOAD = "gpt3-48l-stream"
 
 

@@ -205,6 +205,9 @@ __device__ __forceinline__ half4 tr_read(const f16* p) {
 
 // Waves per SIMD the register budget is sized for.  Three (166 VGPRs at
 // head_dim 128) ran at the same speed as two on the GPT-3 shapes; four spills.
+#ifndef EE_ATTN_SEQ_MAJOR
+#define EE_ATTN_SEQ_MAJOR 1
+#endif
 #ifndef EE_ATTN_WAVES_PER_SIMD
 #define EE_ATTN_WAVES_PER_SIMD 2
 #endif
@@ -235,7 +238,13 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
   static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
   __shared__ __attribute__((aligned(16))) f16 smem[2 * 2 * TILE];  // [stage][K | V]
 
+#if EE_ATTN_SEQ_MAJOR
+  // grid (query tiles, heads, sequences): the workgroups of one sequence's
+  // heads run together, so each packed row is read in one stretch of time
+  const int b = blockIdx.z, head = blockIdx.y;
+#else
   const int b = blockIdx.y, head = blockIdx.z;
+#endif
   const int s0 = cu[b];
   const int L = cu[b + 1] - s0;  // queries (all the sequence's rows, or its new tokens)
   const int q_start = blockIdx.x * kQB;
@@ -485,8 +494,9 @@ void launch_mfma(const AttnAddr& ad, const int32_t* cu, int B, int max_len, int 
   // offsets, up to row k0 + kKB - 1 of the last key tile (past the sequence's
   // end: those loads fall outside the descriptor's range and read zeros)
   if ((hd == 64 || hd == 128) && attn_tr_offsets_fit(max_len, ad.in_row_stride)) {
-    if (hd == 64) hipLaunchKernelGGL((attn_tr_kernel<64, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
-    else hipLaunchKernelGGL((attn_tr_kernel<128, CAUSAL>), grid, block, 0, s, ad, cu, scale_log2);
+    const dim3 tgrid = EE_ATTN_SEQ_MAJOR ? dim3(grid.x, grid.z, grid.y) : grid;
+    if (hd == 64) hipLaunchKernelGGL((attn_tr_kernel<64, CAUSAL>), tgrid, block, 0, s, ad, cu, scale_log2);
+    else hipLaunchKernelGGL((attn_tr_kernel<128, CAUSAL>), tgrid, block, 0, s, ad, cu, scale_log2);
     return;
   }
   switch (hd) {
@@ -537,7 +547,9 @@ hipError_t launch_cache_attention_mfma(ee_dtype dt, const void* qkv, const Exten
   const int64_t Hp = (int64_t)nh * hd;
   const AttnAddr ad{qkv, nullptr, nullptr, o, 0, hd, 3 * Hp, 0, hd, Hp, 1};
   const CacheKV kv{arg, static_cast<const f16*>(kc), static_cast<const f16*>(vc), capacity};
-  const dim3 grid((unsigned)((max_new + kQB - 1) / kQB), (unsigned)B, (unsigned)nh), block(256);
+  const dim3 grid = EE_ATTN_SEQ_MAJOR ? dim3((unsigned)((max_new + kQB - 1) / kQB), (unsigned)nh, (unsigned)B)
+                                       : dim3((unsigned)((max_new + kQB - 1) / kQB), (unsigned)B, (unsigned)nh);
+  const dim3 block(256);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (hd == 64)
     hipLaunchKernelGGL((attn_tr_kernel<64, true, CacheKV>), grid, block, 0, s, ad, cu, scale_log2, kv);
