@@ -105,7 +105,13 @@ def test_the_layers_plans(plan):
         (7889, 49152, 4096, 0, 0): [(0, 7680, WIDE, 0), (7680, 209, T128, 0)],
         (7889, 49152, 1024, 0, 0): [(0, 7680, WIDE, 0), (7680, 209, T128, 0)],
         (4205, 12288, 12288, 0, 0): [(0, 4096, WIDE, 0), (4096, 109, T64, 0)],
-        (7889, 36864, 1024, 0, 0): [(0, 6144, WIDE, 0), (6144, 1745, BIG2, 0)],
+        (7889, 36864, 1024, 0, 0): [(0, 7889, BIG2, 0)],
+        # whole wide rounds, then the 256 x 256 plan for the remaining rows
+        (2700, 36864, 12288, 0, 0): [(0, 2048, WIDE, 0), (2048, 652, BIG2, 0)],
+        # the request stream's QKV at 31 M-tiles: wide tiles on every row, the
+        # last round 62% full (a 256 x 256 launch for the last 1745 rows after
+        # 9 wide rounds measured 3.4% slower)
+        (7889, 36864, 12288, WS, 1): [(0, 7889, WIDE, 0)],
         (4205, 12288, 49152, 0, 0): [(0, 4096, WIDE, 0), (4096, 109, T64, 0)],
         (8457, 12288, 49152, 0, 0): [(0, 8192, WIDE, 0), (8192, 265, T128, 0)],
         # ... and with a workspace, as in-order pieces of one launch

@@ -64,6 +64,13 @@ constexpr int kWideMinGainK = 8192;
 // a launch beyond its rounds (its first and last tiles' loads and stores
 // overlap no other tile's MFMAs; a split's partial sums).
 constexpr double kLaunchCost = 0.05;
+// the 256 x 256 plan of the rows left after whole rounds of 256 x 384 tiles,
+// per estimated round: few M tiles, whose leftover tiles the tile order cannot
+// deal to the XCDs in step (the request stream's QKV GEMM at 7889 rows: its
+// last 1745 rows at 1076 TFLOP/s against 1430 for the wide rounds; 256 x 384
+// tiles on every row, the last round 62% full, ran 3.4% faster than the two
+// launches that the estimate without this factor chose).
+constexpr double kWideRestSquareCost = 1.25;
 
 // Workgroups among which a persistent launch of `wgs` workgroups over tiles
 // 256 rows by bn columns shares its partial last round, or 0 (no split:
@@ -161,8 +168,11 @@ inline int gemm_plan_parts(int64_t M, int N, int K, GemmPart* parts, size_t orde
   const int n_rest = rows_w < M && rows_w > 0
                          ? gemm_plan_square(rows_w, M - rows_w, N, K, rest, ordered_bytes, vec_stores, o, &t_rest)
                          : 0;
-  const double t_split =
-      rows_w > 0 ? (double)(m_tiles * tn / cus) * wide_cost + t_rest + (n_rest > 0 ? kLaunchCost : 0.0) : 1e30;
+  const bool rest_square = n_rest > 0 && (rest[0].cfg == kGemmBig2 || rest[0].cfg == kGemmBig3);
+  const double t_split = rows_w > 0 ? (double)(m_tiles * tn / cus) * wide_cost +
+                                          t_rest * (rest_square ? kWideRestSquareCost : 1.0) +
+                                          (n_rest > 0 ? kLaunchCost : 0.0)
+                                    : 1e30;
   const double t_all = tiles_w >= cus ? (double)((tiles_w + cus - 1) / cus) * wide_cost : 1e30;
   const int64_t p_w =
       vec_stores && tiles_w >= cus && tiles_w % cus != 0 ? ordered_wgs(M, N, K, cus, ordered_bytes, 384) : 0;
