@@ -205,6 +205,12 @@ __device__ __forceinline__ half4 tr_read(const f16* p) {
 
 // Waves per SIMD the register budget is sized for.  Three (166 VGPRs at
 // head_dim 128) ran at the same speed as two on the GPT-3 shapes; four spills.
+#ifndef EE_ATTN_LEAN
+#define EE_ATTN_LEAN 1
+#endif
+// Growth of a row's maximum (exp2 units) that the lean softmax absorbs before
+// it rescales: probabilities stay below 2^8.
+constexpr float kAttnSlack = 8.0f;
 #ifndef EE_ATTN_SEQ_MAJOR
 #define EE_ATTN_SEQ_MAJOR 1
 #endif
@@ -351,6 +357,46 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sacc, 0, 0, 0);
       }
       // element e: key k0 + (e/4)*8 + hk*4 + e%4, query qi
+#if EE_ATTN_LEAN
+      // Masking only where the tile reaches past the wave's first query
+      // (causal) or past the sequence; the scale goes into the exponent's fma.
+      // The running maximum m_run (in exp2 units) is raised only when some row
+      // of the wave exceeds it by more than kAttnSlack: until then the rows'
+      // p = 2^(s - m_run) stay below 2^kAttnSlack (fine in fp16) and the
+      // output accumulator is not rescaled.  The final division by l_run
+      // cancels whichever maximum was used.
+      const bool edge = CAUSAL ? k0 + kKB - 1 > ctx + q0 : k0 + kKB > Lk;
+      if (edge) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int key = k0 + (e >> 2) * 8 + hk * 4 + (e & 3);
+          if (!(CAUSAL ? key <= qpos : key < Lk)) sacc[e] = -INFINITY;
+        }
+      }
+      float mloc = sacc[0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sacc[e]);
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave)) * scale_log2;
+      float alpha = 1.f;
+      const bool rescale = __any(mloc > m_run + kAttnSlack);
+      if (rescale) {
+        const float m_new = fmaxf(m_run, mloc);  // finite: the first tile holds key 0 <= qi
+        alpha = exp2f(m_run - m_new);
+        m_run = m_new;
+      }
+      half8 p0, p1;
+      float rs = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float a = exp2f(__builtin_fmaf(sacc[e], scale_log2, -m_run));
+        const float b = exp2f(__builtin_fmaf(sacc[8 + e], scale_log2, -m_run));
+        p0[e] = (f16)a;
+        p1[e] = (f16)b;
+        rs += a + b;
+      }
+      rs += __shfl_xor(rs, 32, kWave);
+      l_run = l_run * alpha + rs;
+#else
       float mloc = -INFINITY;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -374,10 +420,14 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
       rs += __shfl_xor(rs, 32, kWave);
       l_run = l_run * alpha + rs;
       m_run = m_new;
+      const bool rescale = true;
+#endif
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
+        if (rescale) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+          for (int e = 0; e < 16; ++e) oacc[d][e] *= alpha;
+        }
         // keys 0..15 of the tile (slots: 8h + 4hk + j), then 16..31
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
