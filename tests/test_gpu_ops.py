@@ -623,6 +623,47 @@ def test_attention_long_sequences(dtype, hd, nh, tol, causal):
     assert err <= tol
 
 
+@pytest.mark.parametrize("hd", [128, 64])
+@pytest.mark.parametrize("causal", [True, False])
+def test_attention_growing_and_spiking_scores(hd, causal):
+    """Scores that rise along the sequence: by about 1.4 per key (log2 units)
+    on one sequence and in one jump of ~115 at a late key on another, so the
+    running maximum of the softmax moves by far more than its slack between
+    key tiles (rescales); and by about 0.2 per key on a third, below the
+    slack (kept maxima, probabilities above 1 before the final division).
+    Against the oracle, causal and bidirectional."""
+    nh = 2
+    lens = [300, 257, 200, 40]
+    cu_h = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, Hp = int(cu_h[-1]), nh * hd
+    g = torch.Generator().manual_seed(7)
+    q = 0.5 + 0.05 * torch.randn(T, Hp, generator=g)
+    k = 0.05 * torch.randn(T, Hp, generator=g)
+    v = torch.randn(T, Hp, generator=g)
+    # sequence 0: k_j grows linearly, so q.k_j / sqrt(hd) rises ~1 per key at the end
+    r0 = torch.arange(lens[0], dtype=torch.float32)
+    k[:lens[0]] += (r0 / lens[0] * 2.0 * 300 / (0.5 * hd ** 0.5))[:, None] * 0.5
+    # sequence 1: one key (position 220) far above the rest
+    k[cu_h[1] + 220] += 80.0 / (0.5 * hd ** 0.5)
+    # sequence 2: a slow rise, ~0.2 per key in log2 units (~7 per key tile:
+    # below the slack, so maxima are kept and probabilities exceed 1)
+    r2 = torch.arange(lens[2], dtype=torch.float32)
+    k[cu_h[2]:cu_h[3]] += (0.15 * r2 / (0.5 * hd ** 0.5))[:, None]
+    qkv = torch.cat([q, k, v], dim=1).half()
+    o = torch.empty(T, Hp, dtype=torch.float16, device=DEV)
+    ee.ee_attention_varlen(qkv.to(DEV), torch.tensor(cu_h, device=DEV), len(lens), max(lens), nh, hd, o,
+                           causal=causal)
+    torch.cuda.synchronize()
+    qkv64 = qkv.double().numpy()
+    ref = (oracle.causal_attention_packed(qkv64, cu_h, nh, hd) if causal
+           else oracle.attention_packed_bidirectional(qkv64, cu_h, nh, hd))
+    got = to_host64(o)
+    assert np.isfinite(got).all()
+    err = normwise_rel(got, ref)
+    say(f"attention growing/spiking scores hd={hd} causal={causal}: rel {err:.2e}")
+    assert err <= 3e-3
+
+
 def test_attention_sequences_are_independent():
     """Permuting the sequences of the batch permutes the output rows exactly."""
     nh, hd = 4, 128
