@@ -203,17 +203,12 @@ __device__ __forceinline__ half4 tr_read(const f16* p) {
   return __builtin_bit_cast(half4, v);
 }
 
+// Growth of a row's maximum (exp2 units) that the softmax of attn_tr_kernel
+// absorbs before it rescales: probabilities stay below 2^8.
+constexpr float kAttnSlack = 8.0f;
+
 // Waves per SIMD the register budget is sized for.  Three (166 VGPRs at
 // head_dim 128) ran at the same speed as two on the GPT-3 shapes; four spills.
-#ifndef EE_ATTN_LEAN
-#define EE_ATTN_LEAN 1
-#endif
-// Growth of a row's maximum (exp2 units) that the lean softmax absorbs before
-// it rescales: probabilities stay below 2^8.
-constexpr float kAttnSlack = 8.0f;
-#ifndef EE_ATTN_SEQ_MAJOR
-#define EE_ATTN_SEQ_MAJOR 1
-#endif
 #ifndef EE_ATTN_WAVES_PER_SIMD
 #define EE_ATTN_WAVES_PER_SIMD 2
 #endif
@@ -244,13 +239,9 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
   static_assert(HD == 64 || HD == 128, "head_dim 64 or 128");
   __shared__ __attribute__((aligned(16))) f16 smem[2 * 2 * TILE];  // [stage][K | V]
 
-#if EE_ATTN_SEQ_MAJOR
   // grid (query tiles, heads, sequences): the workgroups of one sequence's
   // heads run together, so each packed row is read in one stretch of time
   const int b = blockIdx.z, head = blockIdx.y;
-#else
-  const int b = blockIdx.y, head = blockIdx.z;
-#endif
   const int s0 = cu[b];
   const int L = cu[b + 1] - s0;  // queries (all the sequence's rows, or its new tokens)
   const int q_start = blockIdx.x * kQB;
@@ -357,7 +348,6 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
         sacc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[kk], sacc, 0, 0, 0);
       }
       // element e: key k0 + (e/4)*8 + hk*4 + e%4, query qi
-#if EE_ATTN_LEAN
       // Masking only where the tile reaches past the wave's first query
       // (causal) or past the sequence; the scale goes into the exponent's fma.
       // The running maximum m_run (in exp2 units) is raised only when some row
@@ -388,40 +378,14 @@ __global__ __launch_bounds__(256, EE_ATTN_WAVES_PER_SIMD) void attn_tr_kernel(At
       float rs = 0.f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float a = exp2f(__builtin_fmaf(sacc[e], scale_log2, -m_run));
-        const float b = exp2f(__builtin_fmaf(sacc[8 + e], scale_log2, -m_run));
-        p0[e] = (f16)a;
-        p1[e] = (f16)b;
-        rs += a + b;
+        const float pa = exp2f(__builtin_fmaf(sacc[e], scale_log2, -m_run));
+        const float pb = exp2f(__builtin_fmaf(sacc[8 + e], scale_log2, -m_run));
+        p0[e] = (f16)pa;
+        p1[e] = (f16)pb;
+        rs += pa + pb;
       }
       rs += __shfl_xor(rs, 32, kWave);
       l_run = l_run * alpha + rs;
-#else
-      float mloc = -INFINITY;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = k0 + (e >> 2) * 8 + hk * 4 + (e & 3);
-        const bool keep = CAUSAL ? key <= qpos : key < Lk;
-        const float v = keep ? sacc[e] * scale_log2 : -INFINITY;
-        sacc[e] = v;
-        mloc = fmaxf(mloc, v);
-      }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, kWave));
-      const float m_new = fmaxf(m_run, mloc);  // finite: the first tile holds key 0 <= qi
-      const float alpha = exp2f(m_run - m_new);
-      half8 p0, p1;
-      float rs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        p0[e] = (f16)exp2f(sacc[e] - m_new);
-        p1[e] = (f16)exp2f(sacc[8 + e] - m_new);
-        rs += (float)p0[e] + (float)p1[e];
-      }
-      rs += __shfl_xor(rs, 32, kWave);
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      const bool rescale = true;
-#endif
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
         if (rescale) {
@@ -544,7 +508,7 @@ void launch_mfma(const AttnAddr& ad, const int32_t* cu, int B, int max_len, int 
   // offsets, up to row k0 + kKB - 1 of the last key tile (past the sequence's
   // end: those loads fall outside the descriptor's range and read zeros)
   if ((hd == 64 || hd == 128) && attn_tr_offsets_fit(max_len, ad.in_row_stride)) {
-    const dim3 tgrid = EE_ATTN_SEQ_MAJOR ? dim3(grid.x, grid.z, grid.y) : grid;
+    const dim3 tgrid(grid.x, grid.z, grid.y);  // (query tiles, heads, sequences)
     if (hd == 64) hipLaunchKernelGGL((attn_tr_kernel<64, CAUSAL>), tgrid, block, 0, s, ad, cu, scale_log2);
     else hipLaunchKernelGGL((attn_tr_kernel<128, CAUSAL>), tgrid, block, 0, s, ad, cu, scale_log2);
     return;
@@ -597,9 +561,7 @@ hipError_t launch_cache_attention_mfma(ee_dtype dt, const void* qkv, const Exten
   const int64_t Hp = (int64_t)nh * hd;
   const AttnAddr ad{qkv, nullptr, nullptr, o, 0, hd, 3 * Hp, 0, hd, Hp, 1};
   const CacheKV kv{arg, static_cast<const f16*>(kc), static_cast<const f16*>(vc), capacity};
-  const dim3 grid = EE_ATTN_SEQ_MAJOR ? dim3((unsigned)((max_new + kQB - 1) / kQB), (unsigned)nh, (unsigned)B)
-                                       : dim3((unsigned)((max_new + kQB - 1) / kQB), (unsigned)B, (unsigned)nh);
-  const dim3 block(256);
+  const dim3 grid((unsigned)((max_new + kQB - 1) / kQB), (unsigned)nh, (unsigned)B), block(256);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)hd);
   if (hd == 64)
     hipLaunchKernelGGL((attn_tr_kernel<64, true, CacheKV>), grid, block, 0, s, ad, cu, scale_log2, kv);
