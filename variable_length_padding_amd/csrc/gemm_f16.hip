@@ -94,6 +94,16 @@ namespace {
 #ifndef EE_GEMM_WIDE_GAP1
 #define EE_GEMM_WIDE_GAP1 5
 #endif
+// Bands of the residual requested ahead in the staged epilogue: 3 on 256 x
+// 256 tiles (the TP-shard out projection, K = 3072, 2-3% faster; no change at
+// K = 12288 and 49152); none on 256 x 384, whose register file has no room
+// (one band ahead added spills and no speed).
+#ifndef EE_GEMM_RES_AHEAD
+#define EE_GEMM_RES_AHEAD 3
+#endif
+#ifndef EE_GEMM_RES_AHEAD_WIDE
+#define EE_GEMM_RES_AHEAD_WIDE 0
+#endif
 #ifndef EE_GEMM_DEEP_W_K
 #define EE_GEMM_DEEP_W_K 32768
 #endif
@@ -189,18 +199,32 @@ __device__ __forceinline__ void store_tile_staged(const typename Frag<MF>::acc_t
     const int cj = col0 + j * MF + lane % MF;
     bcol[j] = (kHasBias<EPI> && cj < N) ? (float)bias[cj] : 0.f;
   }
+  // The residual rows of band b are requested RA bands ahead, while band
+  // b - RA goes through LDS: the registers that held the main loop's operand
+  // fragments are free here, and a request issued at its own band waited
+  // out most of its latency.
+  constexpr int NB = FM / FPB;
+  constexpr int RA = EPI == EE_EPI_BIAS_RESIDUAL ? (FN > 8 ? EE_GEMM_RES_AHEAD_WIDE : EE_GEMM_RES_AHEAD) : 0;
+  constexpr int RS = (RA < NB ? RA : NB - 1) + 1;  // residual band buffers
+  half8 rvb[RS][PASSES];
+  auto load_rv = [&](auto BAND) __attribute__((always_inline)) {
+    constexpr int band = decltype(BAND)::value;
+    if constexpr (EPI == EE_EPI_BIAS_RESIDUAL && band < NB) {
+#pragma unroll
+      for (int it = 0; it < PASSES; ++it) {
+        const int row = row0 + band * SE::kBandRows + it * SE::kRowsPerPass + rsub;
+        if (!to_raw && lane_on && row < M && col < N)
+          rvb[band % RS][it] = *reinterpret_cast<const half8*>(R + (int64_t)row * ldc + col);
+      }
+    }
+  };
+  static_for<0, RS - 1>([&](auto B) __attribute__((always_inline)) { load_rv(B); });
   // bands unrolled by the front end: with GeLU a 12-fragment band is too long
   // for the loop unroller, and an indexed band would put acc in memory
-  static_for<0, FM / FPB>([&](auto BAND) __attribute__((always_inline)) {
+  static_for<0, NB>([&](auto BAND) __attribute__((always_inline)) {
     constexpr int band = decltype(BAND)::value;
-    // the residual of this band is requested before the band goes through LDS
-    half8 rv[PASSES];
-#pragma unroll
-    for (int it = 0; it < PASSES; ++it) {
-      const int row = row0 + band * SE::kBandRows + it * SE::kRowsPerPass + rsub;
-      if (EPI == EE_EPI_BIAS_RESIDUAL && !to_raw && lane_on && row < M && col < N)
-        rv[it] = *reinterpret_cast<const half8*>(R + (int64_t)row * ldc + col);
-    }
+    load_rv(std::integral_constant<int, band + RS - 1>{});
+    half8 (&rv)[PASSES] = rvb[band % RS];
 #pragma unroll
     for (int ii = 0; ii < FPB; ++ii)
 #pragma unroll
