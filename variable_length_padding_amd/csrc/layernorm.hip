@@ -8,7 +8,8 @@
 // which measured faster there (a wave holding a 12288-wide row needs all 256
 // VGPRs and leaves too few rows in flight).  Either way the row is read once into registers with 16-byte loads,
 // reduced twice (mean, then the centred sum of squares, so no cancellation)
-// and written once; gamma/beta are re-read from L2 by every row.
+// and written once.  The workgroup kernel keeps gamma/beta in registers across
+// its rows (the wave kernel re-reads them from L2 by every row).
 #include "device_common.h"
 #include "internal.h"
 
@@ -16,6 +17,7 @@ namespace ee {
 namespace {
 
 constexpr int kLnThreads = 256;
+
 
 __device__ __forceinline__ float block_sum(float v, float* s_red) {
   v = wave_sum(v);
@@ -72,6 +74,21 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* x, const
       }
     }
   };
+  // gamma and beta: the same columns for every row of this thread, so they
+  // are read once into registers (the plain LayerNorm at up to 2048 vectors
+  // per row; the residual-add forms and wider rows have no register room)
+  constexpr bool GB = NORM && !ADD && VPT <= 8;
+  V gam[GB ? VPT : 1], bet[GB ? VPT : 1];
+  if constexpr (GB) {
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = threadIdx.x + i * kLnThreads;
+      if (c < nvec) {
+        gam[i] = reinterpret_cast<const V*>(gamma)[c];
+        bet[i] = reinterpret_cast<const V*>(beta)[c];
+      }
+    }
+  }
   int64_t row = blockIdx.x;
   if (row < rows) load(cur, rcur, row);
   for (; row < rows; row += gridDim.x) {
@@ -114,7 +131,14 @@ __global__ __launch_bounds__(kLnThreads) void layernorm_kernel(const T* x, const
       for (int i = 0; i < VPT; ++i) {
         const int c = threadIdx.x + i * kLnThreads;
         if (c < nvec) {
-          const V g = gv[c], b = bv[c];
+          V g, b;
+          if constexpr (GB) {
+            g = gam[i];
+            b = bet[i];
+          } else {
+            g = gv[c];
+            b = bv[c];
+          }
           V o;
 #pragma unroll
           for (int e = 0; e < E; ++e)
