@@ -312,6 +312,23 @@ hipError_t launch_abrln_t(const void* u, const void* bias, const void* res, cons
 
 // y = LN(x) (r == nullptr), or sum = x + r then y = LN(sum) (gamma != nullptr)
 // or only sum = x + r (gamma == nullptr).
+// Workgroups of kernel KERN resident on a device at once (computed on the
+// first launch of each kernel form, on the device current then; every device
+// this library targets has the same CU count), capped by the row count.
+template <auto KERN>
+unsigned ln_grid(int64_t rows) {
+  static const int resident = [] {
+    int per_cu = 0, dev = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KERN, kLnThreads, 0) != hipSuccess || per_cu < 1)
+      per_cu = 2;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+      cus = 256;
+    return per_cu * cus;
+  }();
+  return (unsigned)(rows < resident ? rows : resident);
+}
+
 template <typename T, bool ADD, bool NORM>
 hipError_t launch_ln_mode(const T* xp, const T* rp, T* sp, const T* gp, const T* bp, int64_t rows, int H, float eps,
                           T* yp, hipStream_t s) {
@@ -333,10 +350,14 @@ hipError_t launch_ln_mode(const T* xp, const T* rp, T* sp, const T* gp, const T*
 #undef EE_LN_WAVE
     return hipGetLastError();
   }
-  // block kernel: a few workgroups per CU, each walking several rows
-  const dim3 grid((unsigned)(rows > 2048 ? 2048 : rows)), blk(kLnThreads);
-#define EE_LN_BLOCK(V) \
-  hipLaunchKernelGGL((layernorm_kernel<T, V, ADD, NORM>), grid, blk, 0, s, xp, rp, sp, gp, bp, rows, H, eps, yp)
+  // block kernel: as many workgroups as the device holds at once (one wave
+  // of workgroups, none waiting for a slot), each walking several rows.  At
+  // 12288 fp16 columns (two workgroups per CU) 512 workgroups ran 8-12%
+  // faster than 2048 on 4096 rows and the same on 8125.
+  const dim3 blk(kLnThreads);
+#define EE_LN_BLOCK(V)                                                                                   \
+  hipLaunchKernelGGL((layernorm_kernel<T, V, ADD, NORM>), dim3(ln_grid<layernorm_kernel<T, V, ADD, NORM>>(rows)), \
+                     blk, 0, s, xp, rp, sp, gp, bp, rows, H, eps, yp)
   if (nvec <= 256)
     EE_LN_BLOCK(1);
   else if (nvec <= 512)
