@@ -112,6 +112,8 @@ def test_remove_rebuild_bit_exact(dtype, H, lens, P):
 @pytest.mark.parametrize("dtype,H,rows,tol", [
     (torch.float16, 768, 37, 2e-3), (torch.float16, 12288, 19, 2e-3), (torch.float16, 64, 300, 2e-3),
     (torch.float32, 64, 33, 1e-5), (torch.float32, 12288, 7, 1e-5), (torch.float16, 4096, 5, 2e-3),
+    # more rows than the grid's workgroups: each walks several rows with gamma/beta held in registers
+    (torch.float16, 12288, 2000, 2e-3), (torch.float32, 4096, 3001, 1e-5), (torch.float16, 8192, 1537, 2e-3),
 ])
 def test_layernorm_parity(dtype, H, rows, tol):
     x = (torch.randn(rows, H, generator=GEN) * 3 + 0.7).to(dtype)
